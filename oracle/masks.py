@@ -1,0 +1,127 @@
+"""CPU oracle for the integer steps: mask localization and tile classes.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/attention.py``): nothing on the
+product path imports it.
+
+Localization follows "FlashMask-3: ядро внимания с масками для GPU Hopper и
+распределённого обучения" (iitog.ru), contributions paragraph and "Key
+facts": the mask is indexed by key position but stores query-axis interval
+bounds, so a rank that holds several fragments of the context localizes it by
+operating on the bound vectors alone (clip, shift, max), with no
+communication. The oracle does not use clip/shift/max: it uses the counting
+definition that the operation must reproduce. With the rank's rows in
+ascending global order g_0 < g_1 < ..., a global bound x becomes
+    x' = #{ r : g_r < x },
+the number of local rows whose global index is below x. Then local row r lies
+in [S', E') exactly when g_r lies in [S, E), so every interval maps to one
+contiguous local interval.
+
+Tile classes: the pages do not describe a tile pre-pass. The rule here is the
+reading adopted for it. Per K/V tile, the minimum and maximum of each bound
+vector over the tile's columns are reduced; a (Q tile, K tile) pair with rows
+[r0, r1) is
+    SKIP    if for the lower or for the upper interval every column's
+            interval covers all rows: max(start) <= r0 and min(end) >= r1;
+    FULL    else if for both intervals every column's interval misses the
+            rows on one common side: max(end) <= r0 or min(start) >= r1;
+    PARTIAL otherwise.
+A missing (None) pair stands for the canonical empty intervals: lower
+[Sq, Sq) and upper [0, 0). The dense-truth classes (all rows x columns
+masked / none masked) are computed separately for soundness checks.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import dense_mask, vectors_for, SKIP, PARTIAL, FULL
+
+
+def local_rows(chunk_start, chunk_len):
+    """Global indices of a rank's rows, chunk by chunk in the listed order."""
+    return np.concatenate([np.arange(int(s), int(s) + int(l), dtype=np.int64)
+                           for s, l in zip(chunk_start, chunk_len)])
+
+
+def localize(vectors, chunk_start, chunk_len):
+    """Localized bound vectors by the counting definition.
+
+    ``vectors`` is (lts, lte, uts, ute), each [Bm, Hm, Sk] or None; chunks must
+    be listed in ascending global order and must not overlap. Returns int32
+    arrays of the same shapes.
+    """
+    rows = local_rows(chunk_start, chunk_len)
+    if np.any(np.diff(rows) <= 0):
+        raise ValueError("chunks must be ascending and non-overlapping")
+    out = []
+    for x in vectors:
+        if x is None:
+            out.append(None)
+            continue
+        x = np.asarray(x, dtype=np.int64)
+        out.append(np.searchsorted(rows, x, side="left").astype(np.int32))
+    return tuple(out)
+
+
+def _canonical(vec, seq_q, n_keys):
+    lts, lte, uts, ute = vec
+    if lts is None:
+        lts = np.full(n_keys, seq_q, dtype=np.int64)
+        lte = np.full(n_keys, seq_q, dtype=np.int64)
+    if uts is None:
+        uts = np.zeros(n_keys, dtype=np.int64)
+        ute = np.zeros(n_keys, dtype=np.int64)
+    return lts, lte, uts, ute
+
+
+def tile_summary(vectors, seq_q, seq_k, block_k, b=0, h=0):
+    """Per K tile: (min, max) of lts, lte, uts, ute over the tile's columns.
+
+    Returns int64 [Tk, 8] ordered
+    (min lts, max lts, min lte, max lte, min uts, max uts, min ute, max ute).
+    """
+    vec = _canonical(vectors_for(vectors, b, h), seq_q, seq_k)
+    tk = -(-seq_k // block_k)
+    out = np.zeros((tk, 8), dtype=np.int64)
+    for t in range(tk):
+        c = slice(t * block_k, min((t + 1) * block_k, seq_k))
+        for i, x in enumerate(vec):
+            out[t, 2 * i] = x[c].min()
+            out[t, 2 * i + 1] = x[c].max()
+    return out
+
+
+def tile_classes(vectors, seq_q, seq_k, block_q, block_k, b=0, h=0):
+    """Class map [Tq, Tk] (uint8) by the min/max rule."""
+    s = tile_summary(vectors, seq_q, seq_k, block_k, b, h)
+    tq = -(-seq_q // block_q)
+    out = np.zeros((tq, s.shape[0]), dtype=np.uint8)
+    for qt in range(tq):
+        r0, r1 = qt * block_q, min((qt + 1) * block_q, seq_q)
+        for kt in range(s.shape[0]):
+            min_ls, max_ls, min_le, max_le, min_us, max_us, min_ue, max_ue = s[kt]
+            covers_l = max_ls <= r0 and min_le >= r1
+            covers_u = max_us <= r0 and min_ue >= r1
+            misses_l = max_le <= r0 or min_ls >= r1
+            misses_u = max_ue <= r0 or min_us >= r1
+            if covers_l or covers_u:
+                out[qt, kt] = SKIP
+            elif misses_l and misses_u:
+                out[qt, kt] = FULL
+            else:
+                out[qt, kt] = PARTIAL
+    return out
+
+
+def tile_classes_dense(vectors, seq_q, seq_k, block_q, block_k, b=0, h=0):
+    """Dense-truth classes [Tq, Tk]: SKIP if every pair of the tile is masked,
+    FULL if none is, PARTIAL otherwise."""
+    vec = vectors_for(vectors, b, h)
+    tq, tk = -(-seq_q // block_q), -(-seq_k // block_k)
+    out = np.zeros((tq, tk), dtype=np.uint8)
+    for qt in range(tq):
+        rows = np.arange(qt * block_q, min((qt + 1) * block_q, seq_q))
+        m = dense_mask(*vec, rows, seq_k)
+        for kt in range(tk):
+            t = m[:, kt * block_k:min((kt + 1) * block_k, seq_k)]
+            out[qt, kt] = SKIP if t.all() else (FULL if not t.any() else PARTIAL)
+    return out

@@ -1,0 +1,9 @@
+"""The CPU oracle against its pins (no GPU)."""
+import pytest
+
+import pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
