@@ -1,0 +1,209 @@
+/*
+ * fm_attn.h — C ABI of libfmattn: exact scaled-dot-product attention under
+ * structural masks in column-sparse form, forward and backward, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source of the operation. "FlashMask-3: ядро внимания с масками для GPU
+ * Hopper и распределённого обучения" (iitog.ru):
+ *   - predecessor paragraph: the mask is held column-sparse, as four bound
+ *     vectors on the query axis per key column (O(n) memory, not O(n^2));
+ *   - contributions paragraph and "Key facts": a rank holding several
+ *     fragments of the context localizes the mask by clip / shift / max on
+ *     the bound vectors, with no communication, and the result feeds the
+ *     single-GPU kernel unchanged.
+ * "FlashAttention-2 ... GPU work partitioning" (iplexlaw.co.kr), section
+ * "Block processing keeps the global normalization": the tiled computation
+ * is exact attention (only the floating-point order differs); section
+ * "Three ways to raise GPU utilization": work is split over batch, heads and
+ * sequence, and Q rows are split among the waves of a workgroup while K/V are
+ * shared.
+ *
+ * The pages give no interface, no vector names and no formula; the reading
+ * used throughout is:
+ *   query row i is MASKED for key column j  iff
+ *       lts[j] <= i < lte[j]   ("lower" interval)   or
+ *       uts[j] <= i < ute[j]   ("upper" interval).
+ *   Intervals are half open; start >= end is empty. Any int32 value is
+ *   accepted (bounds are never validated: the predicate is defined for all).
+ *   O_i = sum_j softmax_j(scale * q_i . k_j over unmasked j) v_j;
+ *   LSE_i = ln sum_{j unmasked} exp(scale * q_i . k_j)  (natural log);
+ *   a row with no unmasked key has O_i = 0, LSE_i = -inf and zero gradients.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" are device memory on the current HIP device;
+ *     "host" pointers are read before the call returns. The caller owns every
+ *     buffer. The library never allocates device memory.
+ *   - Every kernel is launched asynchronously on `stream` (NULL = the null
+ *     stream); no call synchronises the host.
+ *   - A status other than FM_OK means nothing was launched, except
+ *     FM_ERR_HIP, which reports a HIP error raised by a launch. The message
+ *     of the last failure on the calling thread is fm_last_error().
+ *   - Tensor layout: Q, O, dO, dQ are [B, Sq, H, D] and K, V, dK, dV are
+ *     [B, Sk, H, D], addressed by (b, s, h) element strides with the head
+ *     dimension D contiguous. LSE is [B, H, Sq] float32, contiguous.
+ *   - Mask vectors are int32 [Bm, Hm, Sk] with the key axis contiguous and
+ *     element strides (stride_b, stride_h); Bm in {1, B}, Hm in {1, H}; a
+ *     size of 1 broadcasts over batch / heads.
+ */
+#ifndef FM_ATTN_H
+#define FM_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FM_OK = 0,
+  FM_ERR_INVALID_ARGUMENT = 1,  /* null pointer, bad size, stride, alignment, chunk list */
+  FM_ERR_UNSUPPORTED = 2,       /* valid but not implemented (e.g. head_dim 96) */
+  FM_ERR_WORKSPACE = 3,         /* workspace pointer missing or too small */
+  FM_ERR_HIP = 4                /* a kernel launch reported a HIP error */
+} fm_status;
+
+typedef enum {
+  FM_BF16 = 0,   /* bfloat16 inputs and outputs */
+  FM_FP32 = 1    /* float32 inputs and outputs; rounded to bf16 on load for the
+                    matrix products (fp32 accumulation, fp32 softmax state) */
+} fm_dtype;
+
+/* Tile classes of the classification pre-pass. */
+typedef enum {
+  FM_TILE_SKIP = 0,     /* every (row, key) pair of the tile is masked      */
+  FM_TILE_PARTIAL = 1,  /* may hold masked and unmasked pairs: apply mask    */
+  FM_TILE_FULL = 2      /* no pair of the tile is masked                     */
+} fm_tile_class;
+
+/* Column-sparse mask: four device int32 vectors [Bm][Hm][Sk].
+ * The lower pair (lts, lte) may be both NULL: the lower interval is then
+ * empty for every column. Likewise the upper pair (uts, ute). Exactly one
+ * NULL pointer in a pair is an error. */
+typedef struct {
+  const int32_t* lts;
+  const int32_t* lte;
+  const int32_t* uts;
+  const int32_t* ute;
+  int32_t batch;      /* Bm: 1 or B */
+  int32_t heads;      /* Hm: 1 or H */
+  int64_t stride_b;   /* element stride between batch rows of each vector */
+  int64_t stride_h;   /* element stride between head rows of each vector  */
+} fm_mask;
+
+/* Problem description. Strides are in elements, ordered (b, s, h); the head
+ * dimension is contiguous. dO, dQ share the strides of O, Q; dK, dV share
+ * those of K, V. Every tensor base pointer must be 16-byte aligned and every
+ * (b, s, h) row must start 16-byte aligned. */
+typedef struct {
+  int32_t batch;         /* B  >= 1 */
+  int32_t heads;         /* H  >= 1 */
+  int32_t seqlen_q;      /* Sq >= 1 */
+  int32_t seqlen_k;      /* Sk >= 1 */
+  int32_t head_dim;      /* D in {64, 128} */
+  fm_dtype dtype;
+  float softmax_scale;   /* > 0 and finite, e.g. 1/sqrt(D) */
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} fm_problem;
+
+/* Tile sizes (rows of Q, columns of K) used by the forward (bwd = 0) or the
+ * backward (bwd = 1) kernel for a head dimension. Unsupported head_dim
+ * yields 0, 0. */
+void fm_kernel_tile(int32_t head_dim, int32_t bwd, int32_t* block_q, int32_t* block_k);
+
+/* Bytes of device workspace fm_attn_fwd (with_bwd = 0) or fm_attn_bwd
+ * (with_bwd = 1) needs: tile summaries and class map, plus for the backward
+ * the row terms D and the float32 dQ accumulator. */
+fm_status fm_workspace_size(const fm_problem* problem, const fm_mask* mask,
+                            int32_t with_bwd, size_t* bytes);
+
+/* Tile classification pre-pass (reading adopted; the pages do not describe
+ * one). For key tile kt (columns [kt*block_k, min((kt+1)*block_k, Sk)))
+ * the summary holds, as 8 int32, min and max of lts, lte, uts, ute over the
+ * tile's columns (missing pairs count as the empty intervals [Sq, Sq) and
+ * [0, 0)), in the order
+ *   min lts, max lts, min lte, max lte, min uts, max uts, min ute, max ute.
+ * The class of the pair (qt, kt), rows [r0, r1) = [qt*block_q,
+ * min((qt+1)*block_q, Sq)), is
+ *   SKIP    if for lower or upper: max(start) <= r0 and min(end) >= r1;
+ *   FULL    else if for both: max(end) <= r0 or min(start) >= r1;
+ *   PARTIAL otherwise.
+ * Outputs (device):
+ *   summary  int32 [Bm][Hm][Tk][8]
+ *   classes  uint8 [Bm][Hm][Tq][Tk] (transposed = 0) or [Bm][Hm][Tk][Tq]
+ *            (transposed = 1), Tq = ceil(Sq/block_q), Tk = ceil(Sk/block_k).
+ * block_q and block_k must be in [1, 1024]. */
+fm_status fm_tile_classify(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen_k,
+                           int32_t block_q, int32_t block_k, int32_t transposed,
+                           int32_t* summary, uint8_t* classes, hipStream_t stream);
+
+/* Forward. Inputs q [B,Sq,H,D], k, v [B,Sk,H,D] (device, problem dtype).
+ * Outputs o [B,Sq,H,D] (device, problem dtype) and lse [B,H,Sq] (device,
+ * float32). Fully masked (SKIP) tiles are never touched; the mask is
+ * evaluated only on PARTIAL tiles. workspace: device, at least
+ * fm_workspace_size(.., 0) bytes, 256-byte aligned. */
+fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, const void* v,
+                      const fm_mask* mask, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward. Inputs q, k, v, o (the forward output), lse (the forward LSE),
+ * dout (gradient of o), all device. Outputs dq, dk, dv (device, problem
+ * dtype, shapes of q, k, v). workspace: device, at least
+ * fm_workspace_size(.., 1) bytes, 256-byte aligned. dQ is accumulated in
+ * float32 with atomics, so its last bits may differ from run to run. */
+fm_status fm_attn_bwd(const fm_problem* problem, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dout, const fm_mask* mask,
+                      void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Mask localization for one context-parallel rank (FlashMask-3 page,
+ * contributions paragraph: clip, shift, max on the bound vectors, no
+ * communication). The rank holds num_chunks fragments of the global query
+ * axis, chunk c covering global rows [chunk_start[c], chunk_start[c] +
+ * chunk_len[c]); its local rows are these rows in the listed order.
+ * Chunks (host arrays) must be listed in ascending order, must not overlap,
+ * must have chunk_len >= 1 and must lie in [0, seqlen_q_global];
+ * 1 <= num_chunks <= 64. Each global bound x becomes
+ *   x' = max(0, max_c min(clamp(x, 0, Sq_glob) - start_c + off_c,
+ *                         off_c + len_c)),   off_c = sum of len before c,
+ * i.e. the number of local rows whose global index is below x, so that local
+ * row r is masked for key j exactly when its global row is.
+ * out[0..3] (device, int32 [Bm][Hm][seqlen_k] contiguous) receive the
+ * localized lts, lte, uts, ute. A pair that is NULL in `global` is skipped
+ * (its out pointers are ignored and may be NULL). Keys are not localized. */
+fm_status fm_mask_localize(const fm_mask* global, int32_t seqlen_k, int32_t seqlen_q_global,
+                           const int32_t* chunk_start, const int32_t* chunk_len,
+                           int32_t num_chunks, int32_t* const out[4], hipStream_t stream);
+
+/* Per-kernel timing. Between fm_profile_begin and fm_profile_end the library
+ * records a HIP event pair on the launch stream around each of its kernel
+ * launches (at most max_launches pairs; later launches are not recorded).
+ * fm_profile_end waits for those events and writes, per stage, the summed
+ * duration in milliseconds and the number of recorded launches (arrays of
+ * FM_NUM_STAGES entries). Not thread safe; profiling state is per process. */
+typedef enum {
+  FM_STAGE_CLASSIFY_SUMMARY = 0,
+  FM_STAGE_CLASSIFY_MAP = 1,
+  FM_STAGE_FWD = 2,
+  FM_STAGE_BWD_PRE = 3,
+  FM_STAGE_BWD = 4,
+  FM_STAGE_DQ_FINALIZE = 5,
+  FM_STAGE_LOCALIZE = 6,
+  FM_NUM_STAGES = 7
+} fm_stage;
+
+fm_status fm_profile_begin(int32_t max_launches);
+fm_status fm_profile_end(float* total_ms, int32_t* launches);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* fm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FM_ATTN_H */

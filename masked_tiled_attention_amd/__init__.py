@@ -1,0 +1,10 @@
+"""Masked tiled attention for AMD MI355X (gfx950).
+
+Exact scaled-dot-product attention under structural masks in column-sparse
+form (four int32 query-axis bound vectors per key column), forward and
+backward, as hand-written HIP kernels behind a C ABI (libfmattn.so,
+include/fm_attn.h). This package is the thin Python binding.
+"""
+from ._lib import FmError, load, EXPORTS  # noqa: F401
+from .api import (Mask, fm_attn_bwd, fm_attn_fwd, fm_kernel_tile, fm_mask_localize,  # noqa: F401
+                  fm_profile_begin, fm_profile_end, fm_tile_classify, fm_workspace_size)

@@ -1,0 +1,418 @@
+// C ABI of libfmattn (declared in include/fm_attn.h): argument validation,
+// workspace layout, launch sequencing and per-launch event timing.
+// Nothing here allocates device memory; every launch goes on the caller's
+// stream and no call synchronises the host (fm_profile_end excepted).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "fm_attn.h"
+#include "fm_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+fm_status fail(fm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+constexpr int64_t kMaxSeq = int64_t(1) << 24;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- profiling
+struct Profiler {
+  bool enabled = false;
+  int cap = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;     // 2 per record
+  std::vector<int> stage;
+};
+Profiler g_prof;
+
+template <class F>
+hipError_t run_stage(fm_stage st, hipStream_t s, F&& launch) {
+  bool rec = g_prof.enabled && g_prof.used < g_prof.cap;
+  if (rec) rec = hipEventRecord(g_prof.ev[2 * g_prof.used], s) == hipSuccess;
+  hipError_t e = launch();
+  if (rec && hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s) == hipSuccess) {
+    g_prof.stage[g_prof.used] = (int)st;
+    ++g_prof.used;
+  }
+  return e;
+}
+
+fm_status hip_fail(hipError_t e, const char* what) {
+  return fail(FM_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- validation
+fm_status check_mask(const fm_mask* m, int64_t B, int64_t H, fm::MaskArgs* out) {
+  if (!m) return fail(FM_ERR_INVALID_ARGUMENT, "mask is NULL");
+  const bool lo0 = m->lts == nullptr, lo1 = m->lte == nullptr;
+  const bool up0 = m->uts == nullptr, up1 = m->ute == nullptr;
+  if (lo0 != lo1) return fail(FM_ERR_INVALID_ARGUMENT, "mask: exactly one of lts/lte is NULL");
+  if (up0 != up1) return fail(FM_ERR_INVALID_ARGUMENT, "mask: exactly one of uts/ute is NULL");
+  if (!(m->batch == 1 || m->batch == B))
+    return fail(FM_ERR_INVALID_ARGUMENT, "mask batch %d must be 1 or %lld", m->batch, (long long)B);
+  if (!(m->heads == 1 || m->heads == H))
+    return fail(FM_ERR_INVALID_ARGUMENT, "mask heads %d must be 1 or %lld", m->heads, (long long)H);
+  if (m->stride_b < 0 || m->stride_h < 0) return fail(FM_ERR_INVALID_ARGUMENT, "mask strides must be >= 0");
+  const int32_t* ptrs[4] = {m->lts, m->lte, m->uts, m->ute};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && (reinterpret_cast<uintptr_t>(ptrs[i]) % 4))
+      return fail(FM_ERR_INVALID_ARGUMENT, "mask vector %d is not 4-byte aligned", i);
+  out->lts = m->lts;
+  out->lte = m->lte;
+  out->uts = m->uts;
+  out->ute = m->ute;
+  out->stride_b = m->stride_b;
+  out->stride_h = m->stride_h;
+  out->bm = m->batch;
+  out->hm = m->heads;
+  out->has_lower = !lo0;
+  out->has_upper = !up0;
+  return FM_OK;
+}
+
+fm_status check_problem(const fm_problem* p) {
+  if (!p) return fail(FM_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->batch < 1 || p->heads < 1 || p->seqlen_q < 1 || p->seqlen_k < 1)
+    return fail(FM_ERR_INVALID_ARGUMENT, "batch, heads, seqlen_q, seqlen_k must be >= 1");
+  if (p->seqlen_q > kMaxSeq || p->seqlen_k > kMaxSeq)
+    return fail(FM_ERR_INVALID_ARGUMENT, "sequence lengths must be <= %lld", (long long)kMaxSeq);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(FM_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
+  if (p->dtype != FM_BF16 && p->dtype != FM_FP32)
+    return fail(FM_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)p->dtype);
+  if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale))
+    return fail(FM_ERR_INVALID_ARGUMENT, "softmax_scale must be positive and finite");
+  const int64_t es = p->dtype == FM_BF16 ? 2 : 4;
+  const int64_t* st[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
+  const char* nm[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i) {
+      if (st[t][i] < 0) return fail(FM_ERR_INVALID_ARGUMENT, "%s stride %d is negative", nm[t], i);
+      if ((st[t][i] * es) % 16)
+        return fail(FM_ERR_INVALID_ARGUMENT, "%s stride %d (%lld elements) breaks 16-byte row alignment",
+                    nm[t], i, (long long)st[t][i]);
+    }
+  const int64_t tq = ceil_div(p->seqlen_q, fm::kFwdBlockQ);
+  if (tq * p->batch * p->heads > INT32_MAX)
+    return fail(FM_ERR_INVALID_ARGUMENT, "problem too large for one launch");
+  return FM_OK;
+}
+
+fm_status check_ptr(const void* ptr, const char* name) {
+  if (!ptr) return fail(FM_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(ptr) % 16)
+    return fail(FM_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return FM_OK;
+}
+
+struct Layout {
+  size_t summary = 0, map = 0, drow = 0, dqacc = 0, total = 0;
+};
+
+Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
+  Layout L;
+  const int64_t bq = bwd ? fm::kBwdBlockQ : fm::kFwdBlockQ;
+  const int64_t bk = bwd ? fm::kBwdBlockK : fm::kFwdBlockK;
+  const int64_t tq = ceil_div(p->seqlen_q, bq), tk = ceil_div(p->seqlen_k, bk);
+  const int64_t bh = (int64_t)m->batch * m->heads;
+  size_t off = 0;
+  L.summary = off;
+  off = align256(off + (size_t)(bh * tk * 8 * 4));
+  L.map = off;
+  off = align256(off + (size_t)(bh * tq * tk));
+  if (bwd) {
+    L.drow = off;
+    off = align256(off + (size_t)p->batch * p->heads * p->seqlen_q * 4);
+    L.dqacc = off;
+    off = align256(off + (size_t)p->batch * p->seqlen_q * p->heads * p->head_dim * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+fm_status classify_into(const fm::MaskArgs& mk, int32_t sq, int32_t sk, int32_t bq, int32_t bk,
+                        int32_t transposed, int32_t* summary, uint8_t* classes, hipStream_t s) {
+  fm::ClassifyArgs c{};
+  c.mask = mk;
+  c.seq_q = sq;
+  c.seq_k = sk;
+  c.block_q = bq;
+  c.block_k = bk;
+  c.tq = (int32_t)ceil_div(sq, bq);
+  c.tk = (int32_t)ceil_div(sk, bk);
+  c.summary = summary;
+  c.classes = classes;
+  c.transposed = transposed;
+  hipError_t e = run_stage(FM_STAGE_CLASSIFY_SUMMARY, s, [&] { return fm::launch_classify_summary(c, s); });
+  if (e != hipSuccess) return hip_fail(e, "classify summary launch");
+  e = run_stage(FM_STAGE_CLASSIFY_MAP, s, [&] { return fm::launch_classify_map(c, s); });
+  if (e != hipSuccess) return hip_fail(e, "classify map launch");
+  return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fm_last_error(void) { return g_err.c_str(); }
+
+void fm_kernel_tile(int32_t head_dim, int32_t bwd, int32_t* block_q, int32_t* block_k) {
+  int32_t q = 0, k = 0;
+  if (head_dim == 64 || head_dim == 128) {
+    q = bwd ? fm::kBwdBlockQ : fm::kFwdBlockQ;
+    k = bwd ? fm::kBwdBlockK : fm::kFwdBlockK;
+  }
+  if (block_q) *block_q = q;
+  if (block_k) *block_k = k;
+}
+
+fm_status fm_workspace_size(const fm_problem* problem, const fm_mask* mask, int32_t with_bwd, size_t* bytes) {
+  fm_status st = check_problem(problem);
+  if (st != FM_OK) return st;
+  fm::MaskArgs mk;
+  st = check_mask(mask, problem->batch, problem->heads, &mk);
+  if (st != FM_OK) return st;
+  if (!bytes) return fail(FM_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = workspace_layout(problem, mask, with_bwd != 0).total;
+  return FM_OK;
+}
+
+fm_status fm_tile_classify(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen_k, int32_t block_q,
+                           int32_t block_k, int32_t transposed, int32_t* summary, uint8_t* classes,
+                           hipStream_t stream) {
+  fm::MaskArgs mk;
+  if (!mask) return fail(FM_ERR_INVALID_ARGUMENT, "mask is NULL");
+  fm_status st = check_mask(mask, mask->batch, mask->heads, &mk);
+  if (st != FM_OK) return st;
+  if (mask->batch < 1 || mask->heads < 1) return fail(FM_ERR_INVALID_ARGUMENT, "mask batch/heads must be >= 1");
+  if (seqlen_q < 1 || seqlen_k < 1 || seqlen_q > kMaxSeq || seqlen_k > kMaxSeq)
+    return fail(FM_ERR_INVALID_ARGUMENT, "sequence lengths must be in [1, %lld]", (long long)kMaxSeq);
+  if (block_q < 1 || block_q > 1024 || block_k < 1 || block_k > 1024)
+    return fail(FM_ERR_INVALID_ARGUMENT, "block sizes must be in [1, 1024]");
+  const int64_t tq = ceil_div(seqlen_q, block_q), tk = ceil_div(seqlen_k, block_k);
+  if ((transposed ? tk : tq) > 65535 || (int64_t)mask->batch * mask->heads > 65535)
+    return fail(FM_ERR_INVALID_ARGUMENT, "too many tiles for one launch (reduce tiles or use larger blocks)");
+  if (!summary || !classes) return fail(FM_ERR_INVALID_ARGUMENT, "summary/classes is NULL");
+  if (reinterpret_cast<uintptr_t>(summary) % 4) return fail(FM_ERR_INVALID_ARGUMENT, "summary not 4-byte aligned");
+  return classify_into(mk, seqlen_q, seqlen_k, block_q, block_k, transposed ? 1 : 0, summary, classes, stream);
+}
+
+fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v, const fm_mask* mask,
+                      void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  fm::MaskArgs mk;
+  st = check_mask(mask, p->batch, p->heads, &mk);
+  if (st != FM_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
+    return st;
+  const Layout L = workspace_layout(p, mask, false);
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(FM_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(FM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  const int32_t tq = (int32_t)ceil_div(p->seqlen_q, fm::kFwdBlockQ);
+  const int32_t tk = (int32_t)ceil_div(p->seqlen_k, fm::kFwdBlockK);
+  if (tq > 65535) return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_q too large");
+  char* w = static_cast<char*>(ws);
+  int32_t* summary = reinterpret_cast<int32_t*>(w + L.summary);
+  uint8_t* classes = reinterpret_cast<uint8_t*>(w + L.map);
+  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kFwdBlockQ, fm::kFwdBlockK, 0, summary, classes, stream);
+  if (st != FM_OK) return st;
+
+  fm::FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
+  a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
+  a.o_sb = p->o_stride[0]; a.o_ss = p->o_stride[1]; a.o_sh = p->o_stride[2];
+  a.batch = p->batch;
+  a.heads = p->heads;
+  a.seq_q = p->seqlen_q;
+  a.seq_k = p->seqlen_k;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.mask = mk;
+  a.classes = classes;
+  a.tq = tq;
+  a.tk = tk;
+  hipError_t e = run_stage(FM_STAGE_FWD, stream,
+                           [&] { return fm::launch_fwd(a, p->head_dim, p->dtype == FM_FP32, stream); });
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return FM_OK;
+}
+
+fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, const fm_mask* mask, void* dq, void* dk, void* dv,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  fm::MaskArgs mk;
+  st = check_mask(mask, p->batch, p->heads, &mk);
+  if (st != FM_OK) return st;
+  if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
+      (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")) || (st = check_ptr(dout, "dout")) ||
+      (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
+    return st;
+  const Layout L = workspace_layout(p, mask, true);
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(FM_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(FM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  const int32_t tq = (int32_t)ceil_div(p->seqlen_q, fm::kBwdBlockQ);
+  const int32_t tk = (int32_t)ceil_div(p->seqlen_k, fm::kBwdBlockK);
+  if (tk > 65535) return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_k too large");
+  char* w = static_cast<char*>(ws);
+  int32_t* summary = reinterpret_cast<int32_t*>(w + L.summary);
+  uint8_t* classes_t = reinterpret_cast<uint8_t*>(w + L.map);
+  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kBwdBlockQ, fm::kBwdBlockK, 1, summary, classes_t, stream);
+  if (st != FM_OK) return st;
+
+  fm::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.drow = reinterpret_cast<float*>(w + L.drow);
+  a.dq_acc = reinterpret_cast<float*>(w + L.dqacc);
+  a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
+  a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
+  a.o_sb = p->o_stride[0]; a.o_ss = p->o_stride[1]; a.o_sh = p->o_stride[2];
+  a.batch = p->batch;
+  a.heads = p->heads;
+  a.seq_q = p->seqlen_q;
+  a.seq_k = p->seqlen_k;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.mask = mk;
+  a.classes_t = classes_t;
+  a.tq = tq;
+  a.tk = tk;
+  const bool f32 = p->dtype == FM_FP32;
+  hipError_t e = run_stage(FM_STAGE_BWD_PRE, stream, [&] { return fm::launch_bwd_pre(a, p->head_dim, f32, stream); });
+  if (e != hipSuccess) return hip_fail(e, "backward pre-pass launch");
+  e = run_stage(FM_STAGE_BWD, stream, [&] { return fm::launch_bwd(a, p->head_dim, f32, stream); });
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  e = run_stage(FM_STAGE_DQ_FINALIZE, stream, [&] { return fm::launch_dq_finalize(a, p->head_dim, f32, stream); });
+  if (e != hipSuccess) return hip_fail(e, "dQ finalize launch");
+  return FM_OK;
+}
+
+fm_status fm_mask_localize(const fm_mask* global, int32_t seqlen_k, int32_t seqlen_q_global,
+                           const int32_t* chunk_start, const int32_t* chunk_len, int32_t num_chunks,
+                           int32_t* const out[4], hipStream_t stream) {
+  fm::MaskArgs mk;
+  if (!global) return fail(FM_ERR_INVALID_ARGUMENT, "mask is NULL");
+  fm_status st = check_mask(global, global->batch, global->heads, &mk);
+  if (st != FM_OK) return st;
+  if (global->batch < 1 || global->heads < 1 || (int64_t)global->batch * global->heads > 65535)
+    return fail(FM_ERR_INVALID_ARGUMENT, "mask batch*heads must be in [1, 65535]");
+  if (seqlen_k < 1 || seqlen_k > kMaxSeq) return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_k out of range");
+  if (seqlen_q_global < 1 || seqlen_q_global > kMaxSeq)
+    return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_q_global out of range");
+  if (num_chunks < 1 || num_chunks > fm::kMaxChunks)
+    return fail(FM_ERR_INVALID_ARGUMENT, "num_chunks must be in [1, %d]", fm::kMaxChunks);
+  if (!chunk_start || !chunk_len) return fail(FM_ERR_INVALID_ARGUMENT, "chunk list is NULL");
+  if (!out) return fail(FM_ERR_INVALID_ARGUMENT, "out is NULL");
+  fm::LocalizeArgs a{};
+  a.mask = mk;
+  a.seq_k = seqlen_k;
+  a.seq_q_global = seqlen_q_global;
+  a.num_chunks = num_chunks;
+  int64_t prev_end = 0, off = 0;
+  for (int c = 0; c < num_chunks; ++c) {
+    const int64_t s = chunk_start[c], l = chunk_len[c];
+    if (l < 1) return fail(FM_ERR_INVALID_ARGUMENT, "chunk %d has length %lld", c, (long long)l);
+    if (s < prev_end)
+      return fail(FM_ERR_INVALID_ARGUMENT, "chunk %d starts at %lld: chunks must ascend without overlap", c,
+                  (long long)s);
+    if (s + l > seqlen_q_global)
+      return fail(FM_ERR_INVALID_ARGUMENT, "chunk %d ends past seqlen_q_global", c);
+    a.chunk_start[c] = (int32_t)s;
+    a.chunk_len[c] = (int32_t)l;
+    a.chunk_off[c] = (int32_t)off;
+    off += l;
+    prev_end = s + l;
+  }
+  for (int i = 0; i < 4; ++i) {
+    const bool need = i < 2 ? mk.has_lower : mk.has_upper;
+    if (need && !out[i]) return fail(FM_ERR_INVALID_ARGUMENT, "out[%d] is NULL", i);
+    if (need && reinterpret_cast<uintptr_t>(out[i]) % 4)
+      return fail(FM_ERR_INVALID_ARGUMENT, "out[%d] not 4-byte aligned", i);
+    a.out[i] = out[i];
+  }
+  hipError_t e = run_stage(FM_STAGE_LOCALIZE, stream, [&] { return fm::launch_localize(a, stream); });
+  if (e != hipSuccess) return hip_fail(e, "localize launch");
+  return FM_OK;
+}
+
+fm_status fm_profile_begin(int32_t max_launches) {
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(FM_ERR_INVALID_ARGUMENT, "max_launches must be in [1, 2^20]");
+  if ((int)g_prof.ev.size() < 2 * max_launches) {
+    for (hipEvent_t e : g_prof.ev)
+      if (e) (void)hipEventDestroy(e);
+    g_prof.ev.assign(2 * max_launches, nullptr);
+    for (auto& e : g_prof.ev) {
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) return hip_fail(err, "hipEventCreate");
+    }
+  }
+  g_prof.stage.assign(max_launches, 0);
+  g_prof.cap = max_launches;
+  g_prof.used = 0;
+  g_prof.enabled = true;
+  return FM_OK;
+}
+
+fm_status fm_profile_end(float* total_ms, int32_t* launches) {
+  if (!g_prof.enabled) return fail(FM_ERR_INVALID_ARGUMENT, "profiling was not started");
+  g_prof.enabled = false;
+  float tot[FM_NUM_STAGES] = {0};
+  int32_t cnt[FM_NUM_STAGES] = {0};
+  for (int i = 0; i < g_prof.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    tot[g_prof.stage[i]] += ms;
+    cnt[g_prof.stage[i]] += 1;
+  }
+  for (int s = 0; s < FM_NUM_STAGES; ++s) {
+    if (total_ms) total_ms[s] = tot[s];
+    if (launches) launches[s] = cnt[s];
+  }
+  return FM_OK;
+}
+
+}  // extern "C"

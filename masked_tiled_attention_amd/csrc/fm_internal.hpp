@@ -1,0 +1,100 @@
+// Internal interfaces between the C-ABI layer (api.cpp) and the kernel
+// translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fm_attn.h"
+
+namespace fm {
+
+// Tile shapes of the attention kernels (rows of Q x columns of K).
+constexpr int kFwdBlockQ = 128;
+constexpr int kFwdBlockK = 64;
+constexpr int kBwdBlockQ = 64;
+constexpr int kBwdBlockK = 128;
+
+// Mask vectors as seen by the kernels. A missing pair is flagged and its
+// pointers are not dereferenced.
+struct MaskArgs {
+  const int32_t* lts;
+  const int32_t* lte;
+  const int32_t* uts;
+  const int32_t* ute;
+  int64_t stride_b, stride_h;
+  int32_t bm, hm;          // broadcast extents (1 or B / H)
+  int32_t has_lower, has_upper;
+};
+
+struct ClassifyArgs {
+  MaskArgs mask;
+  int32_t seq_q, seq_k, block_q, block_k, tq, tk;
+  int32_t* summary;        // [bm][hm][tk][8]
+  uint8_t* classes;        // [bm][hm][tq][tk] or [bm][hm][tk][tq]
+  int32_t transposed;
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int32_t batch, heads, seq_q, seq_k;
+  float scale;             // softmax scale
+  float scale_log2;        // scale * log2(e)
+  MaskArgs mask;
+  const uint8_t* classes;  // [bm][hm][tq][tk]
+  int32_t tq, tk;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;           // [B][Sq][H][D] float32, contiguous
+  float* drow;             // [B][H][Sq] float32: rowsum(dO * O)
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int32_t batch, heads, seq_q, seq_k;
+  float scale;
+  float scale_log2;
+  MaskArgs mask;
+  const uint8_t* classes_t;  // [bm][hm][tk][tq]
+  int32_t tq, tk;
+};
+
+constexpr int kMaxChunks = 64;
+
+struct LocalizeArgs {
+  MaskArgs mask;
+  int32_t seq_k, seq_q_global, num_chunks;
+  int32_t chunk_start[kMaxChunks];
+  int32_t chunk_len[kMaxChunks];
+  int32_t chunk_off[kMaxChunks];
+  int32_t* out[4];
+};
+
+// Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
+hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream);
+hipError_t launch_classify_map(const ClassifyArgs& a, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f32, hipStream_t stream);
+hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
+hipError_t launch_dq_finalize(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
+hipError_t launch_localize(const LocalizeArgs& a, hipStream_t stream);
+
+}  // namespace fm

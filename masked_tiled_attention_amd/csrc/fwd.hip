@@ -1,0 +1,312 @@
+// Forward kernel: masked attention with an online softmax over K/V tiles.
+//
+// "FlashAttention-2 ... GPU work partitioning" (iplexlaw.co.kr):
+//   - "Block processing keeps the global normalization": inputs are tiled in
+//     on-chip memory and the softmax is streamed, rescaling the running
+//     statistics and partial output so that the result is normalised over
+//     the whole key sequence; no score matrix goes to HBM.
+//   - "Three ways to raise GPU utilization": less non-matmul work (here the
+//     output is normalised once at the end and the mask is evaluated only on
+//     PARTIAL tiles), work split over batch, heads and query tiles, and the
+//     query rows of a tile split among the wavefronts while K/V are shared.
+// "FlashMask-3" page (iitog.ru), predecessor paragraph: the mask arrives as
+// four bound vectors per key column; fully masked tiles are skipped using the
+// classification pre-pass.
+//
+// CDNA4 mapping (one workgroup = 4 wavefronts = 128 query rows of one
+// (batch, head); each wavefront owns 32 rows):
+//   S^T = K Q^T with v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = the
+//         wavefront's Q rows held in registers for the whole kernel. In the
+//         accumulator each lane holds one query row (its column), so row max,
+//         row sum and the rescale are per-lane scalars, combined with the
+//         other half-wave once per tile (max) or once at the end (sum).
+//   O^T += V^T P^T: B = P straight from the S^T accumulator (rounded to bf16),
+//         A = V^T read from a transposed LDS copy of the V tile, with the
+//         contraction index permuted identically on both sides.
+#include <climits>
+#include <cmath>
+
+#include "fm_device.hpp"
+#include "fm_internal.hpp"
+
+namespace fm {
+namespace {
+
+constexpr int BQ = kFwdBlockQ;   // 128 query rows per workgroup
+constexpr int BK = kFwdBlockK;   // 64 keys per K/V tile
+constexpr int NW = BQ / 32;      // 4 wavefronts
+constexpr int NT = NW * 64;      // 256 threads
+constexpr int LIST_CAP = 2048;   // class bytes compacted per pass (8 per thread)
+constexpr uint32_t kPartialBit = 0x80000000u;
+
+template <int D>
+struct alignas(16) FwdSmem {
+  static constexpr int KP = D + 8;    // padded K row (elements): rows shift by 4 banks
+  static constexpr int VP = BK + 4;   // padded V^T row (elements)
+  uint16_t k[BK][KP];
+  uint16_t vt[D][VP];
+  int32_t bnd[4][BK];                 // lts, lte, uts, ute of the tile's columns
+  uint32_t list[LIST_CAP];            // non-SKIP key tiles (kt | partial bit)
+  int32_t scan[NW];
+};
+
+template <int D, bool F32>
+__global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
+  constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
+  constexpr int CB = D / 32;       // 32-channel blocks of O^T
+  constexpr int NB = BK / 32;      // 32-key blocks of a tile
+  __shared__ FwdSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int lr = l & 31;
+  const int g = l >> 5;
+
+  // Heaviest query tiles first (for causal-like masks later rows see more keys).
+  const int nbh = a.batch * a.heads;
+  const int bid = blockIdx.x;
+  const int qt = a.tq - 1 - bid / nbh;
+  const int bh = bid % nbh;
+  const int b = bh / a.heads;
+  const int h = bh % a.heads;
+  const int bm = a.mask.bm > 1 ? b : 0;
+  const int hm = a.mask.hm > 1 ? h : 0;
+  const int64_t mbase = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
+  const uint8_t* crow = a.classes + ((int64_t)(bm * a.mask.hm + hm) * a.tq + qt) * a.tk;
+
+  const int m = qt * BQ + w * 32 + lr;   // this lane's query row
+  const bool row_ok = m < a.seq_q;
+
+  u32x4 qf[KSTEPS];
+  {
+    const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      if (row_ok)
+        qf[s] = load8_as_bf16<F32>(a.q, qoff + 16 * s);
+      else
+        qf[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x16 oacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float C = a.scale_log2;
+  const bool ragged_k = (a.seq_k % BK) != 0;
+
+  for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
+    // ---- compact the non-SKIP key tiles of this row of the class map ----
+    const int n_in = min(LIST_CAP, a.tk - kt0);
+    uint8_t cls[LIST_CAP / NT];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < LIST_CAP / NT; ++e) {
+      const int idx = tid * (LIST_CAP / NT) + e;
+      cls[e] = idx < n_in ? crow[kt0 + idx] : (uint8_t)FM_TILE_SKIP;
+      cnt += cls[e] != FM_TILE_SKIP;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (l >= o) incl += y;
+    }
+    __syncthreads();   // previous pass finished reading sm.list / sm.scan
+    if (l == 63) sm.scan[w] = incl;
+    __syncthreads();
+    int pos = incl - cnt, n_list = 0;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      if (ww < w) pos += sm.scan[ww];
+      n_list += sm.scan[ww];
+    }
+#pragma unroll
+    for (int e = 0; e < LIST_CAP / NT; ++e) {
+      if (cls[e] != FM_TILE_SKIP) {
+        const uint32_t kt = (uint32_t)(kt0 + tid * (LIST_CAP / NT) + e);
+        sm.list[pos++] = kt | (cls[e] == FM_TILE_PARTIAL ? kPartialBit : 0u);
+      }
+    }
+    __syncthreads();
+
+    for (int it = 0; it < n_list; ++it) {
+      const uint32_t ent = sm.list[it];
+      const int kt = (int)(ent & ~kPartialBit);
+      const bool masked_tile = (ent & kPartialBit) || (ragged_k && kt == a.tk - 1);
+      const int n0 = kt * BK;
+
+      // ---- stage K (row-major) and V (transposed) tiles in LDS ----
+#pragma unroll
+      for (int r = 0; r < (BK * D / 8) / NT; ++r) {
+        const int ci = tid + r * NT;
+        const int row = ci / (D / 8);
+        const int c8 = ci % (D / 8);
+        const int n = n0 + row;
+        u32x4 val = u32x4{0u, 0u, 0u, 0u};
+        if (n < a.seq_k)
+          val = load8_as_bf16<F32>(a.k, (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)h * a.k_sh + 8 * c8);
+        *reinterpret_cast<u32x4*>(&sm.k[row][8 * c8]) = val;
+      }
+      for (int gi = tid; gi < (BK / 4) * (D / 8); gi += NT) {
+        const int kq = gi / (D / 8);
+        const int c8 = gi % (D / 8);
+        u32x4 rv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = n0 + 4 * kq + r;
+          rv[r] = u32x4{0u, 0u, 0u, 0u};
+          if (n < a.seq_k)
+            rv[r] = load8_as_bf16<F32>(a.v, (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)h * a.v_sh + 8 * c8);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          u32x2 ev, od;
+          ev[0] = (rv[0][p] & 0xffffu) | (rv[1][p] << 16);
+          ev[1] = (rv[2][p] & 0xffffu) | (rv[3][p] << 16);
+          od[0] = (rv[0][p] >> 16) | (rv[1][p] & 0xffff0000u);
+          od[1] = (rv[2][p] >> 16) | (rv[3][p] & 0xffff0000u);
+          *reinterpret_cast<u32x2*>(&sm.vt[8 * c8 + 2 * p][4 * kq]) = ev;
+          *reinterpret_cast<u32x2*>(&sm.vt[8 * c8 + 2 * p + 1][4 * kq]) = od;
+        }
+      }
+      if (masked_tile && tid < BK) {
+        const int n = n0 + tid;
+        int32_t v0, v1, v2, v3;
+        if (n < a.seq_k) {
+          v0 = a.mask.has_lower ? a.mask.lts[mbase + n] : a.seq_q;
+          v1 = a.mask.has_lower ? a.mask.lte[mbase + n] : a.seq_q;
+          v2 = a.mask.has_upper ? a.mask.uts[mbase + n] : 0;
+          v3 = a.mask.has_upper ? a.mask.ute[mbase + n] : 0;
+        } else {   // keys past the end: masked for every row
+          v0 = INT_MIN;
+          v1 = INT_MAX;
+          v2 = 0;
+          v3 = 0;
+        }
+        sm.bnd[0][tid] = v0;
+        sm.bnd[1][tid] = v1;
+        sm.bnd[2][tid] = v2;
+        sm.bnd[3][tid] = v3;
+      }
+      __syncthreads();
+
+      // ---- S^T = K Q^T ----
+      f32x16 sacc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        sacc[nb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(&sm.k[nb * 32 + lr][16 * s + 8 * g]);
+          sacc[nb] = mfma32(kf, qf[s], sacc[nb]);
+        }
+      }
+
+      // ---- interval mask on PARTIAL (and ragged) tiles only ----
+      if (masked_tile) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int nl = nb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+            const bool mk = (sm.bnd[0][nl] <= m && m < sm.bnd[1][nl]) ||
+                            (sm.bnd[2][nl] <= m && m < sm.bnd[3][nl]);
+            if (mk) sacc[nb][i] = -INFINITY;
+          }
+        }
+      }
+
+      // ---- online softmax (per-lane row) ----
+      float mx = -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run - m_use) * C);
+      const float mC = m_use * C;
+      float rs = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(fmaf(sacc[nb][i], C, -mC));
+          sacc[nb][i] = p;
+          rs += p;
+        }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 pf;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pf[j] = pack_bf16(sacc[nb][8 * t + 2 * j], sacc[nb][8 * t + 2 * j + 1]);
+          const int kb = nb * 32 + 16 * t + 4 * g;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.vt[cb * 32 + lr][kb]);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.vt[cb * 32 + lr][kb + 8]);
+            const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            oacc[cb] = mfma32(va, pf, oacc[cb]);
+          }
+        }
+      }
+      __syncthreads();   // LDS tiles are overwritten by the next iteration
+    }
+  }
+
+  // ---- epilogue: normalise once, write O and LSE ----
+  const float lt = l_run + xor32(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (row_ok) {
+    const int64_t ooff = (int64_t)b * a.o_sb + (int64_t)m * a.o_ss + (int64_t)h * a.o_sh;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c0 = cb * 32 + 8 * q4 + 4 * g;
+        const float x0 = oacc[cb][4 * q4 + 0] * inv, x1 = oacc[cb][4 * q4 + 1] * inv;
+        const float x2 = oacc[cb][4 * q4 + 2] * inv, x3 = oacc[cb][4 * q4 + 3] * inv;
+        if constexpr (F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + ooff + c0) = f32x4{x0, x1, x2, x3};
+        } else {
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + ooff + c0) =
+              u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+        }
+      }
+    }
+    if (g == 0)
+      a.lse[((int64_t)b * a.heads + h) * a.seq_q + m] =
+          lt > 0.f ? (m_run * C + __log2f(lt)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool F32>
+hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  const int nblk = a.tq * a.batch * a.heads;
+  hipLaunchKernelGGL((fwd_kernel<D, F32>), dim3(nblk), dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f32, hipStream_t stream) {
+  if (head_dim == 128) return f32 ? launch_fwd_t<128, true>(a, stream) : launch_fwd_t<128, false>(a, stream);
+  return f32 ? launch_fwd_t<64, true>(a, stream) : launch_fwd_t<64, false>(a, stream);
+}
+
+}  // namespace fm

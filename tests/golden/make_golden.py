@@ -41,15 +41,16 @@ def main():
                   "result the clip/shift/max localization on the bound vectors must give "
                   "(FlashMask-3 page, contributions paragraph and 'Key facts').",
         "cases": [
-            {"note": "rows {2,3,4,10,11,12,13} of 16", "chunk_start": [2, 10], "chunk_len": [3, 4],
+            {"note": "rows {2,3,4,10,11,12,13} of 16", "seq_q_global": 16,
+             "chunk_start": [2, 10], "chunk_len": [3, 4],
              "global": [-5, 0, 2, 3, 5, 7, 10, 11, 14, 16, 99],
              "local": [0, 0, 0, 1, 3, 3, 3, 4, 7, 7, 7]},
             {"note": "dual-chunk rank 3 of 8 over 65536 (chunks 3 and 12 of 4096)",
-             "chunk_start": [12288, 49152], "chunk_len": [4096, 4096],
+             "seq_q_global": 65536, "chunk_start": [12288, 49152], "chunk_len": [4096, 4096],
              "global": [0, 12288, 12289, 16384, 30000, 49152, 50000, 53248, 65536],
              "local": [0, 0, 1, 4096, 4096, 4096, 4944, 8192, 8192]},
             {"note": "one chunk covering everything is the identity inside [0, Sq]",
-             "chunk_start": [0], "chunk_len": [8],
+             "seq_q_global": 8, "chunk_start": [0], "chunk_len": [8],
              "global": [-3, 0, 1, 7, 8, 12], "local": [0, 0, 1, 7, 8, 8]},
         ],
     }

@@ -1,0 +1,108 @@
+"""Backward parity: dQ, dK, dV from the HIP kernels (through the C ABI, fed
+with the HIP forward's O and LSE as in training) vs the float64 oracle's exact
+gradients, element by element, plus edge cases and the gradient invariants."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import BF16_ROUND, assert_close, dev_mask, log, np64
+from oracle import attention as OA
+from synth import masks as SM
+from synth import tensors as ST
+
+pytestmark = pytest.mark.gpu
+
+
+def _families(n, rng):
+    return {
+        "causal": SM.causal(n),
+        "document": SM.document_causal(SM.uniform_doc_lengths(rng, n, 40, 300)),
+        "window": SM.sliding_window_causal(n, 150),
+        "prefix_lm": SM.prefix_lm(n, n // 4),
+        "share_question": SM.share_question(n // 6, SM.answer_lengths(rng, n - n // 6, 5)),
+        "none": SM.no_mask(n, n),
+    }
+
+
+def _run(fm, q, k, v, do, vec, scale):
+    q, k, v, do = (t.cuda() for t in (q, k, v, do))
+    m = dev_mask(vec)
+    o, lse = fm.fm_attn_fwd(q, k, v, m, scale)
+    dq, dk, dv = fm.fm_attn_bwd(q, k, v, o, lse, do, m, scale)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _compare(fm, q, k, v, do, vec, scale, tag, out_round=0.0):
+    log(f"bwd {tag} q={tuple(q.shape)} k={tuple(k.shape)} dtype={q.dtype}")
+    dq, dk, dv = _run(fm, q, k, v, do, vec, scale)
+    rq, rk, rv = OA.backward(np64(q), np64(k), np64(v), np64(do), vec, scale)
+    assert_close(np64(dq), rq, f"{tag} dQ", out_round=out_round)
+    assert_close(np64(dk), rk, f"{tag} dK", out_round=out_round)
+    assert_close(np64(dv), rv, f"{tag} dV", out_round=out_round)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_bwd_mask_families(gpu_lib, d):
+    rng = np.random.default_rng(100 + d)
+    n = 700
+    for name, v in _families(n, rng).items():
+        q, k, vv, do = ST.qkv(2, n, n, 3, d, seed=d + len(name), with_do=True)
+        _compare(gpu_lib, q, k, vv, do, tuple(x[None, None] for x in v), 1 / math.sqrt(d), f"{name} d={d}")
+
+
+def test_bwd_per_batch_and_head_masks(gpu_lib):
+    rng = np.random.default_rng(11)
+    n, B, H, d = 520, 2, 3, 128
+    per = [[list(_families(n, rng).values())[(b * H + h) % 6] for h in range(H)] for b in range(B)]
+    vec = SM.stack(per)
+    q, k, v, do = ST.qkv(B, n, n, H, d, seed=15, with_do=True)
+    _compare(gpu_lib, q, k, v, do, vec, 0.09, "per-(b,h) masks")
+
+
+def test_bwd_random_vectors_rectangular(gpu_lib):
+    rng = np.random.default_rng(12)
+    for sq, sk in ((300, 900), (900, 300), (129, 65)):
+        vec = tuple(rng.integers(-20, sq + 20, (1, 1, sk)).astype(np.int32) for _ in range(4))
+        q, k, v, do = ST.qkv(1, sq, sk, 2, 128, seed=sq + 1, with_do=True)
+        dq, dk, dv = _compare(gpu_lib, q, k, v, do, vec, 0.1, f"random {sq}x{sk}")
+        allowed = ~OA.dense_mask(*[x[0, 0].astype(np.int64) for x in vec], np.arange(sq), sk)
+        empty = torch.from_numpy(~allowed.any(axis=1))
+        assert torch.all(dq[:, empty] == 0)
+
+
+@pytest.mark.parametrize("sq,sk", [(1, 1), (1, 1000), (1000, 1), (64, 128), (65, 129)])
+def test_bwd_tiny_and_edge_shapes(gpu_lib, sq, sk):
+    rng = np.random.default_rng(sq * 5 + sk)
+    vec = tuple(rng.integers(-2, sq + 2, (1, 1, sk)).astype(np.int32) for _ in range(2)) + \
+        (np.zeros((1, 1, sk), np.int32), np.zeros((1, 1, sk), np.int32))
+    q, k, v, do = ST.qkv(1, sq, sk, 1, 64, seed=sq + 2 * sk, with_do=True)
+    # with one key, dV sums dO over up to 1000 rows (|dV| ~ 90): a bf16 output
+    # cannot hold that within 2e-2, so the bar adds the output's own rounding
+    _compare(gpu_lib, q, k, v, do, vec, 0.125, f"edge {sq}x{sk}", out_round=BF16_ROUND)
+
+
+def test_bwd_float32_inputs(gpu_lib):
+    n = 300
+    vec = tuple(x[None, None] for x in SM.causal(n))
+    q, k, v, do = ST.qkv(1, n, n, 2, 64, seed=3, dtype=torch.float32, with_do=True)
+    _compare(gpu_lib, q, k, v, do, vec, 0.125, "fp32 causal")
+
+
+def test_bwd_invariants(gpu_lib):
+    """sum_j dK_j = 0 and sum_j dV_j = sum over rows with an open key of dO_i
+    (softmax shift invariance), on the GPU's own gradients."""
+    n = 800
+    rng = np.random.default_rng(5)
+    vec = tuple(x[None, None] for x in SM.share_question(100, SM.answer_lengths(rng, n - 100, 5)))
+    q, k, v, do = ST.qkv(1, n, n, 2, 128, seed=21, with_do=True)
+    dq, dk, dv = _run(gpu_lib, q, k, v, do, vec, 0.1)
+    sdk = np64(dk).sum(axis=1)
+    sdv = np64(dv).sum(axis=1)
+    ref = np64(do).sum(axis=1)
+    scale_ref = np.abs(np64(dk)).sum(axis=1).max()
+    assert np.abs(sdk).max() <= 1e-2 * scale_ref, np.abs(sdk).max()
+    assert_close(sdv, ref, "sum dV = sum dO", max_abs=0.25, rel_l2=1e-2)

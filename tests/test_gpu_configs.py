@@ -1,0 +1,126 @@
+"""Every named workload at its full size, in the launch configuration the
+benchmark times, against the oracle on sampled outputs it computes one by
+one (query rows for O / LSE / dQ; key columns for dK / dV) and against
+invariants that hold at any size (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
+
+The context-parallel rank share is checked against the GLOBAL problem: the
+rank's rows under localized vectors must equal the same rows of global
+attention (localize-then-attend equals slice-of-global)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_close, dev_mask, log, np64
+from oracle import attention as OA
+from oracle import masks as OM
+from synth import configs as SC
+from synth import tensors as ST
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _open_count_per_key(vec, sq):
+    """Rows attending each key (selection of affordable columns only)."""
+    lts, lte, uts, ute = (x[0, 0].astype(np.int64) for x in vec)
+    a0, a1 = np.clip(lts, 0, sq), np.clip(lte, 0, sq)
+    b0, b1 = np.clip(uts, 0, sq), np.clip(ute, 0, sq)
+    a1, b1 = np.maximum(a1, a0), np.maximum(b1, b0)
+    inter = np.maximum(0, np.minimum(a1, b1) - np.maximum(a0, b0))
+    return sq - ((a1 - a0) + (b1 - b0) - inter)
+
+
+def _sample_rows(sq, rng, k=24):
+    return np.unique(np.concatenate([[0, 1, sq // 2, sq - 2, sq - 1], rng.choice(sq, k, replace=False)]))
+
+
+def _sample_cols(vec, sq, rng, budget=3000, k=12):
+    cnt = _open_count_per_key(vec, sq)
+    ok = np.flatnonzero((cnt >= 1) & (cnt <= budget // 3))
+    if len(ok) == 0:
+        ok = np.flatnonzero(cnt >= 1)
+    cols = rng.choice(ok, min(k, len(ok)), replace=False)
+    chosen, total = [], 0
+    for c in cols:
+        if total + cnt[c] > budget and chosen:
+            continue
+        chosen.append(int(c))
+        total += int(cnt[c])
+    return np.asarray(sorted(chosen))
+
+
+def _run(fm, w, vec_dev):
+    q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
+    o, lse = fm.fm_attn_fwd(q, k, v, vec_dev, w.scale)
+    grads = None
+    if w.backward:
+        do = w.do.cuda()
+        grads = fm.fm_attn_bwd(q, k, v, o, lse, do, vec_dev, w.scale)
+    torch.cuda.synchronize()
+    out = (o.cpu(), lse.cpu())
+    return out, None if grads is None else tuple(g.cpu() for g in grads)
+
+
+@pytest.mark.parametrize("name", [n for n in SC.NAMES if n != "c5_cp_rank3_of_8"])
+def test_workload_full_size(gpu_lib, name):
+    fm = gpu_lib
+    log(f"workload {name}: building inputs")
+    w = SC.build(name, seed=0)
+    (o, lse), grads = _run(fm, w, dev_mask(w.vectors))
+    rng = np.random.default_rng(1)
+    q, k, v = np64(w.q), np64(w.k), np64(w.v)
+    do = np64(w.do) if w.backward else None
+    heads = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    if len(heads) > 4:
+        heads = [heads[i] for i in rng.choice(len(heads), 4, replace=False)]
+    for b, h in heads:
+        rows = _sample_rows(w.seq_q, rng) if w.seq_q > 512 else np.arange(w.seq_q)
+        ro, rl = OA.forward_rows(q, k, v, w.vectors, w.scale, b, h, rows)
+        assert_close(np64(o)[b, rows, h], ro, f"{name} b{b}h{h} O rows")
+        assert_close(lse[b, h, rows].double().numpy(), rl, f"{name} b{b}h{h} LSE rows")
+        if grads is None:
+            continue
+        dq, dk, dv = grads
+        rq = OA.backward_rows(q, k, v, do, w.vectors, w.scale, b, h, rows)
+        assert_close(np64(dq)[b, rows, h], rq, f"{name} b{b}h{h} dQ rows")
+        vb = tuple(None if x is None else x[[b if x.shape[0] > 1 else 0]][:, [h if x.shape[1] > 1 else 0]]
+                   for x in w.vectors)
+        cols = _sample_cols(vb, w.seq_q, rng)
+        rk, rv = OA.backward_cols(q, k, v, do, w.vectors, w.scale, b, h, cols)
+        assert_close(np64(dk)[b, cols, h], rk, f"{name} b{b}h{h} dK cols")
+        assert_close(np64(dv)[b, cols, h], rv, f"{name} b{b}h{h} dV cols")
+    if grads is not None:
+        dq, dk, dv = grads
+        sdk = np64(dk).sum(axis=1)
+        assert np.abs(sdk).max() <= 1e-2 * np.abs(np64(dk)).sum(axis=1).max(), "sum dK != 0"
+        assert_close(np64(dv).sum(axis=1), do.sum(axis=1), f"{name} sum dV = sum dO",
+                     max_abs=2.0, rel_l2=1e-2)
+
+
+def test_workload_cp_rank_share(gpu_lib):
+    """Localize on the GPU, then attend; compare with the global problem."""
+    fm = gpu_lib
+    name = "c5_cp_rank3_of_8"
+    log(f"workload {name}: building inputs")
+    w = SC.build(name, seed=0)
+    loc = fm.fm_mask_localize(dev_mask(w.global_vectors), w.seq_q_global, w.chunk_start, w.chunk_len)
+    loc_ref = OM.localize(w.global_vectors, w.chunk_start, w.chunk_len)
+    for g, r in zip((loc.lts, loc.lte, loc.uts, loc.ute), loc_ref):
+        assert np.array_equal(g.cpu().numpy(), r)
+    (o, lse), (dq, dk, dv) = _run(fm, w, loc)
+    rng = np.random.default_rng(2)
+    qg = np64(ST.randn("q", (w.batch, w.seq_q_global, w.heads, w.head_dim), w.seed, w.dtype))
+    k, v, do_l = np64(w.k), np64(w.v), np64(w.do)
+    do_g = np.zeros_like(qg)
+    do_g[:, w.local_rows] = do_l
+    for h in rng.choice(w.heads, 3, replace=False):
+        rows = _sample_rows(w.seq_q, rng)
+        grows = w.local_rows[rows]
+        ro, rl = OA.forward_rows(qg, k, v, w.global_vectors, w.scale, 0, h, grows)
+        assert_close(np64(o)[0, rows, h], ro, f"cp h{h} O rows (global reference)")
+        assert_close(lse[0, h, rows].double().numpy(), rl, f"cp h{h} LSE rows (global reference)")
+        rq = OA.backward_rows(qg, k, v, do_g, w.global_vectors, w.scale, 0, h, grows)
+        assert_close(np64(dq)[0, rows, h], rq, f"cp h{h} dQ rows (global reference)")
+        cols = _sample_cols(loc_ref, w.seq_q, rng)
+        rk, rv = OA.backward_cols(np64(w.q), k, v, do_l, loc_ref, w.scale, 0, h, cols)
+        assert_close(np64(dk)[0, cols, h], rk, f"cp h{h} dK cols")
+        assert_close(np64(dv)[0, cols, h], rv, f"cp h{h} dV cols")

@@ -1,0 +1,166 @@
+"""Forward parity: HIP kernels (through the C ABI) vs the float64 oracle,
+element by element, at sizes spanning several tiles with ragged tails, plus
+the edge cases (fully masked rows, one row / one key, Sq != Sk, strided
+layouts, head_dim 64, float32 inputs) and determinism."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_close, dev_mask, log, np64
+from oracle import attention as OA
+from synth import masks as SM
+from synth import tensors as ST
+
+pytestmark = pytest.mark.gpu
+
+
+def _families(n, rng):
+    return {
+        "causal": SM.causal(n),
+        "document": SM.document_causal(SM.uniform_doc_lengths(rng, n, 40, 300)),
+        "window": SM.sliding_window_causal(n, 150),
+        "prefix_lm": SM.prefix_lm(n, n // 4),
+        "share_question": SM.share_question(n // 6, SM.answer_lengths(rng, n - n // 6, 5)),
+        "none": SM.no_mask(n, n),
+    }
+
+
+def _run_fwd(fm, q, k, v, vec, scale):
+    o, lse = fm.fm_attn_fwd(q.cuda(), k.cuda(), v.cuda(), dev_mask(vec), scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _compare_fwd(fm, q, k, v, vec, scale, tag):
+    log(f"fwd {tag} q={tuple(q.shape)} k={tuple(k.shape)} dtype={q.dtype}")
+    o, lse = _run_fwd(fm, q, k, v, vec, scale)
+    ro, rl = OA.forward(np64(q), np64(k), np64(v), vec, scale)
+    assert_close(np64(o), ro, f"{tag} O")
+    assert_close(lse.double().numpy(), rl, f"{tag} LSE")
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_fwd_mask_families(gpu_lib, d):
+    rng = np.random.default_rng(d)
+    n = 700
+    for name, v in _families(n, rng).items():
+        q, k, vv = ST.qkv(2, n, n, 3, d, seed=d + len(name))
+        _compare_fwd(gpu_lib, q, k, vv, tuple(x[None, None] for x in v), 1 / math.sqrt(d), f"{name} d={d}")
+
+
+def test_fwd_per_batch_and_head_masks(gpu_lib):
+    rng = np.random.default_rng(1)
+    n, B, H, d = 520, 2, 3, 128
+    per = [[list(_families(n, rng).values())[(b * H + h) % 6] for h in range(H)] for b in range(B)]
+    vec = SM.stack(per)
+    q, k, v = ST.qkv(B, n, n, H, d, seed=5)
+    _compare_fwd(gpu_lib, q, k, v, vec, 0.09, "per-(b,h) masks")
+
+
+def test_fwd_random_vectors_rectangular(gpu_lib):
+    """Random (non-canonical, out-of-range, overlapping) bounds with Sq != Sk;
+    includes fully masked rows (O = 0, LSE = -inf)."""
+    rng = np.random.default_rng(2)
+    for sq, sk in ((300, 900), (900, 300), (129, 65)):
+        vec = tuple(rng.integers(-20, sq + 20, (1, 1, sk)).astype(np.int32) for _ in range(4))
+        q, k, v = ST.qkv(1, sq, sk, 2, 128, seed=sq)
+        o, lse = _compare_fwd(gpu_lib, q, k, v, vec, 0.1, f"random {sq}x{sk}")
+        allowed = ~OA.dense_mask(*[x[0, 0].astype(np.int64) for x in vec], np.arange(sq), sk)
+        empty = ~allowed.any(axis=1)
+        if empty.any():
+            assert torch.all(o[:, torch.from_numpy(empty)] == 0)
+            assert torch.all(lse[:, :, torch.from_numpy(empty)] == -math.inf)
+
+
+def test_fwd_fully_masked_rows_and_tiles(gpu_lib):
+    """Rows 100..299 see no key at all: whole query tiles are SKIP everywhere."""
+    n = 600
+    j = np.arange(n)
+    lts = np.full(n, 100)
+    lte = np.full(n, 300)
+    uts = np.zeros(n, np.int64)
+    ute = j
+    vec = tuple(np.asarray(x, np.int32)[None, None] for x in (lts, lte, uts, ute))
+    q, k, v = ST.qkv(1, n, n, 2, 128, seed=9)
+    o, lse = _compare_fwd(gpu_lib, q, k, v, vec, 0.1, "masked rows 100..299")
+    assert torch.all(o[:, 100:300] == 0) and torch.all(lse[:, :, 100:300] == -math.inf)
+
+
+@pytest.mark.parametrize("sq,sk", [(1, 1), (1, 1000), (1000, 1), (64, 64), (128, 64), (127, 65)])
+def test_fwd_tiny_and_edge_shapes(gpu_lib, sq, sk):
+    rng = np.random.default_rng(sq * 7 + sk)
+    vec = tuple(rng.integers(-2, sq + 2, (1, 1, sk)).astype(np.int32) for _ in range(2)) + \
+        (np.zeros((1, 1, sk), np.int32), np.zeros((1, 1, sk), np.int32))
+    q, k, v = ST.qkv(1, sq, sk, 1, 64, seed=sq + sk)
+    _compare_fwd(gpu_lib, q, k, v, vec, 0.125, f"edge {sq}x{sk}")
+
+
+def test_fwd_q_zero_closed_form(gpu_lib):
+    """Q = 0: O_i is the mean of the open V rows and LSE_i = ln(open count)."""
+    n = 333
+    vec = tuple(x[None, None] for x in SM.sliding_window_causal(n, 50))
+    _, k, v = ST.qkv(1, n, n, 1, 128, seed=4)
+    q = torch.zeros((1, n, 1, 128), dtype=torch.bfloat16)
+    o, lse = _run_fwd(gpu_lib, q, k, v, vec, 0.3)
+    allowed = ~OA.dense_mask(*[x[0, 0].astype(np.int64) for x in vec], np.arange(n))
+    cnt = allowed.sum(axis=1)
+    assert_close(lse[0, 0].double().numpy(), np.log(cnt), "q=0 LSE")
+    vd = np64(v)[0, :, 0]
+    mean = (allowed.astype(np.float64) @ vd) / cnt[:, None]
+    assert_close(np64(o)[0, :, 0], mean, "q=0 O")
+
+
+def test_fwd_strided_layout(gpu_lib):
+    """[B, H, S, D] storage viewed as [B, S, H, D] (non-contiguous strides)."""
+    n, B, H, d = 400, 2, 2, 128
+    g = torch.Generator().manual_seed(3)
+    qh = torch.randn(B, H, n, d, generator=g).to(torch.bfloat16)
+    kh = torch.randn(B, H, n, d, generator=g).to(torch.bfloat16)
+    vh = torch.randn(B, H, n, d, generator=g).to(torch.bfloat16)
+    q, k, v = (t.cuda().transpose(1, 2) for t in (qh, kh, vh))
+    vec = tuple(x[None, None] for x in SM.causal(n))
+    o, lse = gpu_lib.fm_attn_fwd(q, k, v, dev_mask(vec), 0.08)
+    torch.cuda.synchronize()
+    ro, rl = OA.forward(np64(q), np64(k), np64(v), vec, 0.08)
+    assert_close(np64(o), ro, "strided O")
+    assert_close(lse.cpu().double().numpy(), rl, "strided LSE")
+
+
+def test_fwd_float32_inputs(gpu_lib):
+    """Float32 inputs (rounded to bf16 for the products, fp32 softmax state and
+    outputs): the tiny causal workload at its full size."""
+    from synth import configs as SC
+    w = SC.build("c1_tiny_causal", 0)
+    _compare_fwd(gpu_lib, w.q, w.k, w.v, w.vectors, w.scale, "c1 fp32")
+
+
+def test_fwd_key_permutation(gpu_lib):
+    """Permuting K, V and the four vectors by one permutation changes nothing
+    beyond rounding (exercises PARTIAL tiles everywhere)."""
+    n = 500
+    rng = np.random.default_rng(8)
+    vec = tuple(x[None, None] for x in SM.document_causal(SM.uniform_doc_lengths(rng, n, 30, 120)))
+    q, k, v = ST.qkv(1, n, n, 2, 128, seed=8)
+    perm = rng.permutation(n)
+    pv = tuple(x[..., perm] for x in vec)
+    o1, l1 = _run_fwd(gpu_lib, q, k, v, vec, 0.1)
+    tp = torch.from_numpy(perm)
+    o2, l2 = _run_fwd(gpu_lib, q, k[:, tp].contiguous(), v[:, tp].contiguous(), pv, 0.1)
+    ro, rl = OA.forward(np64(q), np64(k), np64(v), vec, 0.1)
+    assert_close(np64(o2), ro, "permuted O")
+    assert_close(l2.double().numpy(), rl, "permuted LSE")
+    assert_close(np64(o1), np64(o2), "O vs permuted O")
+
+
+def test_fwd_deterministic(gpu_lib):
+    n = 1000
+    vec = tuple(x[None, None] for x in SM.causal(n))
+    q, k, v = (t.cuda() for t in ST.qkv(2, n, n, 4, 128, seed=1))
+    m = dev_mask(vec)
+    o1, l1 = gpu_lib.fm_attn_fwd(q, k, v, m, 0.1)
+    o2, l2 = gpu_lib.fm_attn_fwd(q, k, v, m, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
