@@ -1,0 +1,243 @@
+"""Benchmark: masked attention forward + backward on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+tile classification, forward kernel, backward pre-pass, backward kernel and
+dQ finalize (plus mask localization for the context-parallel rank share).
+Inputs are resident in HBM before the timed region starts.
+
+Metric: TFLOP/s counted over UNMASKED pairs only (forward 4*d*NNZ, backward
+10*d*NNZ, NNZ = exact number of open (query, key) pairs summed over batch and
+heads) and that figure as a fraction of the bf16 dense MFMA peak.
+
+Prints ONE JSON line. Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--seed S] [--no-cpu-baseline] [--no-sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "masked attn fwd/bwd TFLOP/s on unmasked FLOPs, % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+HEADLINE = "c4_doc_causal_128k"
+
+
+def nnz_of(vectors, seq_q, batch, heads):
+    """Exact open-pair count from the bound vectors, O(Sk) per (b, h)."""
+    total = 0
+    for b in range(batch):
+        for h in range(heads):
+            pick = lambda x: x[b if x.shape[0] > 1 else 0, h if x.shape[1] > 1 else 0].astype(np.int64)
+            lts, lte, uts, ute = (pick(x) for x in vectors)
+            a0, a1 = np.clip(lts, 0, seq_q), np.clip(lte, 0, seq_q)
+            b0, b1 = np.clip(uts, 0, seq_q), np.clip(ute, 0, seq_q)
+            a1, b1 = np.maximum(a1, a0), np.maximum(b1, b0)
+            inter = np.maximum(0, np.minimum(a1, b1) - np.maximum(a0, b0))
+            total += int((seq_q - ((a1 - a0) + (b1 - b0) - inter)).sum())
+    return total
+
+
+class Runner:
+    """Device-resident inputs, outputs and workspaces of one workload."""
+
+    def __init__(self, fm, w, torch):
+        self.fm, self.w, self.t = fm, w, torch
+        dev = "cuda"
+        self.q, self.k, self.v = (x.to(dev) for x in (w.q, w.k, w.v))
+        self.do = w.do.to(dev) if w.backward else None
+        if w.global_vectors is not None:
+            self.gmask = fm.Mask.from_vectors(w.global_vectors, dev)
+            self.mask = fm.fm_mask_localize(self.gmask, w.seq_q_global, w.chunk_start, w.chunk_len)
+            torch.cuda.synchronize()
+            self.vectors = tuple(x.cpu().numpy() for x in (self.mask.lts, self.mask.lte,
+                                                           self.mask.uts, self.mask.ute))
+        else:
+            self.gmask = None
+            self.mask = fm.Mask.from_vectors(w.vectors, dev)
+            self.vectors = w.vectors
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
+        ws_f = fm.fm_workspace_size(self.q, self.k, self.v, self.mask, False, w.scale)
+        self.ws_f = torch.empty(ws_f, dtype=torch.uint8, device=dev)
+        if w.backward:
+            ws_b = fm.fm_workspace_size(self.q, self.k, self.v, self.mask, True, w.scale)
+            self.ws_b = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+            self.dq, self.dk, self.dv = (torch.empty_like(x) for x in (self.q, self.k, self.v))
+        self.nnz = nnz_of(self.vectors, w.seq_q, w.batch, w.heads)
+
+    def step(self):
+        fm, w = self.fm, self.w
+        if self.gmask is not None:
+            self.mask = fm.fm_mask_localize(self.gmask, w.seq_q_global, w.chunk_start, w.chunk_len)
+        fm.fm_attn_fwd(self.q, self.k, self.v, self.mask, w.scale, o=self.o, lse=self.lse,
+                       workspace=self.ws_f)
+        if w.backward:
+            fm.fm_attn_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.mask, w.scale,
+                           dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_b)
+
+    def flops(self):
+        d = self.w.head_dim
+        return 4 * d * self.nnz, (10 * d * self.nnz if self.w.backward else 0)
+
+
+def time_steps(r, steps, warmup, torch, profile=True):
+    fm = r.fm
+    for _ in range(warmup):
+        r.step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if profile:
+        fm.fm_profile_begin(64 * steps + 64)
+    start.record()
+    for _ in range(steps):
+        r.step()
+    stop.record()
+    torch.cuda.synchronize()
+    stages = fm.fm_profile_end() if profile else {}
+    ms = start.elapsed_time(stop) / steps
+    return ms, stages
+
+
+def cpu_baseline(w, vectors, budget_rows=None):
+    """The oracle (float64 numpy, as it stands) on a bounded sample of the
+    same workload: forward + backward of a contiguous block of query rows of
+    head 0 against all keys (the block as a sub-problem: its rows are a
+    single chunk, the vectors localized to it by the oracle)."""
+    from oracle import attention as OA
+    from oracle import masks as OM
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    d = w.head_dim
+    rows = budget_rows or max(128, min(w.seq_q, int(5e9 / (w.seq_k * d))))
+    r0 = max(0, (w.seq_q - rows) // 2)
+    loc = OM.localize(tuple(x[:1, :1] for x in vectors), [r0], [rows])
+    q = w.q[:1, r0:r0 + rows, :1].double().numpy()
+    k = w.k[:1, :, :1].double().numpy()
+    v = w.v[:1, :, :1].double().numpy()
+    nnz = OA.nnz_closed_form(loc, rows)
+    t0 = time.perf_counter()
+    OA.forward(q, k, v, loc, w.scale, block=256)
+    flops = 4 * d * nnz
+    if w.backward:
+        do = w.do[:1, r0:r0 + rows, :1].double().numpy()
+        OA.backward(q, k, v, do, loc, w.scale, block=256)
+        flops += 10 * d * nnz
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: query rows [{r0}, {r0 + rows}) of batch 0 head 0 against all "
+                      f"{w.seq_k} keys, fwd{'+bwd' if w.backward else ''}, nnz {nnz}, "
+                      f"{dt:.1f} s, float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels shard over (batch, head) with no exchange, but no multi-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import masked_tiled_attention_amd as fm
+    from synth import configs as SC
+
+    fm.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    log(f"[bench] building {args.workload} seed {args.seed}")
+    w = SC.build(args.workload, args.seed)
+    r = Runner(fm, w, torch)
+    ms, stages = time_steps(r, args.steps, args.warmup, torch)
+    f_fwd, f_bwd = r.flops()
+    per = lambda s: stages[s][0] / max(1, args.steps)
+    fwd_ms = per("classify_summary") / (2 if w.backward else 1) + per("classify_map") / (2 if w.backward else 1) + per("fwd")
+    bwd_ms = (per("classify_summary") + per("classify_map")) / 2 + per("bwd_pre") + per("bwd") + per("dq_finalize") \
+        if w.backward else 0.0
+    total_tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
+    log(f"[bench] {w.name}: {ms:.3f} ms/step, {total_tflops:.1f} TFLOP/s")
+
+    # dominant kernel: the one with the largest time per step
+    kern = max(("fwd", "bwd"), key=lambda s: stages[s][0])
+    kflops = f_fwd if kern == "fwd" else f_bwd
+    kms = stages[kern][0] / max(1, stages[kern][1])
+    achieved = kflops / (kms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(total_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_q": w.seq_q,
+                   "seq_k": w.seq_k, "head_dim": w.head_dim, "seed": args.seed,
+                   "passes": "fwd+bwd" if w.backward else "fwd", "nnz": r.nnz,
+                   "density": round(r.nnz / (w.batch * w.heads * w.seq_q * w.seq_k), 5)},
+        "pct_of_bf16_peak": round(100 * total_tflops / PEAK_BF16_TFLOPS, 2),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None},
+        "stages_ms_per_step": {s: round(v[0] / max(1, args.steps), 4) for s, v in stages.items() if v[1]},
+        "roofline": {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, r.vectors)
+    if not args.no_sweep:
+        sweep = []
+        del r
+        torch.cuda.empty_cache()
+        for name in SC.NAMES:
+            if name == args.workload:
+                continue
+            log(f"[bench] sweep {name}")
+            wx = SC.build(name, args.seed)
+            rx = Runner(fm, wx, torch)
+            msx, st = time_steps(rx, 5, 2, torch)
+            a, b = rx.flops()
+            pf = lambda s: st[s][0] / 5
+            item = {"workload": name, "nnz": rx.nnz, "ms_per_step": round(msx, 4),
+                    "tflops": round((a + b) / (msx * 1e-3) / 1e12, 2),
+                    "fwd_kernel_tflops": round(a / (pf("fwd") * 1e-3) / 1e12, 2)}
+            if wx.backward:
+                item["bwd_kernel_tflops"] = round(b / (pf("bwd") * 1e-3) / 1e12, 2)
+            if wx.global_vectors is not None:
+                item["localize_ms"] = round(pf("localize"), 4)
+            sweep.append(item)
+            del rx
+            torch.cuda.empty_cache()
+        out["workloads"] = sweep
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

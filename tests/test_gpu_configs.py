@@ -30,7 +30,18 @@ def _open_count_per_key(vec, sq):
 
 
 def _sample_rows(sq, rng, k=24):
-    return np.unique(np.concatenate([[0, 1, sq // 2, sq - 2, sq - 1], rng.choice(sq, k, replace=False)]))
+    """(uniformly drawn rows, edge rows). The relative L2 bar is defined over
+    the whole tensor, so it is estimated on the uniform draw only; the
+    max-abs bar is checked on both."""
+    uni = np.sort(rng.choice(sq, min(k, sq), replace=False))
+    edge = np.unique(np.asarray([0, 1, sq // 2, sq - 2, sq - 1]) % sq)
+    return uni, edge
+
+
+def _check_rows(got, ref, n_uni, name):
+    """got/ref hold the uniform rows first, then the edge rows."""
+    assert_close(got[:n_uni], ref[:n_uni], name + " (uniform rows)")
+    assert_close(got[n_uni:], ref[n_uni:], name + " (edge rows)", rel_l2=np.inf)
 
 
 def _sample_cols(vec, sq, rng, budget=3000, k=12):
@@ -73,15 +84,19 @@ def test_workload_full_size(gpu_lib, name):
     if len(heads) > 4:
         heads = [heads[i] for i in rng.choice(len(heads), 4, replace=False)]
     for b, h in heads:
-        rows = _sample_rows(w.seq_q, rng) if w.seq_q > 512 else np.arange(w.seq_q)
+        if w.seq_q > 512:
+            uni, edge = _sample_rows(w.seq_q, rng)
+        else:
+            uni, edge = np.arange(w.seq_q), np.zeros(0, dtype=np.int64)
+        rows = np.concatenate([uni, edge])
         ro, rl = OA.forward_rows(q, k, v, w.vectors, w.scale, b, h, rows)
-        assert_close(np64(o)[b, rows, h], ro, f"{name} b{b}h{h} O rows")
-        assert_close(lse[b, h, rows].double().numpy(), rl, f"{name} b{b}h{h} LSE rows")
+        _check_rows(np64(o)[b, rows, h], ro, len(uni), f"{name} b{b}h{h} O")
+        _check_rows(lse[b, h, rows].double().numpy(), rl, len(uni), f"{name} b{b}h{h} LSE")
         if grads is None:
             continue
         dq, dk, dv = grads
         rq = OA.backward_rows(q, k, v, do, w.vectors, w.scale, b, h, rows)
-        assert_close(np64(dq)[b, rows, h], rq, f"{name} b{b}h{h} dQ rows")
+        _check_rows(np64(dq)[b, rows, h], rq, len(uni), f"{name} b{b}h{h} dQ")
         vb = tuple(None if x is None else x[[b if x.shape[0] > 1 else 0]][:, [h if x.shape[1] > 1 else 0]]
                    for x in w.vectors)
         cols = _sample_cols(vb, w.seq_q, rng)
@@ -113,13 +128,14 @@ def test_workload_cp_rank_share(gpu_lib):
     do_g = np.zeros_like(qg)
     do_g[:, w.local_rows] = do_l
     for h in rng.choice(w.heads, 3, replace=False):
-        rows = _sample_rows(w.seq_q, rng)
+        uni, edge = _sample_rows(w.seq_q, rng)
+        rows = np.concatenate([uni, edge])
         grows = w.local_rows[rows]
         ro, rl = OA.forward_rows(qg, k, v, w.global_vectors, w.scale, 0, h, grows)
-        assert_close(np64(o)[0, rows, h], ro, f"cp h{h} O rows (global reference)")
-        assert_close(lse[0, h, rows].double().numpy(), rl, f"cp h{h} LSE rows (global reference)")
+        _check_rows(np64(o)[0, rows, h], ro, len(uni), f"cp h{h} O (global reference)")
+        _check_rows(lse[0, h, rows].double().numpy(), rl, len(uni), f"cp h{h} LSE (global reference)")
         rq = OA.backward_rows(qg, k, v, do_g, w.global_vectors, w.scale, 0, h, grows)
-        assert_close(np64(dq)[0, rows, h], rq, f"cp h{h} dQ rows (global reference)")
+        _check_rows(np64(dq)[0, rows, h], rq, len(uni), f"cp h{h} dQ (global reference)")
         cols = _sample_cols(loc_ref, w.seq_q, rng)
         rk, rv = OA.backward_cols(np64(w.q), k, v, do_l, loc_ref, w.scale, 0, h, cols)
         assert_close(np64(dk)[0, cols, h], rk, f"cp h{h} dK cols")
