@@ -36,25 +36,44 @@ constexpr int BQ = kFwdBlockQ;   // 128 query rows per workgroup
 constexpr int BK = kFwdBlockK;   // 64 keys per K/V tile
 constexpr int NW = BQ / 32;      // 4 wavefronts
 constexpr int NT = NW * 64;      // 256 threads
-constexpr int LIST_CAP = 2048;   // class bytes compacted per pass (8 per thread)
+constexpr int LIST_CAP = 1024;   // class bytes compacted per pass (4 per thread)
 constexpr uint32_t kPartialBit = 0x80000000u;
+
+// V^T rows hold the tile's keys in groups of 4 (8 bytes). Group kg of channel
+// row c is stored at group kg ^ vswz(c): with unpadded 128-byte rows this makes
+// both the transposing writes (16 lanes -> 16 rows 8 apart) and the MFMA
+// operand reads (16 lanes -> 16 consecutive rows) hit 16 distinct 8-byte bank
+// slots.
+__device__ __forceinline__ int vswz(int c) { return (c & 15) ^ ((c >> 3) & 15); }
 
 template <int D>
 struct alignas(16) FwdSmem {
-  static constexpr int KP = D + 8;    // padded K row (elements): rows shift by 4 banks
-  static constexpr int VP = BK + 4;   // padded V^T row (elements)
-  uint16_t k[BK][KP];
-  uint16_t vt[D][VP];
-  int32_t bnd[4][BK];                 // lts, lte, uts, ute of the tile's columns
+  static constexpr int KP = D + 8;    // padded K row (elements): 8 consecutive rows, 8 bank slots
+  uint16_t k[2][BK][KP];              // double-buffered K tile, row-major
+  uint16_t vt[2][D][BK];              // double-buffered V tile, transposed and swizzled
+  int32_t bnd[2][4][BK];              // lts, lte, uts, ute of the tile's columns
   uint32_t list[LIST_CAP];            // non-SKIP key tiles (kt | partial bit)
   int32_t scan[NW];
 };
 
+// Registers carrying one K/V tile from global memory to LDS.
+template <int D>
+struct TileRegs {
+  static constexpr int KR = (BK * D / 8) / NT;                 // 16-byte K chunks per thread
+  static constexpr int VG = (BK / 4) * (D / 8);                // 4-key x 8-channel V groups
+  static constexpr int VR = (VG + NT - 1) / NT;                // V groups per thread
+  u32x4 k[KR];
+  u32x4 v[VR][4];
+  int32_t b[4];
+};
+
 template <int D, bool F32>
-__global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel(FwdArgs a) {
   constexpr int KSTEPS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int CB = D / 32;       // 32-channel blocks of O^T
   constexpr int NB = BK / 32;      // 32-key blocks of a tile
+  using TR = TileRegs<D>;
   __shared__ FwdSmem<D> sm;
 
   const int tid = threadIdx.x;
@@ -98,6 +117,83 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
   const float C = a.scale_log2;
   const bool ragged_k = (a.seq_k % BK) != 0;
 
+  // ---- global -> registers for key tile kt ----
+  auto load_tile = [&](TR& r, int kt, bool masked) {
+    const int n0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < TR::KR; ++i) {
+      const int ci = tid + i * NT;
+      const int n = n0 + ci / (D / 8);
+      const int c8 = ci % (D / 8);
+      r.k[i] = n < a.seq_k ? load8_as_bf16<F32>(a.k, (int64_t)b * a.k_sb + (int64_t)n * a.k_ss +
+                                                         (int64_t)h * a.k_sh + 8 * c8)
+                           : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < TR::VR; ++i) {
+      const int gi = tid + i * NT;
+      const int kq = gi / (D / 8);
+      const int c8 = gi % (D / 8);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int n = n0 + 4 * kq + rr;
+        r.v[i][rr] = (gi < TR::VG && n < a.seq_k)
+                         ? load8_as_bf16<F32>(a.v, (int64_t)b * a.v_sb + (int64_t)n * a.v_ss +
+                                                       (int64_t)h * a.v_sh + 8 * c8)
+                         : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (masked && tid < BK) {
+      const int n = n0 + tid;
+      if (n < a.seq_k) {
+        r.b[0] = a.mask.has_lower ? a.mask.lts[mbase + n] : a.seq_q;
+        r.b[1] = a.mask.has_lower ? a.mask.lte[mbase + n] : a.seq_q;
+        r.b[2] = a.mask.has_upper ? a.mask.uts[mbase + n] : 0;
+        r.b[3] = a.mask.has_upper ? a.mask.ute[mbase + n] : 0;
+      } else {   // keys past the end: masked for every row
+        r.b[0] = INT_MIN;
+        r.b[1] = INT_MAX;
+        r.b[2] = 0;
+        r.b[3] = 0;
+      }
+    }
+  };
+
+  // ---- registers -> LDS buffer buf (K row-major, V transposed) ----
+  auto store_tile = [&](const TR& r, int buf, bool masked) {
+#pragma unroll
+    for (int i = 0; i < TR::KR; ++i) {
+      const int ci = tid + i * NT;
+      *reinterpret_cast<u32x4*>(&sm.k[buf][ci / (D / 8)][8 * (ci % (D / 8))]) = r.k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < TR::VR; ++i) {
+      const int gi = tid + i * NT;
+      if (gi < TR::VG) {
+        const int kq = gi / (D / 8);
+        const int c8 = gi % (D / 8);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int ce = 8 * c8 + 2 * p;
+          u32x2 ev, od;
+          ev[0] = (r.v[i][0][p] & 0xffffu) | (r.v[i][1][p] << 16);
+          ev[1] = (r.v[i][2][p] & 0xffffu) | (r.v[i][3][p] << 16);
+          od[0] = (r.v[i][0][p] >> 16) | (r.v[i][1][p] & 0xffff0000u);
+          od[1] = (r.v[i][2][p] >> 16) | (r.v[i][3][p] & 0xffff0000u);
+          *reinterpret_cast<u32x2*>(&sm.vt[buf][ce][4 * (kq ^ vswz(ce))]) = ev;
+          *reinterpret_cast<u32x2*>(&sm.vt[buf][ce + 1][4 * (kq ^ vswz(ce + 1))]) = od;
+        }
+      }
+    }
+    if (masked && tid < BK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.bnd[buf][j][tid] = r.b[j];
+    }
+  };
+
+  TR regs;
+  int it_global = 0;   // iteration count across chunks (selects the LDS buffer)
+
   for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
     // ---- compact the non-SKIP key tiles of this row of the class map ----
     const int n_in = min(LIST_CAP, a.tk - kt0);
@@ -115,7 +211,7 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
       const int y = __shfl_up(incl, o, 64);
       if (l >= o) incl += y;
     }
-    __syncthreads();   // previous pass finished reading sm.list / sm.scan
+    __syncthreads();   // all waves are done with sm.list, sm.scan and both LDS buffers
     if (l == 63) sm.scan[w] = incl;
     __syncthreads();
     int pos = incl - cnt, n_list = 0;
@@ -132,67 +228,23 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
       }
     }
     __syncthreads();
+    if (n_list == 0) continue;
 
-    for (int it = 0; it < n_list; ++it) {
-      const uint32_t ent = sm.list[it];
-      const int kt = (int)(ent & ~kPartialBit);
-      const bool masked_tile = (ent & kPartialBit) || (ragged_k && kt == a.tk - 1);
-      const int n0 = kt * BK;
+    auto masked_of = [&](uint32_t ent) {
+      return (ent & kPartialBit) || (ragged_k && (int)(ent & ~kPartialBit) == a.tk - 1);
+    };
+    uint32_t ent = sm.list[0];
+    load_tile(regs, (int)(ent & ~kPartialBit), masked_of(ent));
 
-      // ---- stage K (row-major) and V (transposed) tiles in LDS ----
-#pragma unroll
-      for (int r = 0; r < (BK * D / 8) / NT; ++r) {
-        const int ci = tid + r * NT;
-        const int row = ci / (D / 8);
-        const int c8 = ci % (D / 8);
-        const int n = n0 + row;
-        u32x4 val = u32x4{0u, 0u, 0u, 0u};
-        if (n < a.seq_k)
-          val = load8_as_bf16<F32>(a.k, (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)h * a.k_sh + 8 * c8);
-        *reinterpret_cast<u32x4*>(&sm.k[row][8 * c8]) = val;
+    for (int it = 0; it < n_list; ++it, ++it_global) {
+      const int buf = it_global & 1;
+      const bool masked_tile = masked_of(ent);
+      store_tile(regs, buf, masked_tile);
+      __syncthreads();   // tile `buf` visible; the other buffer is free
+      if (it + 1 < n_list) {   // next tile's global loads overlap this tile's math
+        ent = sm.list[it + 1];
+        load_tile(regs, (int)(ent & ~kPartialBit), masked_of(ent));
       }
-      for (int gi = tid; gi < (BK / 4) * (D / 8); gi += NT) {
-        const int kq = gi / (D / 8);
-        const int c8 = gi % (D / 8);
-        u32x4 rv[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = n0 + 4 * kq + r;
-          rv[r] = u32x4{0u, 0u, 0u, 0u};
-          if (n < a.seq_k)
-            rv[r] = load8_as_bf16<F32>(a.v, (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)h * a.v_sh + 8 * c8);
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          u32x2 ev, od;
-          ev[0] = (rv[0][p] & 0xffffu) | (rv[1][p] << 16);
-          ev[1] = (rv[2][p] & 0xffffu) | (rv[3][p] << 16);
-          od[0] = (rv[0][p] >> 16) | (rv[1][p] & 0xffff0000u);
-          od[1] = (rv[2][p] >> 16) | (rv[3][p] & 0xffff0000u);
-          *reinterpret_cast<u32x2*>(&sm.vt[8 * c8 + 2 * p][4 * kq]) = ev;
-          *reinterpret_cast<u32x2*>(&sm.vt[8 * c8 + 2 * p + 1][4 * kq]) = od;
-        }
-      }
-      if (masked_tile && tid < BK) {
-        const int n = n0 + tid;
-        int32_t v0, v1, v2, v3;
-        if (n < a.seq_k) {
-          v0 = a.mask.has_lower ? a.mask.lts[mbase + n] : a.seq_q;
-          v1 = a.mask.has_lower ? a.mask.lte[mbase + n] : a.seq_q;
-          v2 = a.mask.has_upper ? a.mask.uts[mbase + n] : 0;
-          v3 = a.mask.has_upper ? a.mask.ute[mbase + n] : 0;
-        } else {   // keys past the end: masked for every row
-          v0 = INT_MIN;
-          v1 = INT_MAX;
-          v2 = 0;
-          v3 = 0;
-        }
-        sm.bnd[0][tid] = v0;
-        sm.bnd[1][tid] = v1;
-        sm.bnd[2][tid] = v2;
-        sm.bnd[3][tid] = v3;
-      }
-      __syncthreads();
 
       // ---- S^T = K Q^T ----
       f32x16 sacc[NB];
@@ -201,7 +253,7 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
         sacc[nb] = f32x16{};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(&sm.k[nb * 32 + lr][16 * s + 8 * g]);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(&sm.k[buf][nb * 32 + lr][16 * s + 8 * g]);
           sacc[nb] = mfma32(kf, qf[s], sacc[nb]);
         }
       }
@@ -213,8 +265,8 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int nl = nb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool mk = (sm.bnd[0][nl] <= m && m < sm.bnd[1][nl]) ||
-                            (sm.bnd[2][nl] <= m && m < sm.bnd[3][nl]);
+            const bool mk = (sm.bnd[buf][0][nl] <= m && m < sm.bnd[buf][1][nl]) ||
+                            (sm.bnd[buf][2][nl] <= m && m < sm.bnd[buf][3][nl]);
             if (mk) sacc[nb][i] = -INFINITY;
           }
         }
@@ -242,10 +294,12 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
         }
       l_run = l_run * alpha + rs;
       m_run = m_new;
+      if (__any(alpha != 1.f)) {   // wave-uniform: skipped once the row maxima settle
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+          for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+      }
 
       // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -255,17 +309,17 @@ __global__ __launch_bounds__(NT) void fwd_kernel(FwdArgs a) {
           u32x4 pf;
 #pragma unroll
           for (int j = 0; j < 4; ++j) pf[j] = pack_bf16(sacc[nb][8 * t + 2 * j], sacc[nb][8 * t + 2 * j + 1]);
-          const int kb = nb * 32 + 16 * t + 4 * g;
+          const int kg = 8 * nb + 4 * t + g;   // 4-key group of this lane's first 4 keys
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.vt[cb * 32 + lr][kb]);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.vt[cb * 32 + lr][kb + 8]);
-            const u32x4 va = u32x4{lo[0], lo[1], hi[0], hi[1]};
-            oacc[cb] = mfma32(va, pf, oacc[cb]);
+            const int c = cb * 32 + lr;
+            const int sw = vswz(c);
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.vt[buf][c][4 * (kg ^ sw)]);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.vt[buf][c][4 * ((kg + 2) ^ sw)]);
+            oacc[cb] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, oacc[cb]);
           }
         }
       }
-      __syncthreads();   // LDS tiles are overwritten by the next iteration
     }
   }
 
