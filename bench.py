@@ -173,15 +173,21 @@ def main():
     ms, stages = time_steps(r, args.steps, args.warmup, torch)
     f_fwd, f_bwd = r.flops()
     per = lambda s: stages[s][0] / max(1, args.steps)
-    fwd_ms = per("classify_summary") / (2 if w.backward else 1) + per("classify_map") / (2 if w.backward else 1) + per("fwd")
-    bwd_ms = (per("classify_summary") + per("classify_map")) / 2 + per("bwd_pre") + per("bwd") + per("dq_finalize") \
-        if w.backward else 0.0
+    # classification runs once in the forward and twice in the backward (one
+    # per backward kernel tiling); its small cost is split in that ratio
+    cls_ms = per("classify_summary") + per("classify_map")
+    fwd_ms = per("fwd") + (cls_ms / 3 if w.backward else cls_ms)
+    bwd_ms = per("bwd_pre") + per("bwd") + per("bwd_dq") + 2 * cls_ms / 3 if w.backward else 0.0
     total_tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
     log(f"[bench] {w.name}: {ms:.3f} ms/step, {total_tflops:.1f} TFLOP/s")
 
-    # dominant kernel: the one with the largest time per step
-    kern = max(("fwd", "bwd"), key=lambda s: stages[s][0])
-    kflops = f_fwd if kern == "fwd" else f_bwd
+    # dominant kernel: the one with the largest time per step. Executed matrix
+    # flops per open pair: forward 4d (QK^T, PV), dK/dV kernel 8d (QK^T, dO V^T,
+    # P^T dO, dS^T Q), dQ kernel 6d (QK^T, dO V^T, dS K).
+    d = w.head_dim
+    kernel_flops = {"fwd": 4 * d * r.nnz, "bwd": 8 * d * r.nnz, "bwd_dq": 6 * d * r.nnz}
+    kern = max((k for k in kernel_flops if stages[k][1]), key=lambda s: stages[s][0])
+    kflops = kernel_flops[kern]
     kms = stages[kern][0] / max(1, stages[kern][1])
     achieved = kflops / (kms * 1e-3) / 1e12
     out = {
@@ -205,7 +211,8 @@ def main():
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None},
         "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None},
         "stages_ms_per_step": {s: round(v[0] / max(1, args.steps), 4) for s, v in stages.items() if v[1]},
-        "roofline": {"bound": "mfma", "kernel": kern, "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": kern, "kernel_ms": round(kms, 4),
+                     "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }
@@ -229,7 +236,9 @@ def main():
                     "tflops": round((a + b) / (msx * 1e-3) / 1e12, 2),
                     "fwd_kernel_tflops": round(a / (pf("fwd") * 1e-3) / 1e12, 2)}
             if wx.backward:
-                item["bwd_kernel_tflops"] = round(b / (pf("bwd") * 1e-3) / 1e12, 2)
+                item["dkdv_kernel_tflops"] = round(8 * wx.head_dim * rx.nnz / (pf("bwd") * 1e-3) / 1e12, 2)
+                item["dq_kernel_tflops"] = round(6 * wx.head_dim * rx.nnz / (pf("bwd_dq") * 1e-3) / 1e12, 2)
+                item["bwd_tflops"] = round(b / ((pf("bwd") + pf("bwd_dq") + pf("bwd_pre")) * 1e-3) / 1e12, 2)
             if wx.global_vectors is not None:
                 item["localize_ms"] = round(pf("localize"), 4)
             sweep.append(item)

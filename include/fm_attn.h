@@ -116,8 +116,8 @@ typedef struct {
 void fm_kernel_tile(int32_t head_dim, int32_t bwd, int32_t* block_q, int32_t* block_k);
 
 /* Bytes of device workspace fm_attn_fwd (with_bwd = 0) or fm_attn_bwd
- * (with_bwd = 1) needs: tile summaries and class map, plus for the backward
- * the row terms D and the float32 dQ accumulator. */
+ * (with_bwd = 1) needs: tile summaries and class maps, plus for the backward
+ * the row terms D = rowsum(dO * O). */
 fm_status fm_workspace_size(const fm_problem* problem, const fm_mask* mask,
                             int32_t with_bwd, size_t* bytes);
 
@@ -153,8 +153,9 @@ fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, c
 /* Backward. Inputs q, k, v, o (the forward output), lse (the forward LSE),
  * dout (gradient of o), all device. Outputs dq, dk, dv (device, problem
  * dtype, shapes of q, k, v). workspace: device, at least
- * fm_workspace_size(.., 1) bytes, 256-byte aligned. dQ is accumulated in
- * float32 with atomics, so its last bits may differ from run to run. */
+ * fm_workspace_size(.., 1) bytes, 256-byte aligned. dK/dV come from a
+ * key-stationary kernel and dQ from a query-stationary one; both recompute
+ * the probabilities from lse, use no atomics and are deterministic. */
 fm_status fm_attn_bwd(const fm_problem* problem, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, const fm_mask* mask,
                       void* dq, void* dk, void* dv,
@@ -190,8 +191,8 @@ typedef enum {
   FM_STAGE_CLASSIFY_MAP = 1,
   FM_STAGE_FWD = 2,
   FM_STAGE_BWD_PRE = 3,
-  FM_STAGE_BWD = 4,
-  FM_STAGE_DQ_FINALIZE = 5,
+  FM_STAGE_BWD = 4,         /* dK / dV kernel */
+  FM_STAGE_BWD_DQ = 5,      /* dQ kernel */
   FM_STAGE_LOCALIZE = 6,
   FM_NUM_STAGES = 7
 } fm_stage;

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfmattn.s
 FM_OK, FM_ERR_INVALID_ARGUMENT, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_HIP = range(5)
 FM_BF16, FM_FP32 = 0, 1
 FM_TILE_SKIP, FM_TILE_PARTIAL, FM_TILE_FULL = 0, 1, 2
-STAGES = ("classify_summary", "classify_map", "fwd", "bwd_pre", "bwd", "dq_finalize", "localize")
+STAGES = ("classify_summary", "classify_map", "fwd", "bwd_pre", "bwd", "bwd_dq", "localize")
 FM_NUM_STAGES = len(STAGES)
 
 STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_INVALID_ARGUMENT", 2: "FM_ERR_UNSUPPORTED",

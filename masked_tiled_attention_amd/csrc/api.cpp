@@ -123,26 +123,32 @@ fm_status check_ptr(const void* ptr, const char* name) {
   return FM_OK;
 }
 
+// Workspace: per tiling one summary [Bm][Hm][Tk][8] int32 and one class map
+// [Bm][Hm][Tq][Tk] uint8 (forward: the forward tiles; backward: the dK/dV
+// tiles, transposed, and the dQ tiles), plus D [B][H][Sq] float32 for the
+// backward. 256-byte aligned sections.
 struct Layout {
-  size_t summary = 0, map = 0, drow = 0, dqacc = 0, total = 0;
+  size_t summary = 0, map = 0, summary_q = 0, map_q = 0, drow = 0, total = 0;
 };
 
 Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
   Layout L;
-  const int64_t bq = bwd ? fm::kBwdBlockQ : fm::kFwdBlockQ;
-  const int64_t bk = bwd ? fm::kBwdBlockK : fm::kFwdBlockK;
-  const int64_t tq = ceil_div(p->seqlen_q, bq), tk = ceil_div(p->seqlen_k, bk);
   const int64_t bh = (int64_t)m->batch * m->heads;
   size_t off = 0;
-  L.summary = off;
-  off = align256(off + (size_t)(bh * tk * 8 * 4));
-  L.map = off;
-  off = align256(off + (size_t)(bh * tq * tk));
+  auto add_tiling = [&](int64_t bq, int64_t bk, size_t* summary, size_t* map) {
+    const int64_t tq = ceil_div(p->seqlen_q, bq), tk = ceil_div(p->seqlen_k, bk);
+    *summary = off;
+    off = align256(off + (size_t)(bh * tk * 8 * 4));
+    *map = off;
+    off = align256(off + (size_t)(bh * tq * tk));
+  };
   if (bwd) {
+    add_tiling(fm::kBwdBlockQ, fm::kBwdBlockK, &L.summary, &L.map);
+    add_tiling(fm::kDqBlockQ, fm::kDqBlockK, &L.summary_q, &L.map_q);
     L.drow = off;
     off = align256(off + (size_t)p->batch * p->heads * p->seqlen_q * 4);
-    L.dqacc = off;
-    off = align256(off + (size_t)p->batch * p->seqlen_q * p->heads * p->head_dim * 4);
+  } else {
+    add_tiling(fm::kFwdBlockQ, fm::kFwdBlockK, &L.summary, &L.map);
   }
   L.total = off;
   return L;
@@ -284,11 +290,17 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
     return fail(FM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
   const int32_t tq = (int32_t)ceil_div(p->seqlen_q, fm::kBwdBlockQ);
   const int32_t tk = (int32_t)ceil_div(p->seqlen_k, fm::kBwdBlockK);
-  if (tk > 65535) return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_k too large");
+  const int32_t tq_q = (int32_t)ceil_div(p->seqlen_q, fm::kDqBlockQ);
+  const int32_t tk_q = (int32_t)ceil_div(p->seqlen_k, fm::kDqBlockK);
+  if (tk > 65535 || tq_q > 65535) return fail(FM_ERR_INVALID_ARGUMENT, "sequence too long");
   char* w = static_cast<char*>(ws);
-  int32_t* summary = reinterpret_cast<int32_t*>(w + L.summary);
   uint8_t* classes_t = reinterpret_cast<uint8_t*>(w + L.map);
-  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kBwdBlockQ, fm::kBwdBlockK, 1, summary, classes_t, stream);
+  uint8_t* classes_q = reinterpret_cast<uint8_t*>(w + L.map_q);
+  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kBwdBlockQ, fm::kBwdBlockK, 1,
+                     reinterpret_cast<int32_t*>(w + L.summary), classes_t, stream);
+  if (st != FM_OK) return st;
+  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kDqBlockQ, fm::kDqBlockK, 0,
+                     reinterpret_cast<int32_t*>(w + L.summary_q), classes_q, stream);
   if (st != FM_OK) return st;
 
   fm::BwdArgs a{};
@@ -302,7 +314,6 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   a.dk = dk;
   a.dv = dv;
   a.drow = reinterpret_cast<float*>(w + L.drow);
-  a.dq_acc = reinterpret_cast<float*>(w + L.dqacc);
   a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
   a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
   a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
@@ -317,13 +328,16 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   a.classes_t = classes_t;
   a.tq = tq;
   a.tk = tk;
+  a.classes_q = classes_q;
+  a.tq_q = tq_q;
+  a.tk_q = tk_q;
   const bool f32 = p->dtype == FM_FP32;
   hipError_t e = run_stage(FM_STAGE_BWD_PRE, stream, [&] { return fm::launch_bwd_pre(a, p->head_dim, f32, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward pre-pass launch");
-  e = run_stage(FM_STAGE_BWD, stream, [&] { return fm::launch_bwd(a, p->head_dim, f32, stream); });
-  if (e != hipSuccess) return hip_fail(e, "backward launch");
-  e = run_stage(FM_STAGE_DQ_FINALIZE, stream, [&] { return fm::launch_dq_finalize(a, p->head_dim, f32, stream); });
-  if (e != hipSuccess) return hip_fail(e, "dQ finalize launch");
+  e = run_stage(FM_STAGE_BWD, stream, [&] { return fm::launch_bwd_dkdv(a, p->head_dim, f32, stream); });
+  if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+  e = run_stage(FM_STAGE_BWD_DQ, stream, [&] { return fm::launch_bwd_dq(a, p->head_dim, f32, stream); });
+  if (e != hipSuccess) return hip_fail(e, "dQ launch");
   return FM_OK;
 }
 

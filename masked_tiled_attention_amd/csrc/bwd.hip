@@ -8,13 +8,20 @@
 //   P  = exp(scale * Q K^T - LSE)  (0 on masked pairs)
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),  D = rowsum(dO * O)
 //   dK = scale * dS^T Q,   dQ = scale * dS K.
+// Section "Three ways to raise GPU utilization": work is split over batch,
+// heads and sequence tiles, and each wavefront owns its own output rows.
+//
 // Kernels:
-//   bwd_pre     D per query row and zeroing of the float32 dQ accumulator;
-//   bwd         one workgroup per (batch, head, 128-key tile); K and V rows
-//               stay in registers, dK and dV accumulate in registers across
-//               all non-SKIP 64-row query tiles; dQ partial sums are added to
-//               the float32 accumulator with global atomics;
-//   dq_finalize dQ = scale * accumulator, cast to the output dtype.
+//   bwd_pre   D per query row;
+//   bwd_dkdv  one workgroup per (batch, head, 128-key tile); each wavefront
+//             owns 32 keys whose K and V rows stay in registers and whose dK,
+//             dV accumulate in registers over all non-SKIP 64-row query tiles;
+//   bwd_dq    one workgroup per (batch, head, 128-row query tile); each
+//             wavefront owns 32 query rows whose Q, dO, LSE, D stay in
+//             registers and whose dQ accumulates over all non-SKIP 64-key
+//             tiles. It recomputes S and dP (two extra matrix products) so
+//             that no workgroup ever adds into another one's output: no
+//             atomics, deterministic results.
 #include <climits>
 #include <cmath>
 
@@ -24,11 +31,9 @@
 namespace fm {
 namespace {
 
-constexpr int BQ = kBwdBlockQ;   // 64 query rows per inner tile
-constexpr int BK = kBwdBlockK;   // 128 keys per workgroup
-constexpr int NW = BK / 32;      // 4 wavefronts, 32 keys each
-constexpr int NT = NW * 64;
-constexpr int LIST_CAP = 1024;
+constexpr int NW = 4;            // wavefronts per workgroup
+constexpr int NT = NW * 64;      // threads per workgroup
+constexpr int LIST_CAP = 1024;   // class bytes compacted per pass (4 per thread)
 constexpr uint32_t kPartialBit = 0x80000000u;
 
 // ------------------------------------------------------------------ pre-pass
@@ -68,98 +73,112 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) part = fmaf(x[i], y[i], part);
-    float* acc = a.dq_acc + row * D + 8 * sub;
-    *reinterpret_cast<f32x4*>(acc) = f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(acc + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int o = TPR / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
   if (row < nrows && sub == 0) a.drow[((int64_t)b * a.heads + h) * a.seq_q + m] = part;
 }
 
-// ------------------------------------------------------------------ finalize
-template <int D, bool F32>
-__global__ __launch_bounds__(256) void dq_finalize_kernel(BwdArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 8-element chunk
-  const int64_t nchunk = (int64_t)a.batch * a.seq_q * a.heads * (D / 8);
-  if (idx >= nchunk) return;
-  const int64_t row = idx / (D / 8);
-  const int c8 = (int)(idx % (D / 8));
-  const int h = (int)(row % a.heads);
-  const int m = (int)((row / a.heads) % a.seq_q);
-  const int b = (int)(row / ((int64_t)a.heads * a.seq_q));
-  const float* src = a.dq_acc + row * D + 8 * c8;
-  const f32x4 u = *reinterpret_cast<const f32x4*>(src);
-  const f32x4 v = *reinterpret_cast<const f32x4*>(src + 4);
-  const int64_t off = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh + 8 * c8;
-  const float s = a.scale;
-  if constexpr (F32) {
-    float* d = reinterpret_cast<float*>(a.dq) + off;
-    *reinterpret_cast<f32x4*>(d) = f32x4{u[0] * s, u[1] * s, u[2] * s, u[3] * s};
-    *reinterpret_cast<f32x4*>(d + 4) = f32x4{v[0] * s, v[1] * s, v[2] * s, v[3] * s};
-  } else {
-    st16(reinterpret_cast<uint16_t*>(a.dq) + off,
-         u32x4{pack_bf16(u[0] * s, u[1] * s), pack_bf16(u[2] * s, u[3] * s), pack_bf16(v[0] * s, v[1] * s),
-               pack_bf16(v[2] * s, v[3] * s)});
-  }
+// ------------------------------------------------------------------ LDS helpers
+//
+// Row-major tiles (rows of D bf16) store 16-byte chunk ch of row r at chunk
+// ch ^ rsw(r). With it, 16-byte operand reads of 8 consecutive rows, the
+// 16-byte staging writes of one row, and 4-row x 16-column transposing reads
+// (ds_read_b64_tr_b16) each touch distinct bank slots.
+__device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+__device__ __forceinline__ int rm_byte(int row, int col) {   // col: element index, multiple of 4
+  return row * (2 * D) + (((col >> 3) ^ rsw(row)) << 4) + ((col & 7) << 1);
 }
 
-// ------------------------------------------------------------------ main
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane
+// group, lane j receives element (j % 4) of the 4-value row addressed by lane
+// 4k + j / 4, for k = 0..3. When the 16 lanes address rows r..r+3 x columns
+// c..c+15 of a row-major bf16 tile (lane i -> row r + i/4, columns
+// c + 4(i%4) .. +3), lane j receives column c + j of rows r..r+3.
+__device__ __forceinline__ u32x2 tr16(const char* lds_base, int byte) {
+  lds_s16x4* p = (lds_s16x4*)((__attribute__((address_space(3))) char*)lds_base + byte);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
+
+// MFMA operand (32 output indices x 16 contraction values) read transposed from
+// a row-major tile whose rows are the contraction index: lane l gets output
+// index obase + (l & 31) and contraction rows r0 + 0..3 (elements 0..3) and
+// r1 + 0..3 (elements 4..7), r0 / r1 chosen per lane half by the caller.
 template <int D>
-struct alignas(16) BwdSmem {
-  static constexpr int RP = D + 8;     // padded row-major row (elements)
-  static constexpr int QTP = BQ + 4;   // padded transposed row over query rows
-  static constexpr int KTP = BK + 8;   // padded transposed row over keys
-  uint16_t q[BQ][RP];
-  uint16_t qt[D][QTP];
-  uint16_t dout[BQ][RP];
-  uint16_t doutt[D][QTP];
-  uint16_t ds[BQ][BK + 8];
-  uint16_t kt[D][KTP];
-  float lse2[BQ];
-  float dd[BQ];
+__device__ __forceinline__ u32x4 tr_operand(const char* base, int lane, int obase, int r0, int r1) {
+  const int i = lane & 15;
+  const int col = obase + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+  const u32x2 x = tr16(base, rm_byte<D>(r0 + (i >> 2), col));
+  const u32x2 y = tr16(base, rm_byte<D>(r1 + (i >> 2), col));
+  return u32x4{x[0], x[1], y[0], y[1]};
+}
+
+// Compact the non-SKIP entries of one class-map row into sm_list (ascending),
+// flagging PARTIAL ones; returns the count. Ends with a barrier.
+__device__ __forceinline__ int compact_classes(const uint8_t* row, int first, int count, uint32_t* sm_list,
+                                               int32_t* sm_scan, int tid, int lane, int wave) {
+  uint8_t cls[LIST_CAP / NT];
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < LIST_CAP / NT; ++e) {
+    const int idx = tid * (LIST_CAP / NT) + e;
+    cls[e] = idx < count ? row[first + idx] : (uint8_t)FM_TILE_SKIP;
+    cnt += cls[e] != FM_TILE_SKIP;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();   // every wave is done with the previous list and all tile buffers
+  if (lane == 63) sm_scan[wave] = incl;
+  __syncthreads();
+  int pos = incl - cnt, n_list = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    if (ww < wave) pos += sm_scan[ww];
+    n_list += sm_scan[ww];
+  }
+#pragma unroll
+  for (int e = 0; e < LIST_CAP / NT; ++e) {
+    if (cls[e] != FM_TILE_SKIP) {
+      const uint32_t id = (uint32_t)(first + tid * (LIST_CAP / NT) + e);
+      sm_list[pos++] = id | (cls[e] == FM_TILE_PARTIAL ? kPartialBit : 0u);
+    }
+  }
+  __syncthreads();
+  return n_list;
+}
+
+// ------------------------------------------------------------------ dK / dV
+namespace kv {
+constexpr int BQ = kBwdBlockQ;   // 64 query rows per inner tile
+constexpr int BK = kBwdBlockK;   // 128 keys per workgroup (32 per wavefront)
+
+template <int D>
+struct alignas(16) Smem {
+  uint16_t q[2][BQ * D];      // double-buffered query tile
+  uint16_t dout[2][BQ * D];   // double-buffered dO tile
+  float lse2[2][BQ];          // LSE * log2(e); +inf for rows that see nothing / past the end
+  float dd[2][BQ];            // D = rowsum(dO * O)
   uint32_t list[LIST_CAP];
   int32_t scan[NW];
 };
-
-// Write 4 rows x 8 channels (packed bf16, one u32x4 per row) into a
-// row-major tile and its transpose.
-template <int ROWP, int TP>
-__device__ __forceinline__ void store_rows_and_transpose(uint16_t (*rm)[ROWP], uint16_t (*tr)[TP], int r0, int c0,
-                                                         const u32x4 (&rv)[4]) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4*>(&rm[r0 + r][c0]) = rv[r];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    u32x2 ev, od;
-    ev[0] = (rv[0][p] & 0xffffu) | (rv[1][p] << 16);
-    ev[1] = (rv[2][p] & 0xffffu) | (rv[3][p] << 16);
-    od[0] = (rv[0][p] >> 16) | (rv[1][p] & 0xffff0000u);
-    od[1] = (rv[2][p] >> 16) | (rv[3][p] & 0xffff0000u);
-    *reinterpret_cast<u32x2*>(&tr[c0 + 2 * p][r0]) = ev;
-    *reinterpret_cast<u32x2*>(&tr[c0 + 2 * p + 1][r0]) = od;
-  }
-}
-
-template <int TP>
-__device__ __forceinline__ void store_transpose(uint16_t (*tr)[TP], int r0, int c0, const u32x4 (&rv)[4]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    u32x2 ev, od;
-    ev[0] = (rv[0][p] & 0xffffu) | (rv[1][p] << 16);
-    ev[1] = (rv[2][p] & 0xffffu) | (rv[3][p] << 16);
-    od[0] = (rv[0][p] >> 16) | (rv[1][p] & 0xffff0000u);
-    od[1] = (rv[2][p] >> 16) | (rv[3][p] & 0xffff0000u);
-    *reinterpret_cast<u32x2*>(&tr[c0 + 2 * p][r0]) = ev;
-    *reinterpret_cast<u32x2*>(&tr[c0 + 2 * p + 1][r0]) = od;
-  }
-}
+}  // namespace kv
 
 template <int D, bool F32>
-__global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
+  using namespace kv;
   constexpr int KSTEPS = D / 16;
   constexpr int CB = D / 32;
-  __shared__ BwdSmem<D> sm;
+  constexpr int QR = (BQ * D / 8) / NT;   // 16-byte chunks per thread of a Q (or dO) tile
+  __shared__ Smem<D> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -179,8 +198,7 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
   const int64_t mbase = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
   const uint8_t* ccol = a.classes_t + ((int64_t)(bm * a.mask.hm + hm) * a.tk + kt) * a.tq;
 
-  const int n0 = kt * BK;
-  const int n = n0 + 32 * w + lr;   // this lane's key
+  const int n = kt * BK + 32 * w + lr;   // this lane's key
   const bool key_ok = n < a.seq_k;
 
   // K and V rows of this lane's key as MFMA B operands (channels 16s + 8g ..).
@@ -204,21 +222,6 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
   }
   const bool ragged_k = (a.seq_k % BK) != 0 && kt == a.tk - 1;
 
-  // K^T of the whole 128-key tile in LDS (B operand of dQ = dS K).
-  for (int gi = tid; gi < (BK / 4) * (D / 8); gi += NT) {
-    const int kq = gi / (D / 8);
-    const int c8 = gi % (D / 8);
-    u32x4 rv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int nn = n0 + 4 * kq + r;
-      rv[r] = nn < a.seq_k ? load8_as_bf16<F32>(a.k, (int64_t)b * a.k_sb + (int64_t)nn * a.k_ss +
-                                                         (int64_t)h * a.k_sh + 8 * c8)
-                           : u32x4{0u, 0u, 0u, 0u};
-    }
-    store_transpose<BwdSmem<D>::KTP>(sm.kt, 4 * kq, 8 * c8, rv);
-  }
-
   f32x16 dvacc[CB], dkacc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
@@ -228,77 +231,72 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
   const float C = a.scale_log2;
   const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_q;
 
-  for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
-    const int n_in = min(LIST_CAP, a.tq - qt0);
-    uint8_t cls[LIST_CAP / NT];
-    int cnt = 0;
+  // ---- registers carrying one query tile (Q, dO, LSE, D) to LDS ----
+  u32x4 rq[QR], rd[QR];
+  float rl2 = INFINITY, rdd = 0.f;
+  auto load_q = [&](int qt) {
+    const int m0 = qt * BQ;
 #pragma unroll
-    for (int e = 0; e < LIST_CAP / NT; ++e) {
-      const int idx = tid * (LIST_CAP / NT) + e;
-      cls[e] = idx < n_in ? ccol[qt0 + idx] : (uint8_t)FM_TILE_SKIP;
-      cnt += cls[e] != FM_TILE_SKIP;
-    }
-    int incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (l >= o) incl += y;
-    }
-    __syncthreads();
-    if (l == 63) sm.scan[w] = incl;
-    __syncthreads();
-    int pos = incl - cnt, n_list = 0;
-#pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      if (ww < w) pos += sm.scan[ww];
-      n_list += sm.scan[ww];
-    }
-#pragma unroll
-    for (int e = 0; e < LIST_CAP / NT; ++e) {
-      if (cls[e] != FM_TILE_SKIP) {
-        const uint32_t qt = (uint32_t)(qt0 + tid * (LIST_CAP / NT) + e);
-        sm.list[pos++] = qt | (cls[e] == FM_TILE_PARTIAL ? kPartialBit : 0u);
+    for (int i = 0; i < QR; ++i) {
+      const int ci = tid + i * NT;
+      const int mm = m0 + ci / (D / 8);
+      const int ch = ci % (D / 8);
+      if (mm < a.seq_q) {
+        rq[i] = load8_as_bf16<F32>(a.q, (int64_t)b * a.q_sb + (int64_t)mm * a.q_ss + (int64_t)h * a.q_sh + 8 * ch);
+        rd[i] = load8_as_bf16<F32>(a.dout, (int64_t)b * a.o_sb + (int64_t)mm * a.o_ss + (int64_t)h * a.o_sh + 8 * ch);
+      } else {
+        rq[i] = u32x4{0u, 0u, 0u, 0u};
+        rd[i] = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    __syncthreads();
+    if (tid < BQ) {
+      const int mm = m0 + tid;
+      rl2 = INFINITY;
+      rdd = 0.f;
+      if (mm < a.seq_q) {
+        const float lse = a.lse[lrow + mm];
+        rl2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+        rdd = a.drow[lrow + mm];
+      }
+    }
+  };
+  auto store_q = [&](int buf) {
+    char* qb = reinterpret_cast<char*>(sm.q[buf]);
+    char* db = reinterpret_cast<char*>(sm.dout[buf]);
+#pragma unroll
+    for (int i = 0; i < QR; ++i) {
+      const int ci = tid + i * NT;
+      const int off = rm_byte<D>(ci / (D / 8), 8 * (ci % (D / 8)));
+      *reinterpret_cast<u32x4*>(qb + off) = rq[i];
+      *reinterpret_cast<u32x4*>(db + off) = rd[i];
+    }
+    if (tid < BQ) {
+      sm.lse2[buf][tid] = rl2;
+      sm.dd[buf][tid] = rdd;
+    }
+  };
 
-    for (int it = 0; it < n_list; ++it) {
-      const uint32_t ent = sm.list[it];
+  int it_global = 0;
+  for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
+    const int n_list = compact_classes(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.scan, tid, l, w);
+    if (n_list == 0) continue;
+
+    uint32_t ent = sm.list[0];
+    load_q((int)(ent & ~kPartialBit));
+
+    for (int it = 0; it < n_list; ++it, ++it_global) {
+      const int buf = it_global & 1;
       const int qt = (int)(ent & ~kPartialBit);
       const bool masked_tile = (ent & kPartialBit) || ragged_k;
       const int m0 = qt * BQ;
-
-      // ---- stage Q, dO (row-major and transposed), LSE*log2e and D ----
-      for (int gi = tid; gi < (BQ / 4) * (D / 8); gi += NT) {
-        const int rq = gi / (D / 8);
-        const int c8 = gi % (D / 8);
-        u32x4 rq_[4], rd_[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int mm = m0 + 4 * rq + r;
-          if (mm < a.seq_q) {
-            rq_[r] = load8_as_bf16<F32>(a.q, (int64_t)b * a.q_sb + (int64_t)mm * a.q_ss + (int64_t)h * a.q_sh + 8 * c8);
-            rd_[r] = load8_as_bf16<F32>(a.dout, (int64_t)b * a.o_sb + (int64_t)mm * a.o_ss + (int64_t)h * a.o_sh + 8 * c8);
-          } else {
-            rq_[r] = u32x4{0u, 0u, 0u, 0u};
-            rd_[r] = u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-        store_rows_and_transpose<BwdSmem<D>::RP, BwdSmem<D>::QTP>(sm.q, sm.qt, 4 * rq, 8 * c8, rq_);
-        store_rows_and_transpose<BwdSmem<D>::RP, BwdSmem<D>::QTP>(sm.dout, sm.doutt, 4 * rq, 8 * c8, rd_);
+      store_q(buf);
+      __syncthreads();   // tile `buf` visible; the other buffer is free
+      if (it + 1 < n_list) {   // the next query tile's loads overlap this tile's math
+        ent = sm.list[it + 1];
+        load_q((int)(ent & ~kPartialBit));
       }
-      if (tid < BQ) {
-        const int mm = m0 + tid;
-        float l2 = INFINITY, dv = 0.f;
-        if (mm < a.seq_q) {
-          const float lse = a.lse[lrow + mm];
-          l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-          dv = a.drow[lrow + mm];
-        }
-        sm.lse2[tid] = l2;
-        sm.dd[tid] = dv;
-      }
-      __syncthreads();
+      const char* qb = reinterpret_cast<const char*>(sm.q[buf]);
+      const char* db = reinterpret_cast<const char*>(sm.dout[buf]);
 
       // ---- S = Q K^T and dP = dO V^T (lane = key, registers = query rows) ----
       f32x16 sacc[2], dpacc[2];
@@ -308,10 +306,9 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
         dpacc[mb] = f32x16{};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const u32x4 qa = *reinterpret_cast<const u32x4*>(&sm.q[32 * mb + lr][16 * s + 8 * g]);
-          sacc[mb] = mfma32(qa, kf[s], sacc[mb]);
-          const u32x4 da = *reinterpret_cast<const u32x4*>(&sm.dout[32 * mb + lr][16 * s + 8 * g]);
-          dpacc[mb] = mfma32(da, vf[s], dpacc[mb]);
+          const int off = rm_byte<D>(32 * mb + lr, 16 * s + 8 * g);
+          sacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(qb + off), kf[s], sacc[mb]);
+          dpacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(db + off), vf[s], dpacc[mb]);
         }
       }
 
@@ -321,8 +318,8 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int ml = 32 * mb + 8 * q4 + 4 * g;
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[ml]);
-          const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[ml]);
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
+          const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 4 * q4 + r;
@@ -337,15 +334,6 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
           }
         }
       }
-      // dS (bf16) to LDS, row-major [query][key], for the dQ product
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ml = 32 * mb + 8 * (i >> 2) + 4 * g + (i & 3);
-          const __bf16 x = (__bf16)dpacc[mb][i];
-          sm.ds[ml][32 * w + lr] = __builtin_bit_cast(uint16_t, x);
-        }
 
       // ---- dV^T += dO^T P,  dK^T += Q^T dS (contraction over query rows) ----
 #pragma unroll
@@ -358,45 +346,14 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
             pp[j] = pack_bf16(sacc[mb][8 * t + 2 * j], sacc[mb][8 * t + 2 * j + 1]);
             dsp[j] = pack_bf16(dpacc[mb][8 * t + 2 * j], dpacc[mb][8 * t + 2 * j + 1]);
           }
-          const int kb = 32 * mb + 16 * t + 4 * g;
+          const int r0 = 32 * mb + 16 * t + 4 * g;
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
-            const u32x2 d0 = *reinterpret_cast<const u32x2*>(&sm.doutt[32 * cb + lr][kb]);
-            const u32x2 d1 = *reinterpret_cast<const u32x2*>(&sm.doutt[32 * cb + lr][kb + 8]);
-            dvacc[cb] = mfma32(u32x4{d0[0], d0[1], d1[0], d1[1]}, pp, dvacc[cb]);
-            const u32x2 q0 = *reinterpret_cast<const u32x2*>(&sm.qt[32 * cb + lr][kb]);
-            const u32x2 q1 = *reinterpret_cast<const u32x2*>(&sm.qt[32 * cb + lr][kb + 8]);
-            dkacc[cb] = mfma32(u32x4{q0[0], q0[1], q1[0], q1[1]}, dsp, dkacc[cb]);
+            dvacc[cb] = mfma32(tr_operand<D>(db, l, 32 * cb, r0, r0 + 8), pp, dvacc[cb]);
+            dkacc[cb] = mfma32(tr_operand<D>(qb, l, 32 * cb, r0, r0 + 8), dsp, dkacc[cb]);
           }
         }
       }
-      __syncthreads();   // dS tile complete
-
-      // ---- dQ += dS K over the workgroup's 128 keys; float32 atomics ----
-      constexpr int NBLK = 2 * CB;            // (query block, channel block) pairs
-      constexpr int PER_W = NBLK / NW;        // 2 for D = 128, 1 for D = 64
-#pragma unroll
-      for (int u = 0; u < PER_W; ++u) {
-        const int blk = w * PER_W + u;
-        const int mb = blk % 2;
-        const int cb = blk / 2;
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-          const u32x4 da = *reinterpret_cast<const u32x4*>(&sm.ds[32 * mb + lr][16 * s + 8 * g]);
-          const u32x4 kb2 = *reinterpret_cast<const u32x4*>(&sm.kt[32 * cb + lr][16 * s + 8 * g]);
-          acc = mfma32(da, kb2, acc);
-        }
-        // acc holds dQ[m][c]: column c = 32cb + lr, rows m = 32mb + 8(i/4) + 4g + (i&3)
-        const int c = 32 * cb + lr;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int mm = m0 + 32 * mb + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (mm < a.seq_q)
-            unsafeAtomicAdd(a.dq_acc + (((int64_t)b * a.seq_q + mm) * a.heads + h) * D + c, acc[i]);
-        }
-      }
-      __syncthreads();   // LDS tiles are overwritten by the next query tile
     }
   }
 
@@ -427,6 +384,215 @@ __global__ __launch_bounds__(NT) void bwd_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ dQ
+namespace dqk {
+constexpr int BQ = kDqBlockQ;   // 128 query rows per workgroup (32 per wavefront)
+constexpr int BK = kDqBlockK;   // 64 keys per inner tile
+
+template <int D>
+struct alignas(16) Smem {
+  uint16_t k[2][BK * D];      // double-buffered key tile, row-major
+  uint16_t v[2][BK * D];      // double-buffered value tile, row-major
+  int32_t bnd[2][4][BK];      // lts, lte, uts, ute of the tile's keys
+  uint32_t list[LIST_CAP];
+  int32_t scan[NW];
+};
+}  // namespace dqk
+
+template <int D, bool F32>
+__global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
+  using namespace dqk;
+  constexpr int KSTEPS = D / 16;
+  constexpr int CB = D / 32;
+  constexpr int NB = BK / 32;
+  constexpr int KR = (BK * D / 8) / NT;   // 16-byte chunks per thread of a K (or V) tile
+  __shared__ Smem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int lr = l & 31;
+  const int g = l >> 5;
+
+  // Heaviest query tiles first (under causal-like masks later rows see more keys).
+  const int nbh = a.batch * a.heads;
+  const int qt = a.tq_q - 1 - (int)(blockIdx.x / nbh);
+  const int bh = blockIdx.x % nbh;
+  const int b = bh / a.heads;
+  const int h = bh % a.heads;
+  const int bm = a.mask.bm > 1 ? b : 0;
+  const int hm = a.mask.hm > 1 ? h : 0;
+  const int64_t mbase = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
+  const uint8_t* crow = a.classes_q + ((int64_t)(bm * a.mask.hm + hm) * a.tq_q + qt) * a.tk_q;
+
+  const int m = qt * BQ + 32 * w + lr;   // this lane's query row
+  const bool row_ok = m < a.seq_q;
+
+  // Q and dO rows of this lane's query as MFMA B operands; its LSE and D.
+  u32x4 qf[KSTEPS], df[KSTEPS];
+  float l2 = INFINITY, dd = 0.f;
+  {
+    const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
+    const int64_t doff = (int64_t)b * a.o_sb + (int64_t)m * a.o_ss + (int64_t)h * a.o_sh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      qf[s] = row_ok ? load8_as_bf16<F32>(a.q, qoff + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      df[s] = row_ok ? load8_as_bf16<F32>(a.dout, doff + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (row_ok) {
+      const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_q + m;
+      const float lse = a.lse[lrow];
+      l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+      dd = a.drow[lrow];
+    }
+  }
+
+  f32x16 dqacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) dqacc[cb] = f32x16{};
+  const float C = a.scale_log2;
+  const bool ragged_k = (a.seq_k % BK) != 0;
+
+  // ---- registers carrying one key tile (K, V, bounds) to LDS ----
+  u32x4 rk[KR], rv[KR];
+  int32_t rb[4] = {INT_MIN, INT_MAX, 0, 0};
+  auto load_k = [&](int kt, bool masked) {
+    const int n0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      const int ci = tid + i * NT;
+      const int nn = n0 + ci / (D / 8);
+      const int ch = ci % (D / 8);
+      if (nn < a.seq_k) {
+        rk[i] = load8_as_bf16<F32>(a.k, (int64_t)b * a.k_sb + (int64_t)nn * a.k_ss + (int64_t)h * a.k_sh + 8 * ch);
+        rv[i] = load8_as_bf16<F32>(a.v, (int64_t)b * a.v_sb + (int64_t)nn * a.v_ss + (int64_t)h * a.v_sh + 8 * ch);
+      } else {
+        rk[i] = u32x4{0u, 0u, 0u, 0u};
+        rv[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (masked && tid < BK) {
+      const int nn = n0 + tid;
+      if (nn < a.seq_k) {
+        rb[0] = a.mask.has_lower ? a.mask.lts[mbase + nn] : a.seq_q;
+        rb[1] = a.mask.has_lower ? a.mask.lte[mbase + nn] : a.seq_q;
+        rb[2] = a.mask.has_upper ? a.mask.uts[mbase + nn] : 0;
+        rb[3] = a.mask.has_upper ? a.mask.ute[mbase + nn] : 0;
+      } else {   // keys past the end: masked for every row
+        rb[0] = INT_MIN;
+        rb[1] = INT_MAX;
+        rb[2] = 0;
+        rb[3] = 0;
+      }
+    }
+  };
+  auto store_k = [&](int buf, bool masked) {
+    char* kb = reinterpret_cast<char*>(sm.k[buf]);
+    char* vb = reinterpret_cast<char*>(sm.v[buf]);
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+      const int ci = tid + i * NT;
+      const int off = rm_byte<D>(ci / (D / 8), 8 * (ci % (D / 8)));
+      *reinterpret_cast<u32x4*>(kb + off) = rk[i];
+      *reinterpret_cast<u32x4*>(vb + off) = rv[i];
+    }
+    if (masked && tid < BK) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.bnd[buf][j][tid] = rb[j];
+    }
+  };
+  auto masked_of = [&](uint32_t ent) {
+    return (ent & kPartialBit) || (ragged_k && (int)(ent & ~kPartialBit) == a.tk_q - 1);
+  };
+
+  int it_global = 0;
+  for (int kt0 = 0; kt0 < a.tk_q; kt0 += LIST_CAP) {
+    const int n_list = compact_classes(crow, kt0, min(LIST_CAP, a.tk_q - kt0), sm.list, sm.scan, tid, l, w);
+    if (n_list == 0) continue;
+
+    uint32_t ent = sm.list[0];
+    load_k((int)(ent & ~kPartialBit), masked_of(ent));
+
+    for (int it = 0; it < n_list; ++it, ++it_global) {
+      const int buf = it_global & 1;
+      const bool masked_tile = masked_of(ent);
+      store_k(buf, masked_tile);
+      __syncthreads();   // tile `buf` visible; the other buffer is free
+      if (it + 1 < n_list) {   // the next key tile's loads overlap this tile's math
+        ent = sm.list[it + 1];
+        load_k((int)(ent & ~kPartialBit), masked_of(ent));
+      }
+      const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
+      const char* vb = reinterpret_cast<const char*>(sm.v[buf]);
+
+      // ---- S^T = K Q^T and dP^T = V dO^T (lane = query row, registers = keys) ----
+      f32x16 sacc[NB], dpacc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        sacc[nb] = f32x16{};
+        dpacc[nb] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const int off = rm_byte<D>(32 * nb + lr, 16 * s + 8 * g);
+          sacc[nb] = mfma32(*reinterpret_cast<const u32x4*>(kb + off), qf[s], sacc[nb]);
+          dpacc[nb] = mfma32(*reinterpret_cast<const u32x4*>(vb + off), df[s], dpacc[nb]);
+        }
+      }
+
+      // ---- P and dS for this lane's row ----
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(fmaf(sacc[nb][i], C, -l2));
+          if (masked_tile) {
+            const int nl = 32 * nb + 8 * (i >> 2) + 4 * g + (i & 3);
+            const bool mk = (sm.bnd[buf][0][nl] <= m && m < sm.bnd[buf][1][nl]) ||
+                            (sm.bnd[buf][2][nl] <= m && m < sm.bnd[buf][3][nl]);
+            p = mk ? 0.f : p;
+          }
+          dpacc[nb][i] = p * (dpacc[nb][i] - dd);
+        }
+      }
+
+      // ---- dQ^T += K^T dS^T (contraction over the tile's keys) ----
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          u32x4 dsp;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dsp[j] = pack_bf16(dpacc[nb][8 * t + 2 * j], dpacc[nb][8 * t + 2 * j + 1]);
+          const int r0 = 32 * nb + 16 * t + 4 * g;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            dqacc[cb] = mfma32(tr_operand<D>(kb, l, 32 * cb, r0, r0 + 8), dsp, dqacc[cb]);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: dQ = scale * dQ^T, transposed back on store ----
+  if (row_ok) {
+    const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c0 = 32 * cb + 8 * q4 + 4 * g;
+        const float x0 = dqacc[cb][4 * q4] * a.scale, x1 = dqacc[cb][4 * q4 + 1] * a.scale;
+        const float x2 = dqacc[cb][4 * q4 + 2] * a.scale, x3 = dqacc[cb][4 * q4 + 3] * a.scale;
+        if constexpr (F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dq) + qoff + c0) = f32x4{x0, x1, x2, x3};
+        } else {
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.dq) + qoff + c0) =
+              u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+        }
+      }
+    }
+  }
+}
+
 template <int D, bool F32>
 hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
   const int64_t nrows = (int64_t)a.batch * a.seq_q * a.heads;
@@ -436,15 +602,14 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
 }
 
 template <int D, bool F32>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_kernel<D, F32>), dim3(a.tk * a.batch * a.heads), dim3(NT), 0, s, a);
+hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32>), dim3(a.tk * a.batch * a.heads), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D, bool F32>
-hipError_t launch_fin_t(const BwdArgs& a, hipStream_t s) {
-  const int64_t nchunk = (int64_t)a.batch * a.seq_q * a.heads * (D / 8);
-  hipLaunchKernelGGL((dq_finalize_kernel<D, F32>), dim3((unsigned)((nchunk + 255) / 256)), dim3(256), 0, s, a);
+hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_kernel<D, F32>), dim3(a.tq_q * a.batch * a.heads), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -455,14 +620,14 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool f32, hipStream_t 
   return f32 ? launch_pre_t<64, true>(a, s) : launch_pre_t<64, false>(a, s);
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool f32, hipStream_t s) {
-  if (head_dim == 128) return f32 ? launch_bwd_t<128, true>(a, s) : launch_bwd_t<128, false>(a, s);
-  return f32 ? launch_bwd_t<64, true>(a, s) : launch_bwd_t<64, false>(a, s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, bool f32, hipStream_t s) {
+  if (head_dim == 128) return f32 ? launch_dkdv_t<128, true>(a, s) : launch_dkdv_t<128, false>(a, s);
+  return f32 ? launch_dkdv_t<64, true>(a, s) : launch_dkdv_t<64, false>(a, s);
 }
 
-hipError_t launch_dq_finalize(const BwdArgs& a, int head_dim, bool f32, hipStream_t s) {
-  if (head_dim == 128) return f32 ? launch_fin_t<128, true>(a, s) : launch_fin_t<128, false>(a, s);
-  return f32 ? launch_fin_t<64, true>(a, s) : launch_fin_t<64, false>(a, s);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool f32, hipStream_t s) {
+  if (head_dim == 128) return f32 ? launch_dq_t<128, true>(a, s) : launch_dq_t<128, false>(a, s);
+  return f32 ? launch_dq_t<64, true>(a, s) : launch_dq_t<64, false>(a, s);
 }
 
 }  // namespace fm

@@ -12,8 +12,10 @@ namespace fm {
 // Tile shapes of the attention kernels (rows of Q x columns of K).
 constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
-constexpr int kBwdBlockQ = 64;
-constexpr int kBwdBlockK = 128;
+constexpr int kBwdBlockQ = 64;    // dK/dV kernel: query rows per inner tile
+constexpr int kBwdBlockK = 128;   // dK/dV kernel: keys per workgroup
+constexpr int kDqBlockQ = 128;    // dQ kernel: query rows per workgroup
+constexpr int kDqBlockK = 64;     // dQ kernel: keys per inner tile
 
 // Mask vectors as seen by the kernels. A missing pair is flagged and its
 // pointers are not dereferenced.
@@ -63,7 +65,6 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;           // [B][Sq][H][D] float32, contiguous
   float* drow;             // [B][H][Sq] float32: rowsum(dO * O)
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
@@ -73,8 +74,10 @@ struct BwdArgs {
   float scale;
   float scale_log2;
   MaskArgs mask;
-  const uint8_t* classes_t;  // [bm][hm][tk][tq]
+  const uint8_t* classes_t;  // [bm][hm][tk][tq] with the dK/dV kernel's tiles
   int32_t tq, tk;
+  const uint8_t* classes_q;  // [bm][hm][tq_q][tk_q] with the dQ kernel's tiles
+  int32_t tq_q, tk_q;
 };
 
 constexpr int kMaxChunks = 64;
@@ -93,8 +96,8 @@ hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream);
 hipError_t launch_classify_map(const ClassifyArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
-hipError_t launch_dq_finalize(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_localize(const LocalizeArgs& a, hipStream_t stream);
 
 }  // namespace fm
