@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -166,6 +168,16 @@ def main():
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] reference copy: {nbytes} bytes read, {nbytes} bytes written")
+        del src, dst
 
     log(f"[bench] building {args.workload} seed {args.seed}")
     w = SC.build(args.workload, args.seed)

@@ -110,6 +110,10 @@ fm_status check_problem(const fm_problem* p) {
         return fail(FM_ERR_INVALID_ARGUMENT, "%s stride %d (%lld elements) breaks 16-byte row alignment",
                     nm[t], i, (long long)st[t][i]);
     }
+  // kernels address one tile (at most 256 rows) with 32-bit byte offsets
+  for (int t = 0; t < 4; ++t)
+    if (st[t][1] * es * 256 > INT32_MAX)
+      return fail(FM_ERR_UNSUPPORTED, "%s sequence stride %lld elements is too large", nm[t], (long long)st[t][1]);
   const int64_t tq = ceil_div(p->seqlen_q, fm::kFwdBlockQ);
   if (tq * p->batch * p->heads > INT32_MAX)
     return fail(FM_ERR_INVALID_ARGUMENT, "problem too large for one launch");

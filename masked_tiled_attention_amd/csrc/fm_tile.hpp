@@ -1,0 +1,137 @@
+// LDS tile layout, transposing operand reads and class-list compaction shared
+// by the attention kernels (gfx950).
+#pragma once
+
+#include "fm_attn.h"
+#include "fm_device.hpp"
+
+namespace fm {
+
+constexpr uint32_t kPartialBit = 0x80000000u;   // list entry flag: tile needs the mask
+
+// Row-major bf16 tiles (rows of D elements) store 16-byte chunk ch of row r at
+// chunk ch ^ rsw(r). With it, 16-byte operand reads of 8 consecutive rows,
+// 16-byte staging writes of one row, and 4-row x 16-column transposing reads
+// (ds_read_b64_tr_b16) each touch distinct bank slots.
+__device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+template <int D>
+__device__ __forceinline__ int rm_byte(int row, int col) {   // col: element index, multiple of 4
+  return row * (2 * D) + (((col >> 3) ^ rsw(row)) << 4) + ((col & 7) << 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane
+// group, lane j receives element (j % 4) of the 4-value row addressed by lane
+// 4k + j / 4, for k = 0..3. When the 16 lanes address rows r..r+3 x columns
+// c..c+15 of a row-major bf16 tile (lane i -> row r + i/4, columns
+// c + 4(i%4) .. +3), lane j receives column c + j of rows r..r+3.
+__device__ __forceinline__ u32x2 tr16(const char* lds_base, int byte) {
+  lds_s16x4* p = (lds_s16x4*)((__attribute__((address_space(3))) char*)lds_base + byte);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
+
+// MFMA operand (32 output indices x 16 contraction values) read transposed from
+// a row-major tile whose rows are the contraction index: lane l gets output
+// index obase + (l & 31) and contraction rows r0 + 0..3 (elements 0..3) and
+// r1 + 0..3 (elements 4..7), r0 / r1 chosen per lane half by the caller.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const char* base, int lane, int obase, int r0, int r1) {
+  const int i = lane & 15;
+  const int col = obase + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+  const u32x2 x = tr16(base, rm_byte<D>(r0 + (i >> 2), col));
+  const u32x2 y = tr16(base, rm_byte<D>(r1 + (i >> 2), col));
+  return u32x4{x[0], x[1], y[0], y[1]};
+}
+
+// Compact the non-SKIP entries of one class-map row (entries [first,
+// first + count)) into sm_list in ascending order, flagging PARTIAL ones;
+// returns the number of entries. CAP / NT entries per thread. Starts and ends
+// with a barrier, so callers may reuse every LDS buffer around it.
+template <int CAP, int NT>
+__device__ __forceinline__ int compact_classes(const uint8_t* row, int first, int count, uint32_t* sm_list,
+                                               int32_t* sm_scan, int tid) {
+  constexpr int PER = CAP / NT;
+  constexpr int NWAVE = NT / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  uint8_t cls[PER];
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid * PER + e;
+    cls[e] = idx < count ? row[first + idx] : (uint8_t)FM_TILE_SKIP;
+    cnt += cls[e] != FM_TILE_SKIP;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) sm_scan[wave] = incl;
+  __syncthreads();
+  int pos = incl - cnt, n_list = 0;
+#pragma unroll
+  for (int ww = 0; ww < NWAVE; ++ww) {
+    if (ww < wave) pos += sm_scan[ww];
+    n_list += sm_scan[ww];
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (cls[e] != FM_TILE_SKIP) {
+      const uint32_t id = (uint32_t)(first + tid * PER + e);
+      sm_list[pos++] = id | (cls[e] == FM_TILE_PARTIAL ? kPartialBit : 0u);
+    }
+  }
+  __syncthreads();
+  return n_list;
+}
+
+// Global -> registers for a row-major [rows][D] tile slice: 16-byte chunk
+// ci = tid + i * NT holds row ci / (D/8), elements 8 * (ci % (D/8)) .. +8.
+// tile_offsets() gives each chunk's byte offset from the tile's first row
+// (computed once per kernel); `tile` is that row's byte address (uniform).
+// In a ragged tile, rows at or past `nvalid` are re-read from row nvalid - 1
+// (callers mask or discard them), so no load leaves the tensor.
+template <int D, bool F32, int CHUNKS, int NT>
+__device__ __forceinline__ void tile_offsets(uint32_t (&off)[CHUNKS], int64_t ld, int tid) {
+  constexpr int ES = F32 ? 4 : 2;
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i) {
+    const int ci = tid + i * NT;
+    off[i] = (uint32_t)((ci / (D / 8)) * ld + (ci % (D / 8)) * 8 * ES);
+  }
+}
+
+template <int D, bool F32, int CHUNKS, int NT>
+__device__ __forceinline__ void load_tile_rows(u32x4 (&r)[CHUNKS], const char* tile, const uint32_t (&off)[CHUNKS],
+                                               int64_t ld, int tid, int nvalid) {
+  constexpr int ES = F32 ? 4 : 2;
+  constexpr int ROWS = CHUNKS * NT / (D / 8);
+  if (nvalid >= ROWS) {
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) r[i] = load8_as_bf16<F32>(tile + off[i], 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      const int ci = tid + i * NT;
+      const int row = min(ci / (D / 8), nvalid - 1);
+      r[i] = load8_as_bf16<F32>(tile + (int64_t)row * ld + (ci % (D / 8)) * 8 * ES, 0);
+    }
+  }
+}
+
+// Registers -> LDS for the same slice (row-major, swizzled).
+template <int D, int CHUNKS, int NT>
+__device__ __forceinline__ void store_tile_rows(char* lds, const u32x4 (&r)[CHUNKS], int tid) {
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i) {
+    const int ci = tid + i * NT;
+    *reinterpret_cast<u32x4*>(lds + rm_byte<D>(ci / (D / 8), 8 * (ci % (D / 8)))) = r[i];
+  }
+}
+
+}  // namespace fm
