@@ -27,6 +27,7 @@
 
 #include "fm_device.hpp"
 #include "fm_internal.hpp"
+#include "fm_tile.hpp"
 
 namespace fm {
 namespace {
@@ -34,7 +35,6 @@ namespace {
 constexpr int NW = 4;            // wavefronts per workgroup
 constexpr int NT = NW * 64;      // threads per workgroup
 constexpr int LIST_CAP = 1024;   // class bytes compacted per pass (4 per thread)
-constexpr uint32_t kPartialBit = 0x80000000u;
 
 // ------------------------------------------------------------------ pre-pass
 template <int D, bool F32>
@@ -77,83 +77,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 #pragma unroll
   for (int o = TPR / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
   if (row < nrows && sub == 0) a.drow[((int64_t)b * a.heads + h) * a.seq_q + m] = part;
-}
-
-// ------------------------------------------------------------------ LDS helpers
-//
-// Row-major tiles (rows of D bf16) store 16-byte chunk ch of row r at chunk
-// ch ^ rsw(r). With it, 16-byte operand reads of 8 consecutive rows, the
-// 16-byte staging writes of one row, and 4-row x 16-column transposing reads
-// (ds_read_b64_tr_b16) each touch distinct bank slots.
-__device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
-template <int D>
-__device__ __forceinline__ int rm_byte(int row, int col) {   // col: element index, multiple of 4
-  return row * (2 * D) + (((col >> 3) ^ rsw(row)) << 4) + ((col & 7) << 1);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane
-// group, lane j receives element (j % 4) of the 4-value row addressed by lane
-// 4k + j / 4, for k = 0..3. When the 16 lanes address rows r..r+3 x columns
-// c..c+15 of a row-major bf16 tile (lane i -> row r + i/4, columns
-// c + 4(i%4) .. +3), lane j receives column c + j of rows r..r+3.
-__device__ __forceinline__ u32x2 tr16(const char* lds_base, int byte) {
-  lds_s16x4* p = (lds_s16x4*)((__attribute__((address_space(3))) char*)lds_base + byte);
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
-}
-
-// MFMA operand (32 output indices x 16 contraction values) read transposed from
-// a row-major tile whose rows are the contraction index: lane l gets output
-// index obase + (l & 31) and contraction rows r0 + 0..3 (elements 0..3) and
-// r1 + 0..3 (elements 4..7), r0 / r1 chosen per lane half by the caller.
-template <int D>
-__device__ __forceinline__ u32x4 tr_operand(const char* base, int lane, int obase, int r0, int r1) {
-  const int i = lane & 15;
-  const int col = obase + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-  const u32x2 x = tr16(base, rm_byte<D>(r0 + (i >> 2), col));
-  const u32x2 y = tr16(base, rm_byte<D>(r1 + (i >> 2), col));
-  return u32x4{x[0], x[1], y[0], y[1]};
-}
-
-// Compact the non-SKIP entries of one class-map row into sm_list (ascending),
-// flagging PARTIAL ones; returns the count. Ends with a barrier.
-__device__ __forceinline__ int compact_classes(const uint8_t* row, int first, int count, uint32_t* sm_list,
-                                               int32_t* sm_scan, int tid, int lane, int wave) {
-  uint8_t cls[LIST_CAP / NT];
-  int cnt = 0;
-#pragma unroll
-  for (int e = 0; e < LIST_CAP / NT; ++e) {
-    const int idx = tid * (LIST_CAP / NT) + e;
-    cls[e] = idx < count ? row[first + idx] : (uint8_t)FM_TILE_SKIP;
-    cnt += cls[e] != FM_TILE_SKIP;
-  }
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  __syncthreads();   // every wave is done with the previous list and all tile buffers
-  if (lane == 63) sm_scan[wave] = incl;
-  __syncthreads();
-  int pos = incl - cnt, n_list = 0;
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) {
-    if (ww < wave) pos += sm_scan[ww];
-    n_list += sm_scan[ww];
-  }
-#pragma unroll
-  for (int e = 0; e < LIST_CAP / NT; ++e) {
-    if (cls[e] != FM_TILE_SKIP) {
-      const uint32_t id = (uint32_t)(first + tid * (LIST_CAP / NT) + e);
-      sm_list[pos++] = id | (cls[e] == FM_TILE_PARTIAL ? kPartialBit : 0u);
-    }
-  }
-  __syncthreads();
-  return n_list;
 }
 
 // ------------------------------------------------------------------ dK / dV
@@ -202,14 +125,16 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const bool key_ok = n < a.seq_k;
 
   // K and V rows of this lane's key as MFMA B operands (channels 16s + 8g ..).
+  // (keys past the end re-read the last key; the ragged tile masks them)
   u32x4 kf[KSTEPS], vf[KSTEPS];
   {
-    const int64_t koff = (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)h * a.k_sh + 8 * g;
-    const int64_t voff = (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)h * a.v_sh + 8 * g;
+    const int nk = min(n, a.seq_k - 1);
+    const int64_t koff = (int64_t)b * a.k_sb + (int64_t)nk * a.k_ss + (int64_t)h * a.k_sh + 8 * g;
+    const int64_t voff = (int64_t)b * a.v_sb + (int64_t)nk * a.v_ss + (int64_t)h * a.v_sh + 8 * g;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      kf[s] = key_ok ? load8_as_bf16<F32>(a.k, koff + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      vf[s] = key_ok ? load8_as_bf16<F32>(a.v, voff + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      kf[s] = load8_as_bf16<F32>(a.k, koff + 16 * s);
+      vf[s] = load8_as_bf16<F32>(a.v, voff + 16 * s);
     }
   }
   // The lane's key bounds (keys past the end are masked for every row).
@@ -232,23 +157,20 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_q;
 
   // ---- registers carrying one query tile (Q, dO, LSE, D) to LDS ----
+  // Rows past the end re-read the last row; their LSE is +inf, so P = dS = 0.
+  constexpr int ES = F32 ? 4 : 2;
+  const int64_t q_ld = a.q_ss * ES, o_ld = a.o_ss * ES;
+  const char* qbh = reinterpret_cast<const char*>(a.q) + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ES;
+  const char* dbh = reinterpret_cast<const char*>(a.dout) + ((int64_t)b * a.o_sb + (int64_t)h * a.o_sh) * ES;
+  uint32_t qoff[QR], doff[QR];
+  tile_offsets<D, F32, QR, NT>(qoff, q_ld, tid);
+  tile_offsets<D, F32, QR, NT>(doff, o_ld, tid);
   u32x4 rq[QR], rd[QR];
   float rl2 = INFINITY, rdd = 0.f;
   auto load_q = [&](int qt) {
     const int m0 = qt * BQ;
-#pragma unroll
-    for (int i = 0; i < QR; ++i) {
-      const int ci = tid + i * NT;
-      const int mm = m0 + ci / (D / 8);
-      const int ch = ci % (D / 8);
-      if (mm < a.seq_q) {
-        rq[i] = load8_as_bf16<F32>(a.q, (int64_t)b * a.q_sb + (int64_t)mm * a.q_ss + (int64_t)h * a.q_sh + 8 * ch);
-        rd[i] = load8_as_bf16<F32>(a.dout, (int64_t)b * a.o_sb + (int64_t)mm * a.o_ss + (int64_t)h * a.o_sh + 8 * ch);
-      } else {
-        rq[i] = u32x4{0u, 0u, 0u, 0u};
-        rd[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    load_tile_rows<D, F32, QR, NT>(rq, qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
+    load_tile_rows<D, F32, QR, NT>(rd, dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
     if (tid < BQ) {
       const int mm = m0 + tid;
       rl2 = INFINITY;
@@ -261,15 +183,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   auto store_q = [&](int buf) {
-    char* qb = reinterpret_cast<char*>(sm.q[buf]);
-    char* db = reinterpret_cast<char*>(sm.dout[buf]);
-#pragma unroll
-    for (int i = 0; i < QR; ++i) {
-      const int ci = tid + i * NT;
-      const int off = rm_byte<D>(ci / (D / 8), 8 * (ci % (D / 8)));
-      *reinterpret_cast<u32x4*>(qb + off) = rq[i];
-      *reinterpret_cast<u32x4*>(db + off) = rd[i];
-    }
+    store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.q[buf]), rq, tid);
+    store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.dout[buf]), rd, tid);
     if (tid < BQ) {
       sm.lse2[buf][tid] = rl2;
       sm.dd[buf][tid] = rdd;
@@ -278,7 +193,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
 
   int it_global = 0;
   for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
-    const int n_list = compact_classes(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.scan, tid, l, w);
+    const int n_list = compact_classes<LIST_CAP, NT>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.scan, tid);
     if (n_list == 0) continue;
 
     uint32_t ent = sm.list[0];
@@ -326,7 +241,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
             float p = fast_exp2(fmaf(sacc[mb][i], C, -l2[r]));
             if (masked_tile) {
               const int mm = m0 + ml + r;
-              const bool mk = (b_lts <= mm && mm < b_lte) || (b_uts <= mm && mm < b_ute);
+              const bool mk = ((b_lts <= mm) & (mm < b_lte)) | ((b_uts <= mm) & (mm < b_ute));
               p = mk ? 0.f : p;
             }
             sacc[mb][i] = p;
@@ -429,15 +344,17 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
   const bool row_ok = m < a.seq_q;
 
   // Q and dO rows of this lane's query as MFMA B operands; its LSE and D.
+  // (rows past the end re-read the last row; their results are never stored)
   u32x4 qf[KSTEPS], df[KSTEPS];
   float l2 = INFINITY, dd = 0.f;
   {
-    const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
-    const int64_t doff = (int64_t)b * a.o_sb + (int64_t)m * a.o_ss + (int64_t)h * a.o_sh + 8 * g;
+    const int mq = min(m, a.seq_q - 1);
+    const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)mq * a.q_ss + (int64_t)h * a.q_sh + 8 * g;
+    const int64_t doff = (int64_t)b * a.o_sb + (int64_t)mq * a.o_ss + (int64_t)h * a.o_sh + 8 * g;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      qf[s] = row_ok ? load8_as_bf16<F32>(a.q, qoff + 16 * s) : u32x4{0u, 0u, 0u, 0u};
-      df[s] = row_ok ? load8_as_bf16<F32>(a.dout, doff + 16 * s) : u32x4{0u, 0u, 0u, 0u};
+      qf[s] = load8_as_bf16<F32>(a.q, qoff + 16 * s);
+      df[s] = load8_as_bf16<F32>(a.dout, doff + 16 * s);
     }
     if (row_ok) {
       const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_q + m;
@@ -454,23 +371,19 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
   const bool ragged_k = (a.seq_k % BK) != 0;
 
   // ---- registers carrying one key tile (K, V, bounds) to LDS ----
+  constexpr int ES = F32 ? 4 : 2;
+  const int64_t k_ld = a.k_ss * ES, v_ld = a.v_ss * ES;
+  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
+  const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * ES;
+  uint32_t koff[KR], voff[KR];
+  tile_offsets<D, F32, KR, NT>(koff, k_ld, tid);
+  tile_offsets<D, F32, KR, NT>(voff, v_ld, tid);
   u32x4 rk[KR], rv[KR];
   int32_t rb[4] = {INT_MIN, INT_MAX, 0, 0};
   auto load_k = [&](int kt, bool masked) {
     const int n0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < KR; ++i) {
-      const int ci = tid + i * NT;
-      const int nn = n0 + ci / (D / 8);
-      const int ch = ci % (D / 8);
-      if (nn < a.seq_k) {
-        rk[i] = load8_as_bf16<F32>(a.k, (int64_t)b * a.k_sb + (int64_t)nn * a.k_ss + (int64_t)h * a.k_sh + 8 * ch);
-        rv[i] = load8_as_bf16<F32>(a.v, (int64_t)b * a.v_sb + (int64_t)nn * a.v_ss + (int64_t)h * a.v_sh + 8 * ch);
-      } else {
-        rk[i] = u32x4{0u, 0u, 0u, 0u};
-        rv[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    load_tile_rows<D, F32, KR, NT>(rk, kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
+    load_tile_rows<D, F32, KR, NT>(rv, vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
     if (masked && tid < BK) {
       const int nn = n0 + tid;
       if (nn < a.seq_k) {
@@ -487,15 +400,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
     }
   };
   auto store_k = [&](int buf, bool masked) {
-    char* kb = reinterpret_cast<char*>(sm.k[buf]);
-    char* vb = reinterpret_cast<char*>(sm.v[buf]);
-#pragma unroll
-    for (int i = 0; i < KR; ++i) {
-      const int ci = tid + i * NT;
-      const int off = rm_byte<D>(ci / (D / 8), 8 * (ci % (D / 8)));
-      *reinterpret_cast<u32x4*>(kb + off) = rk[i];
-      *reinterpret_cast<u32x4*>(vb + off) = rv[i];
-    }
+    store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.k[buf]), rk, tid);
+    store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.v[buf]), rv, tid);
     if (masked && tid < BK) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.bnd[buf][j][tid] = rb[j];
@@ -507,7 +413,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
 
   int it_global = 0;
   for (int kt0 = 0; kt0 < a.tk_q; kt0 += LIST_CAP) {
-    const int n_list = compact_classes(crow, kt0, min(LIST_CAP, a.tk_q - kt0), sm.list, sm.scan, tid, l, w);
+    const int n_list = compact_classes<LIST_CAP, NT>(crow, kt0, min(LIST_CAP, a.tk_q - kt0), sm.list, sm.scan, tid);
     if (n_list == 0) continue;
 
     uint32_t ent = sm.list[0];
@@ -543,15 +449,25 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(sacc[nb][i], C, -l2));
+        for (int q4 = 0; q4 < 4; ++q4) {
+          i32x4 l0, l1, u0, u1;
           if (masked_tile) {
-            const int nl = 32 * nb + 8 * (i >> 2) + 4 * g + (i & 3);
-            const bool mk = (sm.bnd[buf][0][nl] <= m && m < sm.bnd[buf][1][nl]) ||
-                            (sm.bnd[buf][2][nl] <= m && m < sm.bnd[buf][3][nl]);
-            p = mk ? 0.f : p;
+            const int nl = 32 * nb + 8 * q4 + 4 * g;   // 4 consecutive keys
+            l0 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][0][nl]);
+            l1 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][1][nl]);
+            u0 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][2][nl]);
+            u1 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][3][nl]);
           }
-          dpacc[nb][i] = p * (dpacc[nb][i] - dd);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * q4 + r;
+            float p = fast_exp2(fmaf(sacc[nb][i], C, -l2));
+            if (masked_tile) {
+              const bool mk = ((l0[r] <= m) & (m < l1[r])) | ((u0[r] <= m) & (m < u1[r]));
+              p = mk ? 0.f : p;
+            }
+            dpacc[nb][i] = p * (dpacc[nb][i] - dd);
+          }
         }
       }
 
