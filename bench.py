@@ -44,6 +44,29 @@ def nnz_of(vectors, seq_q, batch, heads):
     return total
 
 
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summaries under profiles/, or None when none was
+    taken on the kernel's current source (sha256 prefix recorded with it)."""
+    import glob
+    import hashlib
+    import re
+    root = os.path.dirname(os.path.abspath(__file__))
+    src = {"fwd": "fwd.hip", "bwd": "bwd.hip", "bwd_dq": "bwd.hip"}.get(kernel)
+    if src is None:
+        return None
+    with open(os.path.join(root, "masked_tiled_attention_amd", "csrc", src), "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    pat = re.compile(r"traffic: kernel=(\S+) workload=(\S+) source=(\S+) sha256=(\S+) bytes=(\d+)")
+    for path in sorted(glob.glob(os.path.join(root, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                m = pat.match(line.strip())
+                if m and m[1] == kernel and m[2] == workload and m[3] == src and m[4] == digest:
+                    return int(m[5])
+    return None
+
+
 class Runner:
     """Device-resident inputs, outputs and workspaces of one workload."""
 
@@ -118,7 +141,7 @@ def cpu_baseline(w, vectors, budget_rows=None):
     except Exception:
         threads = len(os.sched_getaffinity(0))
     d = w.head_dim
-    rows = budget_rows or max(128, min(w.seq_q, int(5e9 / (w.seq_k * d))))
+    rows = budget_rows or max(128, min(w.seq_q, int(7e10 / (w.seq_k * d))))
     r0 = max(0, (w.seq_q - rows) // 2)
     loc = OM.localize(tuple(x[:1, :1] for x in vectors), [r0], [rows])
     q = w.q[:1, r0:r0 + rows, :1].double().numpy()
@@ -226,7 +249,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": kern, "kernel_ms": round(kms, 4),
                      "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(kern, w.name)},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
