@@ -29,11 +29,18 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Two floats -> packed bf16 pair (round to nearest even; hardware convert).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// acc + lo(x) + hi(x) for a packed bf16 pair, one v_dot2c_f32_bf16.
+__device__ __forceinline__ float add_bf16_pair(uint32_t x, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }

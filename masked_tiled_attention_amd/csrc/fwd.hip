@@ -218,28 +218,33 @@ void fwd_kernel(FwdArgs a) {
       }
       m_run = move ? m_cand : m_run;
       const float mC = (m_run == -INFINITY ? 0.f : m_run) * C;
-      float rs = 0.f;
+      // P rounded to bf16 as the MFMA consumes it; the row sum adds the same
+      // rounded values (two per v_dot2c), so O and l share one set of weights.
+      u32x4 pf[NB][2];
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(sacc[nb][i], C, -mC));
-          sacc[nb][i] = p;
-          rs += p;
-        }
-      l_run += rs;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p0 = fast_exp2(fmaf(sacc[nb][8 * t + 2 * j], C, -mC));
+            const float p1 = fast_exp2(fmaf(sacc[nb][8 * t + 2 * j + 1], C, -mC));
+            pf[nb][t][j] = pack_bf16(p0, p1);
+            if (j & 1) rs1 = add_bf16_pair(pf[nb][t][j], rs1);
+            else rs0 = add_bf16_pair(pf[nb][t][j], rs0);
+          }
+      l_run += rs0 + rs1;
 
       // ---- O^T += V^T P^T ----
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          u32x4 pf;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) pf[j] = pack_bf16(sacc[nb][8 * t + 2 * j], sacc[nb][8 * t + 2 * j + 1]);
           const int r0 = nb * 32 + 16 * t + 4 * g;   // first of this lane's 4-key groups
 #pragma unroll
-          for (int cb = 0; cb < CB; ++cb) oacc[cb] = mfma32(tr_operand<D>(vb, l, cb * 32, r0, r0 + 8), pf, oacc[cb]);
+          for (int cb = 0; cb < CB; ++cb)
+            oacc[cb] = mfma32(tr_operand<D>(vb, l, cb * 32, r0, r0 + 8), pf[nb][t], oacc[cb]);
         }
       }
     }
