@@ -226,6 +226,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
           dpacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(db + off), vf[s], dpacc[mb]);
         }
       }
+      sched_lds_mfma<4 * KSTEPS, 1, 4>();
 
       // ---- P and dS ----
 #pragma unroll
@@ -269,6 +270,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
           }
         }
       }
+      sched_lds_mfma<2 * 2 * 2 * CB, 2, 3>();
     }
   }
 
@@ -444,6 +446,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
           dpacc[nb] = mfma32(*reinterpret_cast<const u32x4*>(vb + off), df[s], dpacc[nb]);
         }
       }
+      sched_lds_mfma<2 * NB * KSTEPS, 1, 4>();
 
       // ---- P and dS for this lane's row ----
 #pragma unroll
@@ -485,6 +488,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
             dqacc[cb] = mfma32(tr_operand<D>(kb, l, 32 * cb, r0, r0 + 8), dsp, dqacc[cb]);
         }
       }
+      sched_lds_mfma<NB * 2 * CB, 2, 3>();
     }
   }
 

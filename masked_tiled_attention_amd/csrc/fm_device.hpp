@@ -71,6 +71,21 @@ __device__ __forceinline__ u32x4 load8_as_bf16(const void* base, int64_t elem_of
   }
 }
 
+// Instruction-order hints for the machine scheduler (one basic block):
+// N MFMAs, each consuming R LDS reads, with the reads of the next DEPTH MFMAs
+// issued ahead, so that DEPTH * R reads stay in flight behind each MFMA.
+// Masks: 0x008 MFMA, 0x100 LDS read.
+template <int N, int R, int DEPTH>
+__device__ __forceinline__ void sched_lds_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, DEPTH * R, 0);
+#pragma unroll
+  for (int j = 0; j < N - DEPTH; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, DEPTH, 0);
+}
+
 // Lane id within the wavefront.
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

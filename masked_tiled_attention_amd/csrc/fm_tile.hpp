@@ -10,14 +10,28 @@ namespace fm {
 constexpr uint32_t kPartialBit = 0x80000000u;   // list entry flag: tile needs the mask
 
 // Row-major bf16 tiles (rows of D elements) store 16-byte chunk ch of row r at
-// chunk ch ^ rsw(r). With it, 16-byte operand reads of 8 consecutive rows,
-// 16-byte staging writes of one row, and 4-row x 16-column transposing reads
-// (ds_read_b64_tr_b16) each touch distinct bank slots.
-__device__ __forceinline__ int rsw(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// chunk ch ^ swz<D>(r). The gfx950 LDS has 64 four-byte banks; a 16-byte read
+// is served 16 lanes per cycle and an 8-byte read 32 lanes per cycle. With the
+// swizzle, 16-byte operand reads of 16 consecutive rows, 16-byte staging
+// writes of one row, and 4-row x 32-column transposing reads
+// (ds_read_b64_tr_b16) each touch every bank once per cycle.
+//   D = 128 (256-byte rows, one bank sweep per row): the two low bit pairs of
+//     r swapped, so 16 consecutive rows get distinct chunk offsets and 4
+//     consecutive rows differ in the chunk-group bits [3:2].
+//   D = 64 (128-byte rows, two rows per bank sweep): a bijection of r[3:1]
+//     with r[1] on chunk bit 2.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
+  }
+}
 
 template <int D>
 __device__ __forceinline__ int rm_byte(int row, int col) {   // col: element index, multiple of 4
-  return row * (2 * D) + (((col >> 3) ^ rsw(row)) << 4) + ((col & 7) << 1);
+  return row * (2 * D) + (((col >> 3) ^ swz<D>(row)) << 4) + ((col & 7) << 1);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

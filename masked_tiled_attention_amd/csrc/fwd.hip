@@ -176,6 +176,7 @@ void fwd_kernel(FwdArgs a) {
           sacc[nb] = mfma32(*reinterpret_cast<const u32x4*>(kb + rm_byte<D>(nb * 32 + lr, 16 * s + 8 * g)), qf[s],
                             sacc[nb]);
       }
+      sched_lds_mfma<NB * KSTEPS, 1, 4>();
 
       // ---- interval mask on PARTIAL (and ragged) tiles only ----
       if (masked_tile) {
@@ -247,6 +248,7 @@ void fwd_kernel(FwdArgs a) {
             oacc[cb] = mfma32(tr_operand<D>(vb, l, cb * 32, r0, r0 + 8), pf[nb][t], oacc[cb]);
         }
       }
+      sched_lds_mfma<NB * 2 * CB, 2, 3>();
     }
   }
 
