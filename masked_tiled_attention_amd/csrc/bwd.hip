@@ -156,21 +156,36 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const float C = a.scale_log2;
   const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_q;
 
-  // ---- registers carrying one query tile (Q, dO, LSE, D) to LDS ----
-  // Rows past the end re-read the last row; their LSE is +inf, so P = dS = 0.
+  // ---- query tile staging (Q, dO; LSE and D through registers) ----
+  // bf16: Q and dO straight from global memory into LDS; float32: through
+  // registers, rounded to bf16 on the way. Rows past the end re-read the last
+  // row; their LSE is +inf, so P = dS = 0.
   constexpr int ES = F32 ? 4 : 2;
   const int64_t q_ld = a.q_ss * ES, o_ld = a.o_ss * ES;
   const char* qbh = reinterpret_cast<const char*>(a.q) + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ES;
   const char* dbh = reinterpret_cast<const char*>(a.dout) + ((int64_t)b * a.o_sb + (int64_t)h * a.o_sh) * ES;
-  uint32_t qoff[QR], doff[QR];
-  tile_offsets<D, F32, QR, NT>(qoff, q_ld, tid);
-  tile_offsets<D, F32, QR, NT>(doff, o_ld, tid);
-  u32x4 rq[QR], rd[QR];
+  using Dma = DmaTile<D, BQ, NT>;
+  constexpr int NOFF = F32 ? QR : Dma::PER;
+  constexpr int NREG = F32 ? QR : 1;
+  uint32_t qoff[NOFF], doff[NOFF];
+  if constexpr (F32) {
+    tile_offsets<D, F32, QR, NT>(qoff, q_ld, tid);
+    tile_offsets<D, F32, QR, NT>(doff, o_ld, tid);
+  } else {
+    Dma::offsets(qoff, q_ld, tid);
+    Dma::offsets(doff, o_ld, tid);
+  }
+  u32x4 rq[NREG], rd[NREG];
   float rl2 = INFINITY, rdd = 0.f;
-  auto load_q = [&](int qt) {
+  auto load_q = [&](int qt, int buf) {
     const int m0 = qt * BQ;
-    load_tile_rows<D, F32, QR, NT>(rq, qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
-    load_tile_rows<D, F32, QR, NT>(rd, dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
+    if constexpr (F32) {
+      load_tile_rows<D, F32, QR, NT>(rq, qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
+      load_tile_rows<D, F32, QR, NT>(rd, dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
+    } else {
+      Dma::load(reinterpret_cast<char*>(sm.q[buf]), qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
+      Dma::load(reinterpret_cast<char*>(sm.dout[buf]), dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
+    }
     if (tid < BQ) {
       const int mm = m0 + tid;
       rl2 = INFINITY;
@@ -183,8 +198,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   auto store_q = [&](int buf) {
-    store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.q[buf]), rq, tid);
-    store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.dout[buf]), rd, tid);
+    if constexpr (F32) {
+      store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.q[buf]), rq, tid);
+      store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.dout[buf]), rd, tid);
+    }
     if (tid < BQ) {
       sm.lse2[buf][tid] = rl2;
       sm.dd[buf][tid] = rdd;
@@ -197,7 +214,7 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     if (n_list == 0) continue;
 
     uint32_t ent = sm.list[0];
-    load_q((int)(ent & ~kPartialBit));
+    load_q((int)(ent & ~kPartialBit), it_global & 1);
 
     for (int it = 0; it < n_list; ++it, ++it_global) {
       const int buf = it_global & 1;
@@ -205,10 +222,11 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       const bool masked_tile = (ent & kPartialBit) || ragged_k;
       const int m0 = qt * BQ;
       store_q(buf);
-      __syncthreads();   // tile `buf` visible; the other buffer is free
+      wait_vmem();
+      __syncthreads();   // tile `buf` complete and visible; the other buffer is free
       if (it + 1 < n_list) {   // the next query tile's loads overlap this tile's math
         ent = sm.list[it + 1];
-        load_q((int)(ent & ~kPartialBit));
+        load_q((int)(ent & ~kPartialBit), buf ^ 1);
       }
       const char* qb = reinterpret_cast<const char*>(sm.q[buf]);
       const char* db = reinterpret_cast<const char*>(sm.dout[buf]);
@@ -372,20 +390,35 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
   const float C = a.scale_log2;
   const bool ragged_k = (a.seq_k % BK) != 0;
 
-  // ---- registers carrying one key tile (K, V, bounds) to LDS ----
+  // ---- key tile staging (K, V; bounds through registers) ----
+  // bf16: straight from global memory into LDS; float32: through registers,
+  // rounded to bf16 on the way.
   constexpr int ES = F32 ? 4 : 2;
   const int64_t k_ld = a.k_ss * ES, v_ld = a.v_ss * ES;
   const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
   const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * ES;
-  uint32_t koff[KR], voff[KR];
-  tile_offsets<D, F32, KR, NT>(koff, k_ld, tid);
-  tile_offsets<D, F32, KR, NT>(voff, v_ld, tid);
-  u32x4 rk[KR], rv[KR];
+  using Dma = DmaTile<D, BK, NT>;
+  constexpr int NOFF = F32 ? KR : Dma::PER;
+  constexpr int NREG = F32 ? KR : 1;
+  uint32_t koff[NOFF], voff[NOFF];
+  if constexpr (F32) {
+    tile_offsets<D, F32, KR, NT>(koff, k_ld, tid);
+    tile_offsets<D, F32, KR, NT>(voff, v_ld, tid);
+  } else {
+    Dma::offsets(koff, k_ld, tid);
+    Dma::offsets(voff, v_ld, tid);
+  }
+  u32x4 rk[NREG], rv[NREG];
   int32_t rb[4] = {INT_MIN, INT_MAX, 0, 0};
-  auto load_k = [&](int kt, bool masked) {
+  auto load_k = [&](int kt, bool masked, int buf) {
     const int n0 = kt * BK;
-    load_tile_rows<D, F32, KR, NT>(rk, kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
-    load_tile_rows<D, F32, KR, NT>(rv, vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
+    if constexpr (F32) {
+      load_tile_rows<D, F32, KR, NT>(rk, kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
+      load_tile_rows<D, F32, KR, NT>(rv, vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
+    } else {
+      Dma::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
+      Dma::load(reinterpret_cast<char*>(sm.v[buf]), vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
+    }
     if (masked && tid < BK) {
       const int nn = n0 + tid;
       if (nn < a.seq_k) {
@@ -402,8 +435,10 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
     }
   };
   auto store_k = [&](int buf, bool masked) {
-    store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.k[buf]), rk, tid);
-    store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.v[buf]), rv, tid);
+    if constexpr (F32) {
+      store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.k[buf]), rk, tid);
+      store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.v[buf]), rv, tid);
+    }
     if (masked && tid < BK) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.bnd[buf][j][tid] = rb[j];
@@ -419,16 +454,17 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
     if (n_list == 0) continue;
 
     uint32_t ent = sm.list[0];
-    load_k((int)(ent & ~kPartialBit), masked_of(ent));
+    load_k((int)(ent & ~kPartialBit), masked_of(ent), it_global & 1);
 
     for (int it = 0; it < n_list; ++it, ++it_global) {
       const int buf = it_global & 1;
       const bool masked_tile = masked_of(ent);
       store_k(buf, masked_tile);
-      __syncthreads();   // tile `buf` visible; the other buffer is free
+      wait_vmem();
+      __syncthreads();   // tile `buf` complete and visible; the other buffer is free
       if (it + 1 < n_list) {   // the next key tile's loads overlap this tile's math
         ent = sm.list[it + 1];
-        load_k((int)(ent & ~kPartialBit), masked_of(ent));
+        load_k((int)(ent & ~kPartialBit), masked_of(ent), buf ^ 1);
       }
       const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
       const char* vb = reinterpret_cast<const char*>(sm.v[buf]);

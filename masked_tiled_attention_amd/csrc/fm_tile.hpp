@@ -148,4 +148,77 @@ __device__ __forceinline__ void store_tile_rows(char* lds, const u32x4 (&r)[CHUN
   }
 }
 
+// Direct global -> LDS staging (gfx950 global_load_lds, 16 bytes per lane) of
+// a [ROWS][D] bf16 tile into the swizzled row-major layout, without passing
+// through registers. One wave instruction fills one contiguous KiB of LDS
+// (lane l writes bytes 16 l .. 16 l + 15 of it), so lane l fetches the logical
+// chunk that the swizzle stores at that position. KiB block b = i * NW + w is
+// written by wavefront w's i-th instruction.
+template <int D, int ROWS, int NT>
+struct DmaTile {
+  static constexpr int NW = NT / 64;
+  static constexpr int BLOCKS = ROWS * D * 2 / 1024;
+  static constexpr int PER = BLOCKS / NW;   // instructions per wavefront
+  static constexpr int RPB = 512 / D;       // rows per KiB block
+  static_assert(PER * NW == BLOCKS, "tile must split evenly over the wavefronts");
+
+  // Byte offset (from the tile's first row) of the chunk lane `lane` of
+  // wavefront `w` fetches in instruction i; row clamped to nvalid - 1.
+  __device__ static __forceinline__ uint32_t offset(int i, int w, int lane, int64_t ld, int nvalid) {
+    const int row = (i * NW + w) * RPB + (16 * lane) / (2 * D);
+    const int pc = ((16 * lane) % (2 * D)) / 16;
+    const int ch = pc ^ swz<D>(row);
+    return (uint32_t)(min(row, nvalid - 1) * ld + ch * 16);
+  }
+
+  __device__ static __forceinline__ void offsets(uint32_t (&off)[PER], int64_t ld, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) off[i] = offset(i, tid >> 6, tid & 63, ld, ROWS);
+  }
+
+  // Issue the tile's loads; `lds` is the tile's LDS base. Rows at or past
+  // `nvalid` re-read row nvalid - 1. The caller awaits completion with
+  // wait_vmem() before the barrier that publishes the tile.
+  __device__ static __forceinline__ void load(char* lds, const char* tile, const uint32_t (&off)[PER], int64_t ld,
+                                              int tid, int nvalid) {
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t base = lds_address(lds) + (uint32_t)w * 1024u;
+    if (nvalid >= ROWS) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) dma16(tile, off[i], base + (uint32_t)(i * NW) * 1024u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) dma16(tile, offset(i, w, tid & 63, ld, nvalid), base + (uint32_t)(i * NW) * 1024u);
+    }
+  }
+
+  __device__ static __forceinline__ uint32_t lds_address(const char* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  }
+
+  // One global_load_lds_dwordx4: lane l copies 16 bytes from base + voff(l)
+  // to LDS byte lds_dst + 16 l. Written as inline assembly so that the
+  // compiler, which cannot tell the two LDS buffers apart, does not hold back
+  // reads of the other buffer until this load lands; the M0 write is followed
+  // by the one wait state the LDS-DMA hazard needs.
+  // No other code in these kernels keeps a value in M0, so clobbering it here
+  // is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  __device__ static __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_dst) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_dst), "v"(voff), "s"(base)
+        : "memory", "m0");
+  }
+#pragma clang diagnostic pop
+};
+
+// Wait until this wavefront's outstanding global loads (including the direct
+// loads into LDS above) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 }  // namespace fm

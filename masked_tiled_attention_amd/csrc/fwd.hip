@@ -105,20 +105,37 @@ void fwd_kernel(FwdArgs a) {
   const float C = a.scale_log2;
   const bool ragged_k = (a.seq_k % BK) != 0;
 
-  // ---- tile staging: global -> registers -> LDS ----
+  // ---- tile staging ----
+  // bf16: straight from global memory into LDS (no staging registers);
+  // float32: through registers, rounded to bf16 on the way.
   const int64_t k_ld = a.k_ss * ES, v_ld = a.v_ss * ES;
   const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
   const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * ES;
-  uint32_t koff[KR], voff[KR];
-  tile_offsets<D, F32, KR, NT>(koff, k_ld, tid);
-  tile_offsets<D, F32, KR, NT>(voff, v_ld, tid);
-  u32x4 rk[KR], rv[KR];
+  using Dma = DmaTile<D, BK, NT>;
+  constexpr int NOFF = F32 ? KR : Dma::PER;
+  constexpr int NREG = F32 ? KR : 1;
+  uint32_t koff[NOFF], voff[NOFF];
+  if constexpr (F32) {
+    tile_offsets<D, F32, KR, NT>(koff, k_ld, tid);
+    tile_offsets<D, F32, KR, NT>(voff, v_ld, tid);
+  } else {
+    Dma::offsets(koff, k_ld, tid);
+    Dma::offsets(voff, v_ld, tid);
+  }
+  u32x4 rk[NREG], rv[NREG];
   int32_t rb[4] = {INT_MIN, INT_MAX, 0, 0};
 
-  auto load_tile = [&](int kt, bool masked) {
+  // Start fetching key tile kt into LDS buffer `buf` (bf16) or registers (f32),
+  // and its bounds into registers.
+  auto load_tile = [&](int kt, bool masked, int buf) {
     const int n0 = kt * BK;
-    load_tile_rows<D, F32, KR, NT>(rk, kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
-    load_tile_rows<D, F32, KR, NT>(rv, vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
+    if constexpr (F32) {
+      load_tile_rows<D, F32, KR, NT>(rk, kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
+      load_tile_rows<D, F32, KR, NT>(rv, vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
+    } else {
+      Dma::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
+      Dma::load(reinterpret_cast<char*>(sm.v[buf]), vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
+    }
     if (masked && tid < BK) {
       const int n = n0 + tid;
       if (n < a.seq_k) {
@@ -134,9 +151,12 @@ void fwd_kernel(FwdArgs a) {
       }
     }
   };
+  // Finish staging into buffer `buf` what load_tile() left in registers.
   auto store_tile = [&](int buf, bool masked) {
-    store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.k[buf]), rk, tid);
-    store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.v[buf]), rv, tid);
+    if constexpr (F32) {
+      store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.k[buf]), rk, tid);
+      store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.v[buf]), rv, tid);
+    }
     if (masked && tid < BK) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sm.bnd[buf][j][tid] = rb[j];
@@ -152,16 +172,17 @@ void fwd_kernel(FwdArgs a) {
     if (n_list == 0) continue;
 
     uint32_t ent = sm.list[0];
-    load_tile((int)(ent & ~kPartialBit), masked_of(ent));
+    load_tile((int)(ent & ~kPartialBit), masked_of(ent), it_global & 1);
 
     for (int it = 0; it < n_list; ++it, ++it_global) {
       const int buf = it_global & 1;
       const bool masked_tile = masked_of(ent);
       store_tile(buf, masked_tile);
-      __syncthreads();   // tile `buf` visible; the other buffer is free
+      wait_vmem();
+      __syncthreads();   // tile `buf` complete and visible; the other buffer is free
       if (it + 1 < n_list) {   // next tile's global loads overlap this tile's math
         ent = sm.list[it + 1];
-        load_tile((int)(ent & ~kPartialBit), masked_of(ent));
+        load_tile((int)(ent & ~kPartialBit), masked_of(ent), buf ^ 1);
       }
       const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
       const char* vb = reinterpret_cast<const char*>(sm.v[buf]);
