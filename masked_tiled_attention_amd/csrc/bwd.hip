@@ -165,15 +165,15 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const char* qbh = reinterpret_cast<const char*>(a.q) + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ES;
   const char* dbh = reinterpret_cast<const char*>(a.dout) + ((int64_t)b * a.o_sb + (int64_t)h * a.o_sh) * ES;
   using Dma = DmaTile<D, BQ, NT>;
-  constexpr int NOFF = F32 ? QR : Dma::PER;
+  constexpr int NOFF = F32 ? QR : 1;
   constexpr int NREG = F32 ? QR : 1;
   uint32_t qoff[NOFF], doff[NOFF];
   if constexpr (F32) {
     tile_offsets<D, F32, QR, NT>(qoff, q_ld, tid);
     tile_offsets<D, F32, QR, NT>(doff, o_ld, tid);
   } else {
-    Dma::offsets(qoff, q_ld, tid);
-    Dma::offsets(doff, o_ld, tid);
+    qoff[0] = Dma::offset(q_ld, tid);
+    doff[0] = Dma::offset(o_ld, tid);
   }
   u32x4 rq[NREG], rd[NREG];
   float rl2 = INFINITY, rdd = 0.f;
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       load_tile_rows<D, F32, QR, NT>(rq, qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
       load_tile_rows<D, F32, QR, NT>(rd, dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
     } else {
-      Dma::load(reinterpret_cast<char*>(sm.q[buf]), qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
-      Dma::load(reinterpret_cast<char*>(sm.dout[buf]), dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
+      Dma::load(reinterpret_cast<char*>(sm.q[buf]), qbh + m0 * q_ld, qoff[0], q_ld, tid, a.seq_q - m0);
+      Dma::load(reinterpret_cast<char*>(sm.dout[buf]), dbh + m0 * o_ld, doff[0], o_ld, tid, a.seq_q - m0);
     }
     if (tid < BQ) {
       const int mm = m0 + tid;
@@ -335,7 +335,7 @@ struct alignas(16) Smem {
 }  // namespace dqk
 
 template <int D, bool F32>
-__global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
   using namespace dqk;
   constexpr int KSTEPS = D / 16;
   constexpr int CB = D / 32;
@@ -398,15 +398,15 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
   const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
   const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * ES;
   using Dma = DmaTile<D, BK, NT>;
-  constexpr int NOFF = F32 ? KR : Dma::PER;
+  constexpr int NOFF = F32 ? KR : 1;
   constexpr int NREG = F32 ? KR : 1;
   uint32_t koff[NOFF], voff[NOFF];
   if constexpr (F32) {
     tile_offsets<D, F32, KR, NT>(koff, k_ld, tid);
     tile_offsets<D, F32, KR, NT>(voff, v_ld, tid);
   } else {
-    Dma::offsets(koff, k_ld, tid);
-    Dma::offsets(voff, v_ld, tid);
+    koff[0] = Dma::offset(k_ld, tid);
+    voff[0] = Dma::offset(v_ld, tid);
   }
   u32x4 rk[NREG], rv[NREG];
   int32_t rb[4] = {INT_MIN, INT_MAX, 0, 0};
@@ -416,8 +416,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_kernel(BwdArgs a) {
       load_tile_rows<D, F32, KR, NT>(rk, kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
       load_tile_rows<D, F32, KR, NT>(rv, vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
     } else {
-      Dma::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
-      Dma::load(reinterpret_cast<char*>(sm.v[buf]), vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
+      Dma::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff[0], k_ld, tid, a.seq_k - n0);
+      Dma::load(reinterpret_cast<char*>(sm.v[buf]), vbh + n0 * v_ld, voff[0], v_ld, tid, a.seq_k - n0);
     }
     if (masked && tid < BK) {
       const int nn = n0 + tid;

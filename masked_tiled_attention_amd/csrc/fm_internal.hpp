@@ -15,7 +15,7 @@ constexpr int kFwdBlockK = 64;
 constexpr int kBwdBlockQ = 64;    // dK/dV kernel: query rows per inner tile
 constexpr int kBwdBlockK = 128;   // dK/dV kernel: keys per workgroup
 constexpr int kDqBlockQ = 128;    // dQ kernel: query rows per workgroup
-constexpr int kDqBlockK = 64;     // dQ kernel: keys per inner tile
+constexpr int kDqBlockK = 32;     // dQ kernel: keys per inner tile
 
 // Mask vectors as seen by the kernels. A missing pair is flagged and its
 // pointers are not dereferenced.

@@ -153,42 +153,46 @@ __device__ __forceinline__ void store_tile_rows(char* lds, const u32x4 (&r)[CHUN
 // through registers. One wave instruction fills one contiguous KiB of LDS
 // (lane l writes bytes 16 l .. 16 l + 15 of it), so lane l fetches the logical
 // chunk that the swizzle stores at that position. KiB block b = i * NW + w is
-// written by wavefront w's i-th instruction.
+// written by wavefront w's i-th instruction; its rows are b * RPB + 16 l / 2D.
+// Successive instructions of a wavefront step NW * RPB rows (a multiple of 16),
+// which leaves swz() unchanged, so a lane needs one offset for all of them and
+// the step goes into the uniform base address.
 template <int D, int ROWS, int NT>
 struct DmaTile {
   static constexpr int NW = NT / 64;
   static constexpr int BLOCKS = ROWS * D * 2 / 1024;
   static constexpr int PER = BLOCKS / NW;   // instructions per wavefront
   static constexpr int RPB = 512 / D;       // rows per KiB block
+  static constexpr int STEP = NW * RPB;     // rows between a wavefront's instructions
   static_assert(PER * NW == BLOCKS, "tile must split evenly over the wavefronts");
+  static_assert(STEP % 16 == 0, "the row step must keep the swizzle");
 
-  // Byte offset (from the tile's first row) of the chunk lane `lane` of
-  // wavefront `w` fetches in instruction i; row clamped to nvalid - 1.
-  __device__ static __forceinline__ uint32_t offset(int i, int w, int lane, int64_t ld, int nvalid) {
-    const int row = (i * NW + w) * RPB + (16 * lane) / (2 * D);
-    const int pc = ((16 * lane) % (2 * D)) / 16;
-    const int ch = pc ^ swz<D>(row);
-    return (uint32_t)(min(row, nvalid - 1) * ld + ch * 16);
+  // This lane's first row and its logical chunk in every instruction.
+  __device__ static __forceinline__ int row0(int tid) { return (tid >> 6) * RPB + (16 * (tid & 63)) / (2 * D); }
+  __device__ static __forceinline__ int chunk(int tid) {
+    return (((16 * (tid & 63)) % (2 * D)) / 16) ^ swz<D>(row0(tid));
+  }
+  // Byte offset, from the tile's first row, of what this lane fetches in a
+  // wavefront's first instruction.
+  __device__ static __forceinline__ uint32_t offset(int64_t ld, int tid) {
+    return (uint32_t)(row0(tid) * ld + chunk(tid) * 16);
   }
 
-  __device__ static __forceinline__ void offsets(uint32_t (&off)[PER], int64_t ld, int tid) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) off[i] = offset(i, tid >> 6, tid & 63, ld, ROWS);
-  }
-
-  // Issue the tile's loads; `lds` is the tile's LDS base. Rows at or past
-  // `nvalid` re-read row nvalid - 1. The caller awaits completion with
-  // wait_vmem() before the barrier that publishes the tile.
-  __device__ static __forceinline__ void load(char* lds, const char* tile, const uint32_t (&off)[PER], int64_t ld,
-                                              int tid, int nvalid) {
+  // Issue the tile's loads; `lds` is the tile's LDS base, `off` = offset().
+  // Rows at or past `nvalid` re-read row nvalid - 1. The caller awaits
+  // completion with wait_vmem() before the barrier that publishes the tile.
+  __device__ static __forceinline__ void load(char* lds, const char* tile, uint32_t off, int64_t ld, int tid,
+                                              int nvalid) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t base = lds_address(lds) + (uint32_t)w * 1024u;
     if (nvalid >= ROWS) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) dma16(tile, off[i], base + (uint32_t)(i * NW) * 1024u);
+      for (int i = 0; i < PER; ++i) dma16(tile + i * STEP * ld, off, base + (uint32_t)(i * NW) * 1024u);
     } else {
+      const int r0 = row0(tid), ch = chunk(tid);
 #pragma unroll
-      for (int i = 0; i < PER; ++i) dma16(tile, offset(i, w, tid & 63, ld, nvalid), base + (uint32_t)(i * NW) * 1024u);
+      for (int i = 0; i < PER; ++i)
+        dma16(tile, (uint32_t)(min(r0 + i * STEP, nvalid - 1) * ld + ch * 16), base + (uint32_t)(i * NW) * 1024u);
     }
   }
 

@@ -112,15 +112,15 @@ void fwd_kernel(FwdArgs a) {
   const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
   const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * ES;
   using Dma = DmaTile<D, BK, NT>;
-  constexpr int NOFF = F32 ? KR : Dma::PER;
+  constexpr int NOFF = F32 ? KR : 1;
   constexpr int NREG = F32 ? KR : 1;
   uint32_t koff[NOFF], voff[NOFF];
   if constexpr (F32) {
     tile_offsets<D, F32, KR, NT>(koff, k_ld, tid);
     tile_offsets<D, F32, KR, NT>(voff, v_ld, tid);
   } else {
-    Dma::offsets(koff, k_ld, tid);
-    Dma::offsets(voff, v_ld, tid);
+    koff[0] = Dma::offset(k_ld, tid);
+    voff[0] = Dma::offset(v_ld, tid);
   }
   u32x4 rk[NREG], rv[NREG];
   int32_t rb[4] = {INT_MIN, INT_MAX, 0, 0};
@@ -133,8 +133,8 @@ void fwd_kernel(FwdArgs a) {
       load_tile_rows<D, F32, KR, NT>(rk, kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
       load_tile_rows<D, F32, KR, NT>(rv, vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
     } else {
-      Dma::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
-      Dma::load(reinterpret_cast<char*>(sm.v[buf]), vbh + n0 * v_ld, voff, v_ld, tid, a.seq_k - n0);
+      Dma::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff[0], k_ld, tid, a.seq_k - n0);
+      Dma::load(reinterpret_cast<char*>(sm.v[buf]), vbh + n0 * v_ld, voff[0], v_ld, tid, a.seq_k - n0);
     }
     if (masked && tid < BK) {
       const int n = n0 + tid;
