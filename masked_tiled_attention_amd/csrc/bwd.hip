@@ -23,6 +23,7 @@
 //             that no workgroup ever adds into another one's output: no
 //             atomics, deterministic results.
 #include <climits>
+#include <type_traits>
 #include <cmath>
 
 #include "fm_device.hpp"
@@ -145,6 +146,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     b_uts = a.mask.has_upper ? a.mask.uts[mbase + n] : 0;
     b_ute = a.mask.has_upper ? a.mask.ute[mbase + n] : 0;
   }
+  // Interval widths (0 for empty intervals): row mm is masked by [s, e) iff
+  // (uint)(mm - s) < width, exact for every int32 s, e.
+  const uint32_t b_lw = b_lte > b_lts ? (uint32_t)b_lte - (uint32_t)b_lts : 0u;
+  const uint32_t b_uw = b_ute > b_uts ? (uint32_t)b_ute - (uint32_t)b_uts : 0u;
   const bool ragged_k = (a.seq_k % BK) != 0 && kt == a.tk - 1;
 
   f32x16 dvacc[CB], dkacc[CB];
@@ -210,86 +215,134 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
 
   int it_global = 0;
   for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
-    const int n_list = compact_classes<LIST_CAP, NT>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.scan, tid);
+    int n_full;
+    const int n_list = compact_classes_split<LIST_CAP, NT>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.scan,
+                                                           tid, ragged_k, &n_full);
     if (n_list == 0) continue;
 
-    uint32_t ent = sm.list[0];
-    load_q((int)(ent & ~kPartialBit), it_global & 1);
+    load_q((int)(sm.list[0] & ~kPartialBit), it_global & 1);
 
-    for (int it = 0; it < n_list; ++it, ++it_global) {
+    // FULL tiles first, then PARTIAL ones, each with its own straight-line
+    // body (one branch-free basic block per query tile).
+    auto iteration = [&](auto masked_c, int it) {
+      constexpr bool MASKED = decltype(masked_c)::value;
       const int buf = it_global & 1;
-      const int qt = (int)(ent & ~kPartialBit);
-      const bool masked_tile = (ent & kPartialBit) || ragged_k;
+      const int qt = (int)(sm.list[it] & ~kPartialBit);
       const int m0 = qt * BQ;
       store_q(buf);
       wait_vmem();
       __syncthreads();   // tile `buf` complete and visible; the other buffer is free
-      if (it + 1 < n_list) {   // the next query tile's loads overlap this tile's math
-        ent = sm.list[it + 1];
-        load_q((int)(ent & ~kPartialBit), buf ^ 1);
-      }
+      if (it + 1 < n_list) load_q((int)(sm.list[it + 1] & ~kPartialBit), buf ^ 1);   // overlaps the math below
       const char* qb = reinterpret_cast<const char*>(sm.q[buf]);
       const char* db = reinterpret_cast<const char*>(sm.dout[buf]);
 
-      // ---- S = Q K^T and dP = dO V^T (lane = key, registers = query rows) ----
-      f32x16 sacc[2], dpacc[2];
+      // One 64-row query tile as two 32-row halves (A: rows 0-31, B: 32-63),
+      // ordered so that each half's elementwise work runs beside the other
+      // half's matrix products (the MFMA unit works while the same wavefront
+      // issues independent VALU instructions):
+      //   S,dP(A) | S,dP(B) + P,dS(A) | dV,dK(A) + P,dS(B) | dV,dK(B)
+      {
+        f32x16 sacc[2], dpacc[2];
+        u32x4 pp[2][2], dsp[2][2];
+        // S = Q K^T and dP = dO V^T (lane = key, registers = query rows)
+        auto sdp = [&](int mb) {
+          sacc[mb] = f32x16{};
+          dpacc[mb] = f32x16{};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        sacc[mb] = f32x16{};
-        dpacc[mb] = f32x16{};
+          for (int s = 0; s < KSTEPS; ++s) {
+            const int off = rm_byte<D>(32 * mb + lr, 16 * s + 8 * g);
+            sacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(qb + off), kf[s], sacc[mb]);
+            dpacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(db + off), vf[s], dpacc[mb]);
+          }
+        };
+        // P = exp2(S * scale * log2(e) - LSE * log2(e)), dS = P (dP - D),
+        // both rounded to bf16 MFMA operands
+        auto softmax = [&](int mb) {
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const int off = rm_byte<D>(32 * mb + lr, 16 * s + 8 * g);
-          sacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(qb + off), kf[s], sacc[mb]);
-          dpacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(db + off), vf[s], dpacc[mb]);
-        }
-      }
-      sched_lds_mfma<4 * KSTEPS, 1, 4>();
-
-      // ---- P and dS ----
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int ml = 32 * mb + 8 * q4 + 4 * g;
+            const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ml = 32 * mb + 8 * q4 + 4 * g;
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
-          const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * q4 + r;
-            float p = fast_exp2(fmaf(sacc[mb][i], C, -l2[r]));
-            if (masked_tile) {
-              const int mm = m0 + ml + r;
-              const bool mk = ((b_lts <= mm) & (mm < b_lte)) | ((b_uts <= mm) & (mm < b_ute));
-              p = mk ? 0.f : p;
+            for (int r = 0; r < 4; ++r) {
+              const int i = 4 * q4 + r;
+              float p = fast_exp2(fmaf(sacc[mb][i], C, -l2[r]));
+              if constexpr (MASKED) {
+                const int mm = m0 + ml + r;
+                const bool mk = ((uint32_t)(mm - b_lts) < b_lw) | ((uint32_t)(mm - b_uts) < b_uw);
+                p = mk ? 0.f : p;
+              }
+              sacc[mb][i] = p;
+              dpacc[mb][i] = p * (dpacc[mb][i] - dd[r]);
             }
-            sacc[mb][i] = p;
-            dpacc[mb][i] = p * (dpacc[mb][i] - dd[r]);
           }
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              pp[mb][t][j] = pack_bf16(sacc[mb][8 * t + 2 * j], sacc[mb][8 * t + 2 * j + 1]);
+              dsp[mb][t][j] = pack_bf16(dpacc[mb][8 * t + 2 * j], dpacc[mb][8 * t + 2 * j + 1]);
+            }
+        };
+        // dV^T += dO^T P, dK^T += Q^T dS (contraction over the half's rows)
+        auto dvdk = [&](int mb) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int r0 = 32 * mb + 16 * t + 4 * g;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+              dvacc[cb] = mfma32(tr_operand<D>(db, l, 32 * cb, r0, r0 + 8), pp[mb][t], dvacc[cb]);
+              dkacc[cb] = mfma32(tr_operand<D>(qb, l, 32 * cb, r0, r0 + 8), dsp[mb][t], dkacc[cb]);
+            }
+          }
+        };
+        // Four scheduling regions; in each, operand reads run ahead of their
+        // MFMAs and the other half's elementwise work sits between MFMAs.
+        sdp(0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int j = 0; j < 2 * KSTEPS - 4; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-      }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
 
-      // ---- dV^T += dO^T P,  dK^T += Q^T dS (contraction over query rows) ----
+        sdp(1);
+        softmax(0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 pp, dsp;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pp[j] = pack_bf16(sacc[mb][8 * t + 2 * j], sacc[mb][8 * t + 2 * j + 1]);
-            dsp[j] = pack_bf16(dpacc[mb][8 * t + 2 * j], dpacc[mb][8 * t + 2 * j + 1]);
-          }
-          const int r0 = 32 * mb + 16 * t + 4 * g;
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            dvacc[cb] = mfma32(tr_operand<D>(db, l, 32 * cb, r0, r0 + 8), pp, dvacc[cb]);
-            dkacc[cb] = mfma32(tr_operand<D>(qb, l, 32 * cb, r0, r0 + 8), dsp, dkacc[cb]);
-          }
+        for (int j = 0; j < 2 * KSTEPS; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 9 : 6, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+
+        dvdk(0);
+        softmax(1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int j = 0; j < 4 * CB; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 9 : 6, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        dvdk(1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int j = 0; j < 4 * CB - 3; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
       }
-      sched_lds_mfma<2 * 2 * 2 * CB, 2, 3>();
-    }
+    };
+    int it = 0;
+    for (; it < n_full; ++it, ++it_global) iteration(std::false_type{}, it);
+    for (; it < n_list; ++it, ++it_global) iteration(std::true_type{}, it);
   }
 
   // ---- epilogue: dK = scale * dK^T, dV = dV^T, transposed back on store ----

@@ -104,6 +104,55 @@ __device__ __forceinline__ int compact_classes(const uint8_t* row, int first, in
   return n_list;
 }
 
+// As compact_classes(), but the list holds the FULL entries first and the
+// PARTIAL ones after them (each group ascending); *n_full receives the number
+// of FULL entries. With all_partial, every entry counts as PARTIAL.
+template <int CAP, int NT>
+__device__ __forceinline__ int compact_classes_split(const uint8_t* row, int first, int count, uint32_t* sm_list,
+                                                     int32_t* sm_scan, int tid, bool all_partial, int* n_full) {
+  constexpr int PER = CAP / NT;
+  constexpr int NWAVE = NT / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  uint8_t cls[PER];
+  int cf = 0, cp = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid * PER + e;
+    uint8_t c = idx < count ? row[first + idx] : (uint8_t)FM_TILE_SKIP;
+    if (all_partial && c == FM_TILE_FULL) c = FM_TILE_PARTIAL;
+    cls[e] = c;
+    cf += c == FM_TILE_FULL;
+    cp += c == FM_TILE_PARTIAL;
+  }
+  // both counts in one scan: FULL in the low 16 bits, PARTIAL in the high
+  int incl = cf | (cp << 16);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) sm_scan[wave] = incl;
+  __syncthreads();
+  int pos = incl - (cf | (cp << 16)), tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < NWAVE; ++ww) {
+    if (ww < wave) pos += sm_scan[ww];
+    tot += sm_scan[ww];
+  }
+  const int nf = tot & 0xffff, np = tot >> 16;
+  int pf = pos & 0xffff, pp = nf + (pos >> 16);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const uint32_t id = (uint32_t)(first + tid * PER + e);
+    if (cls[e] == FM_TILE_FULL) sm_list[pf++] = id;
+    else if (cls[e] == FM_TILE_PARTIAL) sm_list[pp++] = id | kPartialBit;
+  }
+  __syncthreads();
+  *n_full = nf;
+  return nf + np;
+}
+
 // Global -> registers for a row-major [rows][D] tile slice: 16-byte chunk
 // ci = tid + i * NT holds row ci / (D/8), elements 8 * (ci % (D/8)) .. +8.
 // tile_offsets() gives each chunk's byte offset from the tile's first row
