@@ -129,11 +129,14 @@ fm_status check_ptr(const void* ptr, const char* name) {
 
 // Workspace: per tiling one summary [Bm][Hm][Tk][8] int32 and one class map
 // [Bm][Hm][Tq][Tk] uint8 (forward: the forward tiles; backward: the dK/dV
-// tiles, transposed, and the dQ tiles), plus D [B][H][Sq] float32 for the
-// backward. 256-byte aligned sections.
+// tiles, transposed, and the dQ tiles), plus for the backward the per-row
+// LSE * log2(e) and D [B][H][Sp] float32 (Sp = Sq rounded up to 128, the
+// padding rows neutral). 256-byte aligned sections.
 struct Layout {
-  size_t summary = 0, map = 0, summary_q = 0, map_q = 0, drow = 0, total = 0;
+  size_t summary = 0, map = 0, summary_q = 0, map_q = 0, lse2 = 0, drow = 0, total = 0;
 };
+
+int64_t padded_rows(int64_t sq) { return ceil_div(sq, 128) * 128; }
 
 Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
   Layout L;
@@ -149,8 +152,11 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
   if (bwd) {
     add_tiling(fm::kBwdBlockQ, fm::kBwdBlockK, &L.summary, &L.map);
     add_tiling(fm::kDqBlockQ, fm::kDqBlockK, &L.summary_q, &L.map_q);
+    const size_t rows = (size_t)p->batch * p->heads * padded_rows(p->seqlen_q) * 4;
+    L.lse2 = off;
+    off = align256(off + rows);
     L.drow = off;
-    off = align256(off + (size_t)p->batch * p->heads * p->seqlen_q * 4);
+    off = align256(off + rows);
   } else {
     add_tiling(fm::kFwdBlockQ, fm::kFwdBlockK, &L.summary, &L.map);
   }
@@ -317,7 +323,9 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
+  a.lse2 = reinterpret_cast<float*>(w + L.lse2);
   a.drow = reinterpret_cast<float*>(w + L.drow);
+  a.seq_pad = (int32_t)padded_rows(p->seqlen_q);
   a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
   a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
   a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];

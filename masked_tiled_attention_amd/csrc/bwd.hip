@@ -38,19 +38,24 @@ constexpr int NT = NW * 64;      // threads per workgroup
 constexpr int LIST_CAP = 1024;   // class bytes compacted per pass (4 per thread)
 
 // ------------------------------------------------------------------ pre-pass
+// Per query row (padded to Sp): D = rowsum(dO * O) and LSE * log2(e), the
+// latter +inf where the row sees no key (LSE = -inf) so that P = 0 there; rows
+// past Sq get +inf and 0, so tiles may read whole padded row blocks.
 template <int D, bool F32>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int TPR = D / 8;            // threads per row
   constexpr int RPB = 256 / TPR;        // rows per block
   const int sub = threadIdx.x % TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;   // (b, m, h) linear
-  const int64_t nrows = (int64_t)a.batch * a.seq_q * a.heads;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;   // (b, m, h) linear, m < Sp
+  const int64_t nrows = (int64_t)a.batch * a.seq_pad * a.heads;
   float part = 0.f;
   int b = 0, m = 0, h = 0;
   if (row < nrows) {
     h = (int)(row % a.heads);
-    m = (int)((row / a.heads) % a.seq_q);
-    b = (int)(row / ((int64_t)a.heads * a.seq_q));
+    m = (int)((row / a.heads) % a.seq_pad);
+    b = (int)(row / ((int64_t)a.heads * a.seq_pad));
+  }
+  if (row < nrows && m < a.seq_q) {
     const int64_t off = (int64_t)b * a.o_sb + (int64_t)m * a.o_ss + (int64_t)h * a.o_sh + 8 * sub;
     float x[8], y[8];
     if constexpr (F32) {
@@ -77,7 +82,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int o = TPR / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-  if (row < nrows && sub == 0) a.drow[((int64_t)b * a.heads + h) * a.seq_q + m] = part;
+  if (row < nrows && sub == 0) {
+    const int64_t r = ((int64_t)b * a.heads + h) * a.seq_pad + m;
+    float l2 = INFINITY;
+    if (m < a.seq_q) {
+      const float lse = a.lse[((int64_t)b * a.heads + h) * a.seq_q + m];
+      l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+    }
+    a.lse2[r] = l2;
+    a.drow[r] = part;
+  }
 }
 
 // ------------------------------------------------------------------ dK / dV
@@ -85,12 +99,14 @@ namespace kv {
 constexpr int BQ = kBwdBlockQ;   // 64 query rows per inner tile
 constexpr int BK = kBwdBlockK;   // 128 keys per workgroup (32 per wavefront)
 
+constexpr int NBUF = 3;          // query tiles in flight: the current one and two prefetched
+
 template <int D>
 struct alignas(16) Smem {
-  uint16_t q[2][BQ * D];      // double-buffered query tile
-  uint16_t dout[2][BQ * D];   // double-buffered dO tile
-  float lse2[2][BQ];          // LSE * log2(e); +inf for rows that see nothing / past the end
-  float dd[2][BQ];            // D = rowsum(dO * O)
+  uint16_t q[NBUF][BQ * D];      // query tiles, row-major, swizzled
+  uint16_t dout[NBUF][BQ * D];   // dO tiles
+  float lse2[NBUF][BQ];          // LSE * log2(e); +inf for rows that see nothing / past the end
+  float dd[NBUF][BQ];            // D = rowsum(dO * O)
   uint32_t list[LIST_CAP];
   int32_t scan[NW];
 };
@@ -159,19 +175,19 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     dkacc[cb] = f32x16{};
   }
   const float C = a.scale_log2;
-  const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_q;
+  const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_pad;
 
-  // ---- query tile staging (Q, dO; LSE and D through registers) ----
-  // bf16: Q and dO straight from global memory into LDS; float32: through
-  // registers, rounded to bf16 on the way. Rows past the end re-read the last
-  // row; their LSE is +inf, so P = dS = 0.
+  // ---- query tile staging ----
+  // Q and dO (bf16) and the rows' LSE*log2(e) and D go straight from global
+  // memory into LDS, two tiles ahead of the math; float32 Q and dO pass
+  // through registers (rounded to bf16) when their tile is staged. Rows past
+  // the end re-read the last row; their LSE*log2(e) is +inf, so P = dS = 0.
   constexpr int ES = F32 ? 4 : 2;
   const int64_t q_ld = a.q_ss * ES, o_ld = a.o_ss * ES;
   const char* qbh = reinterpret_cast<const char*>(a.q) + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ES;
   const char* dbh = reinterpret_cast<const char*>(a.dout) + ((int64_t)b * a.o_sb + (int64_t)h * a.o_sh) * ES;
   using Dma = DmaTile<D, BQ, NT>;
   constexpr int NOFF = F32 ? QR : 1;
-  constexpr int NREG = F32 ? QR : 1;
   uint32_t qoff[NOFF], doff[NOFF];
   if constexpr (F32) {
     tile_offsets<D, F32, QR, NT>(qoff, q_ld, tid);
@@ -180,37 +196,24 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     qoff[0] = Dma::offset(q_ld, tid);
     doff[0] = Dma::offset(o_ld, tid);
   }
-  u32x4 rq[NREG], rd[NREG];
-  float rl2 = INFINITY, rdd = 0.f;
-  auto load_q = [&](int qt, int buf) {
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  // Direct loads per tile and wavefront: Q and dO (bf16), plus one for the
+  // LSE row block (wavefront 0) or the D row block (wavefront 1).
+  constexpr int GROUP = F32 ? 0 : 2 * Dma::PER;
+  auto stage_q = [&](int qt, int buf) {
     const int m0 = qt * BQ;
     if constexpr (F32) {
+      u32x4 rq[QR], rd[QR];
       load_tile_rows<D, F32, QR, NT>(rq, qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
       load_tile_rows<D, F32, QR, NT>(rd, dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
+      store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.q[buf]), rq, tid);
+      store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.dout[buf]), rd, tid);
     } else {
       Dma::load(reinterpret_cast<char*>(sm.q[buf]), qbh + m0 * q_ld, qoff[0], q_ld, tid, a.seq_q - m0);
       Dma::load(reinterpret_cast<char*>(sm.dout[buf]), dbh + m0 * o_ld, doff[0], o_ld, tid, a.seq_q - m0);
     }
-    if (tid < BQ) {
-      const int mm = m0 + tid;
-      rl2 = INFINITY;
-      rdd = 0.f;
-      if (mm < a.seq_q) {
-        const float lse = a.lse[lrow + mm];
-        rl2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-        rdd = a.drow[lrow + mm];
-      }
-    }
-  };
-  auto store_q = [&](int buf) {
-    if constexpr (F32) {
-      store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.q[buf]), rq, tid);
-      store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.dout[buf]), rd, tid);
-    }
-    if (tid < BQ) {
-      sm.lse2[buf][tid] = rl2;
-      sm.dd[buf][tid] = rdd;
-    }
+    if (wu == 0) dma4(a.lse2 + lrow + m0, 4u * (uint32_t)l, lds_address(sm.lse2[buf]));
+    else if (wu == 1) dma4(a.drow + lrow + m0, 4u * (uint32_t)l, lds_address(sm.dd[buf]));
   };
 
   int it_global = 0;
@@ -220,19 +223,25 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
                                                            tid, ragged_k, &n_full);
     if (n_list == 0) continue;
 
-    load_q((int)(sm.list[0] & ~kPartialBit), it_global & 1);
+    stage_q((int)(sm.list[0] & ~kPartialBit), it_global % NBUF);
+    if (n_list > 1) stage_q((int)(sm.list[1] & ~kPartialBit), (it_global + 1) % NBUF);
 
     // FULL tiles first, then PARTIAL ones, each with its own straight-line
     // body (one branch-free basic block per query tile).
     auto iteration = [&](auto masked_c, int it) {
       constexpr bool MASKED = decltype(masked_c)::value;
-      const int buf = it_global & 1;
+      const int buf = it_global % NBUF;
       const int qt = (int)(sm.list[it] & ~kPartialBit);
       const int m0 = qt * BQ;
-      store_q(buf);
-      wait_vmem();
-      __syncthreads();   // tile `buf` complete and visible; the other buffer is free
-      if (it + 1 < n_list) load_q((int)(sm.list[it + 1] & ~kPartialBit), buf ^ 1);   // overlaps the math below
+      // this tile's loads done (the next tile's may still be in flight)
+      if (it + 1 < n_list) {
+        if (wu < 2) wait_vmem_le<GROUP + 1>();
+        else wait_vmem_le<GROUP>();
+      } else {
+        wait_vmem();
+      }
+      __syncthreads();   // tile `buf` visible to all; the buffer read last iteration is free
+      if (it + 2 < n_list) stage_q((int)(sm.list[it + 2] & ~kPartialBit), (it_global + 2) % NBUF);
       const char* qb = reinterpret_cast<const char*>(sm.q[buf]);
       const char* db = reinterpret_cast<const char*>(sm.dout[buf]);
 
@@ -429,12 +438,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       qf[s] = load8_as_bf16<F32>(a.q, qoff + 16 * s);
       df[s] = load8_as_bf16<F32>(a.dout, doff + 16 * s);
     }
-    if (row_ok) {
-      const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_q + m;
-      const float lse = a.lse[lrow];
-      l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-      dd = a.drow[lrow];
-    }
+    const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_pad + m;   // m < Sp
+    l2 = a.lse2[lrow];
+    dd = a.drow[lrow];
   }
 
   f32x16 dqacc[CB];
@@ -604,7 +610,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
 template <int D, bool F32>
 hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
-  const int64_t nrows = (int64_t)a.batch * a.seq_q * a.heads;
+  const int64_t nrows = (int64_t)a.batch * a.seq_pad * a.heads;
   const int rpb = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D, F32>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -65,7 +65,9 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* drow;             // [B][H][Sq] float32: rowsum(dO * O)
+  float* lse2;             // [B][H][Sp] float32: LSE * log2(e); +inf for rows that see no key or lie past Sq
+  float* drow;             // [B][H][Sp] float32: D = rowsum(dO * O); 0 past Sq
+  int32_t seq_pad;         // Sp: Sq rounded up to a multiple of 128
   int64_t q_sb, q_ss, q_sh;
   int64_t k_sb, k_ss, k_sh;
   int64_t v_sb, v_ss, v_sh;

@@ -270,8 +270,33 @@ struct DmaTile {
 #pragma clang diagnostic pop
 };
 
-// Wait until this wavefront's outstanding global loads (including the direct
-// loads into LDS above) have completed: s_waitcnt vmcnt(0).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// One global_load_lds_dword: lane l copies 4 bytes from base + voff(l) to LDS
+// byte lds_dst + 4 l (same reasoning as DmaTile::dma16).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds_dst) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2"
+      :
+      : "s"(lds_dst), "v"(voff), "s"(base)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Wait until at most N of this wavefront's global loads (including direct
+// loads into LDS) are outstanding: s_waitcnt vmcnt(N). Loads complete in
+// issue order, so this awaits everything but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
 }  // namespace fm
