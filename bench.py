@@ -70,7 +70,7 @@ def measured_traffic(kernel: str, workload: str):
 class Runner:
     """Device-resident inputs, outputs and workspaces of one workload."""
 
-    def __init__(self, fm, w, torch):
+    def __init__(self, fm, w, torch, store_ds=True):
         self.fm, self.w, self.t = fm, w, torch
         dev = "cuda"
         self.q, self.k, self.v = (x.to(dev) for x in (w.q, w.k, w.v))
@@ -90,8 +90,12 @@ class Runner:
         ws_f = fm.fm_workspace_size(self.q, self.k, self.v, self.mask, False, w.scale)
         self.ws_f = torch.empty(ws_f, dtype=torch.uint8, device=dev)
         if w.backward:
-            ws_b = fm.fm_workspace_size(self.q, self.k, self.v, self.mask, True, w.scale)
+            # with the stored-dS workspace (sized from the classified mask) dQ is
+            # formed from the dS tiles the dK/dV kernel writes; else recomputed
+            ws_b = (fm.fm_bwd_workspace_size_ds(self.q, self.k, self.v, self.mask, w.scale) if store_ds
+                    else fm.fm_workspace_size(self.q, self.k, self.v, self.mask, True, w.scale))
             self.ws_b = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+            self.ws_b_bytes = ws_b
             self.dq, self.dk, self.dv = (torch.empty_like(x) for x in (self.q, self.k, self.v))
         self.nnz = nnz_of(self.vectors, w.seq_q, w.batch, w.heads)
 
@@ -171,6 +175,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-store-ds", action="store_true",
+                    help="minimum backward workspace: dQ recomputes S and dP instead of reading stored dS")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -204,7 +210,8 @@ def main():
 
     log(f"[bench] building {args.workload} seed {args.seed}")
     w = SC.build(args.workload, args.seed)
-    r = Runner(fm, w, torch)
+    store_ds = not args.no_store_ds
+    r = Runner(fm, w, torch, store_ds)
     ms, stages = time_steps(r, args.steps, args.warmup, torch)
     f_fwd, f_bwd = r.flops()
     per = lambda s: stages[s][0] / max(1, args.steps)
@@ -212,15 +219,17 @@ def main():
     # per backward kernel tiling); its small cost is split in that ratio
     cls_ms = per("classify_summary") + per("classify_map")
     fwd_ms = per("fwd") + (cls_ms / 3 if w.backward else cls_ms)
-    bwd_ms = per("bwd_pre") + per("bwd") + per("bwd_dq") + 2 * cls_ms / 3 if w.backward else 0.0
+    bwd_ms = (per("bwd_pre") + per("bwd_plan") + per("bwd") + per("bwd_dq") + per("bwd_dq_ds") + 2 * cls_ms / 3
+              if w.backward else 0.0)
     total_tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
     log(f"[bench] {w.name}: {ms:.3f} ms/step, {total_tflops:.1f} TFLOP/s")
 
     # dominant kernel: the one with the largest time per step. Executed matrix
     # flops per open pair: forward 4d (QK^T, PV), dK/dV kernel 8d (QK^T, dO V^T,
-    # P^T dO, dS^T Q), dQ kernel 6d (QK^T, dO V^T, dS K).
+    # P^T dO, dS^T Q), dQ kernel 6d (QK^T, dO V^T, dS K) or, from stored dS, 2d.
     d = w.head_dim
-    kernel_flops = {"fwd": 4 * d * r.nnz, "bwd": 8 * d * r.nnz, "bwd_dq": 6 * d * r.nnz}
+    kernel_flops = {"fwd": 4 * d * r.nnz, "bwd": 8 * d * r.nnz, "bwd_dq": 6 * d * r.nnz,
+                    "bwd_dq_ds": 2 * d * r.nnz}
     kern = max((k for k in kernel_flops if stages[k][1]), key=lambda s: stages[s][0])
     kflops = kernel_flops[kern]
     kms = stages[kern][0] / max(1, stages[kern][1])
@@ -241,6 +250,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_q": w.seq_q,
                    "seq_k": w.seq_k, "head_dim": w.head_dim, "seed": args.seed,
                    "passes": "fwd+bwd" if w.backward else "fwd", "nnz": r.nnz,
+                   "dq_from": ("stored dS" if store_ds else "recompute") if w.backward else None,
                    "density": round(r.nnz / (w.batch * w.heads * w.seq_q * w.seq_k), 5)},
         "pct_of_bf16_peak": round(100 * total_tflops / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None},
@@ -264,7 +274,7 @@ def main():
                 continue
             log(f"[bench] sweep {name}")
             wx = SC.build(name, args.seed)
-            rx = Runner(fm, wx, torch)
+            rx = Runner(fm, wx, torch, store_ds)
             msx, st = time_steps(rx, 5, 2, torch)
             a, b = rx.flops()
             pf = lambda s: st[s][0] / 5
@@ -273,8 +283,13 @@ def main():
                     "fwd_kernel_tflops": round(a / (pf("fwd") * 1e-3) / 1e12, 2)}
             if wx.backward:
                 item["dkdv_kernel_tflops"] = round(8 * wx.head_dim * rx.nnz / (pf("bwd") * 1e-3) / 1e12, 2)
-                item["dq_kernel_tflops"] = round(6 * wx.head_dim * rx.nnz / (pf("bwd_dq") * 1e-3) / 1e12, 2)
-                item["bwd_tflops"] = round(b / ((pf("bwd") + pf("bwd_dq") + pf("bwd_pre")) * 1e-3) / 1e12, 2)
+                if st["bwd_dq_ds"][1] and pf("bwd_dq_ds") > pf("bwd_dq"):
+                    item["dq_ds_kernel_tflops"] = round(2 * wx.head_dim * rx.nnz / (pf("bwd_dq_ds") * 1e-3) / 1e12, 2)
+                    item["dq_ds_gbs"] = round(2 * rx.nnz / (pf("bwd_dq_ds") * 1e-3) / 1e9, 1)
+                else:
+                    item["dq_kernel_tflops"] = round(6 * wx.head_dim * rx.nnz / (pf("bwd_dq") * 1e-3) / 1e12, 2)
+                bwd_x = sum(pf(s_) for s_ in ("bwd_pre", "bwd_plan", "bwd", "bwd_dq", "bwd_dq_ds"))
+                item["bwd_tflops"] = round(b / (bwd_x * 1e-3) / 1e12, 2)
             if wx.global_vectors is not None:
                 item["localize_ms"] = round(pf("localize"), 4)
             sweep.append(item)

@@ -116,10 +116,25 @@ typedef struct {
 void fm_kernel_tile(int32_t head_dim, int32_t bwd, int32_t* block_q, int32_t* block_k);
 
 /* Bytes of device workspace fm_attn_fwd (with_bwd = 0) or fm_attn_bwd
- * (with_bwd = 1) needs: tile summaries and class maps, plus for the backward
- * the row terms D = rowsum(dO * O). */
+ * (with_bwd = 1) needs at least: tile summaries and class maps, plus for the
+ * backward the per-row terms LSE * log2(e) and D = rowsum(dO * O) and the
+ * stored-dS plan counters. With this much, fm_attn_bwd recomputes S and dP a
+ * second time for dQ. */
 fm_status fm_workspace_size(const fm_problem* problem, const fm_mask* mask,
                             int32_t with_bwd, size_t* bytes);
+
+/* Bytes of workspace with which fm_attn_bwd keeps dS instead of recomputing
+ * it: the dK/dV kernel writes the bf16 dS tiles it forms anyway, and dQ is the
+ * product scale * dS K over the stored tiles. That is fm_workspace_size(.., 1)
+ * plus a slot index per tile of the dK/dV tiling and 2 bytes per (query row,
+ * key) pair of every non-SKIP tile, for every (b, h) (rows and keys padded to
+ * the tile). The count depends on the mask contents, so the call classifies
+ * the mask on `stream` using `workspace` (device, at least
+ * fm_workspace_size(.., 1) bytes, 256-byte aligned; contents overwritten) and
+ * waits for the stream. */
+fm_status fm_bwd_workspace_size_ds(const fm_problem* problem, const fm_mask* mask,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                   size_t* bytes);
 
 /* Tile classification pre-pass (reading adopted; the pages do not describe
  * one). For key tile kt (columns [kt*block_k, min((kt+1)*block_k, Sk)))
@@ -154,8 +169,11 @@ fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, c
  * dout (gradient of o), all device. Outputs dq, dk, dv (device, problem
  * dtype, shapes of q, k, v). workspace: device, at least
  * fm_workspace_size(.., 1) bytes, 256-byte aligned. dK/dV come from a
- * key-stationary kernel and dQ from a query-stationary one; both recompute
- * the probabilities from lse, use no atomics and are deterministic. */
+ * key-stationary kernel that recomputes the probabilities from lse. dQ comes
+ * from stored dS tiles (dQ = scale * dS K) when the workspace is at least
+ * fm_bwd_workspace_size_ds bytes, which is decided on the device from the
+ * classified mask, else from a query-stationary kernel that recomputes S and
+ * dP. No atomics; results are deterministic for a given workspace size. */
 fm_status fm_attn_bwd(const fm_problem* problem, const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout, const fm_mask* mask,
                       void* dq, void* dk, void* dv,
@@ -194,7 +212,9 @@ typedef enum {
   FM_STAGE_BWD = 4,         /* dK / dV kernel */
   FM_STAGE_BWD_DQ = 5,      /* dQ kernel */
   FM_STAGE_LOCALIZE = 6,
-  FM_NUM_STAGES = 7
+  FM_STAGE_BWD_PLAN = 7,    /* stored-dS slot plan (count, scan) */
+  FM_STAGE_BWD_DQ_DS = 8,   /* dQ from stored dS */
+  FM_NUM_STAGES = 9
 } fm_stage;
 
 fm_status fm_profile_begin(int32_t max_launches);

@@ -6,5 +6,5 @@ backward, as hand-written HIP kernels behind a C ABI (libfmattn.so,
 include/fm_attn.h). This package is the thin Python binding.
 """
 from ._lib import FmError, load, EXPORTS  # noqa: F401
-from .api import (Mask, fm_attn_bwd, fm_attn_fwd, fm_kernel_tile, fm_mask_localize,  # noqa: F401
-                  fm_profile_begin, fm_profile_end, fm_tile_classify, fm_workspace_size)
+from .api import (Mask, fm_attn_bwd, fm_attn_fwd, fm_bwd_workspace_size_ds, fm_kernel_tile,  # noqa: F401
+                  fm_mask_localize, fm_profile_begin, fm_profile_end, fm_tile_classify, fm_workspace_size)

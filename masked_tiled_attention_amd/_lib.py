@@ -13,15 +13,16 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfmattn.s
 FM_OK, FM_ERR_INVALID_ARGUMENT, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_HIP = range(5)
 FM_BF16, FM_FP32 = 0, 1
 FM_TILE_SKIP, FM_TILE_PARTIAL, FM_TILE_FULL = 0, 1, 2
-STAGES = ("classify_summary", "classify_map", "fwd", "bwd_pre", "bwd", "bwd_dq", "localize")
+STAGES = ("classify_summary", "classify_map", "fwd", "bwd_pre", "bwd", "bwd_dq", "localize",
+          "bwd_plan", "bwd_dq_ds")
 FM_NUM_STAGES = len(STAGES)
 
 STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_INVALID_ARGUMENT", 2: "FM_ERR_UNSUPPORTED",
                 3: "FM_ERR_WORKSPACE", 4: "FM_ERR_HIP"}
 
 # Every symbol the header declares (checked by the CPU test-suite).
-EXPORTS = ("fm_kernel_tile", "fm_workspace_size", "fm_tile_classify", "fm_attn_fwd",
-           "fm_attn_bwd", "fm_mask_localize", "fm_profile_begin", "fm_profile_end",
+EXPORTS = ("fm_kernel_tile", "fm_workspace_size", "fm_bwd_workspace_size_ds", "fm_tile_classify",
+           "fm_attn_fwd", "fm_attn_bwd", "fm_mask_localize", "fm_profile_begin", "fm_profile_end",
            "fm_last_error")
 
 
@@ -64,6 +65,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.fm_kernel_tile.argtypes = [i32, i32, P(i32), P(i32)]
     lib.fm_workspace_size.restype = C.c_int
     lib.fm_workspace_size.argtypes = [P(fm_problem), P(fm_mask), i32, P(sz)]
+    lib.fm_bwd_workspace_size_ds.restype = C.c_int
+    lib.fm_bwd_workspace_size_ds.argtypes = [P(fm_problem), P(fm_mask), vp, sz, vp, P(sz)]
     lib.fm_tile_classify.restype = C.c_int
     lib.fm_tile_classify.argtypes = [P(fm_mask), i32, i32, i32, i32, i32, vp, vp, vp]
     lib.fm_attn_fwd.restype = C.c_int

@@ -119,6 +119,22 @@ def fm_workspace_size(q, k, v, mask: Mask, with_bwd: bool, scale=None) -> int:
     return n.value
 
 
+def fm_bwd_workspace_size_ds(q, k, v, mask: Mask, scale=None, stream=None) -> int:
+    """Workspace bytes with which fm_attn_bwd stores dS and forms dQ from it
+    (the count depends on the mask contents: classifies on the device and
+    synchronizes the stream)."""
+    prob = _problem(q, k, v, q, scale)
+    m = mask._c()
+    lib = L.load()
+    n = C.c_size_t()
+    L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 1, C.byref(n)))
+    tmp = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q.device)
+    out = C.c_size_t()
+    L.check(lib.fm_bwd_workspace_size_ds(C.byref(prob), C.byref(m), tmp.data_ptr(), tmp.numel(),
+                                         _stream(stream), C.byref(out)))
+    return out.value
+
+
 def _workspace(nbytes: int, device, workspace):
     if workspace is not None:
         return workspace

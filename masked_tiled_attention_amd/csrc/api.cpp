@@ -1,7 +1,8 @@
 // C ABI of libfmattn (declared in include/fm_attn.h): argument validation,
 // workspace layout, launch sequencing and per-launch event timing.
 // Nothing here allocates device memory; every launch goes on the caller's
-// stream and no call synchronises the host (fm_profile_end excepted).
+// stream and no call synchronises the host (fm_profile_end and
+// fm_bwd_workspace_size_ds excepted).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -131,9 +132,13 @@ fm_status check_ptr(const void* ptr, const char* name) {
 // [Bm][Hm][Tq][Tk] uint8 (forward: the forward tiles; backward: the dK/dV
 // tiles, transposed, and the dQ tiles), plus for the backward the per-row
 // LSE * log2(e) and D [B][H][Sp] float32 (Sp = Sq rounded up to 128, the
-// padding rows neutral). 256-byte aligned sections.
+// padding rows neutral) and the stored-dS plan counters. total is the
+// minimum. Beyond it, the backward may place the stored-dS slot map
+// [Bm*Hm][Tk][Tq] int32 at `slots` and the dS tiles from `ds` on.
+// 256-byte aligned sections.
 struct Layout {
-  size_t summary = 0, map = 0, summary_q = 0, map_q = 0, lse2 = 0, drow = 0, total = 0;
+  size_t summary = 0, map = 0, summary_q = 0, map_q = 0, lse2 = 0, drow = 0;
+  size_t row_cnt = 0, row_off = 0, plan = 0, total = 0, slots = 0, ds = 0;
 };
 
 int64_t padded_rows(int64_t sq) { return ceil_div(sq, 128) * 128; }
@@ -157,6 +162,16 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
     off = align256(off + rows);
     L.drow = off;
     off = align256(off + rows);
+    const int64_t mrows = (int64_t)m->batch * m->heads;
+    const int64_t tq = ceil_div(p->seqlen_q, fm::kBwdBlockQ), tk = ceil_div(p->seqlen_k, fm::kBwdBlockK);
+    L.row_cnt = off;
+    off = align256(off + (size_t)(mrows * tk * 4));
+    L.row_off = off;
+    off = align256(off + (size_t)(mrows * tk * 4));
+    L.plan = off;
+    off = align256(off + 16);
+    L.slots = off;
+    L.ds = align256(off + (size_t)(mrows * tk * tq * 4));
   } else {
     add_tiling(fm::kFwdBlockQ, fm::kFwdBlockK, &L.summary, &L.map);
   }
@@ -181,6 +196,64 @@ fm_status classify_into(const fm::MaskArgs& mk, int32_t sq, int32_t sk, int32_t 
   if (e != hipSuccess) return hip_fail(e, "classify summary launch");
   e = run_stage(FM_STAGE_CLASSIFY_MAP, s, [&] { return fm::launch_classify_map(c, s); });
   if (e != hipSuccess) return hip_fail(e, "classify map launch");
+  return FM_OK;
+}
+
+// Validation, classification (both tilings) and the arguments shared by
+// fm_attn_bwd and fm_bwd_workspace_size_ds; tensor pointers are left unset.
+fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t ws_bytes, hipStream_t stream,
+                    fm::BwdArgs* out, Layout* lay) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  fm::MaskArgs mk;
+  st = check_mask(mask, p->batch, p->heads, &mk);
+  if (st != FM_OK) return st;
+  const Layout L = workspace_layout(p, mask, true);
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(FM_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(FM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  const int32_t tq = (int32_t)ceil_div(p->seqlen_q, fm::kBwdBlockQ);
+  const int32_t tk = (int32_t)ceil_div(p->seqlen_k, fm::kBwdBlockK);
+  const int32_t tq_q = (int32_t)ceil_div(p->seqlen_q, fm::kDqBlockQ);
+  const int32_t tk_q = (int32_t)ceil_div(p->seqlen_k, fm::kDqBlockK);
+  if (tk > 65535 || tq_q > 65535) return fail(FM_ERR_INVALID_ARGUMENT, "sequence too long");
+  char* w = static_cast<char*>(ws);
+  uint8_t* classes_t = reinterpret_cast<uint8_t*>(w + L.map);
+  uint8_t* classes_q = reinterpret_cast<uint8_t*>(w + L.map_q);
+  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kBwdBlockQ, fm::kBwdBlockK, 1,
+                     reinterpret_cast<int32_t*>(w + L.summary), classes_t, stream);
+  if (st != FM_OK) return st;
+  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kDqBlockQ, fm::kDqBlockK, 0,
+                     reinterpret_cast<int32_t*>(w + L.summary_q), classes_q, stream);
+  if (st != FM_OK) return st;
+
+  fm::BwdArgs& a = *out;
+  a.lse2 = reinterpret_cast<float*>(w + L.lse2);
+  a.drow = reinterpret_cast<float*>(w + L.drow);
+  a.seq_pad = (int32_t)padded_rows(p->seqlen_q);
+  a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
+  a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
+  a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
+  a.o_sb = p->o_stride[0]; a.o_ss = p->o_stride[1]; a.o_sh = p->o_stride[2];
+  a.batch = p->batch;
+  a.heads = p->heads;
+  a.seq_q = p->seqlen_q;
+  a.seq_k = p->seqlen_k;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+  a.mask = mk;
+  a.classes_t = classes_t;
+  a.tq = tq;
+  a.tk = tk;
+  a.classes_q = classes_q;
+  a.tq_q = tq_q;
+  a.tk_q = tk_q;
+  a.row_cnt = reinterpret_cast<int32_t*>(w + L.row_cnt);
+  a.row_off = reinterpret_cast<int32_t*>(w + L.row_off);
+  a.plan = reinterpret_cast<int32_t*>(w + L.plan);
+  a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
+  *lay = L;
   return FM_OK;
 }
 
@@ -286,34 +359,13 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
                       void* ws, size_t ws_bytes, hipStream_t stream) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
-  fm::MaskArgs mk;
-  st = check_mask(mask, p->batch, p->heads, &mk);
-  if (st != FM_OK) return st;
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")) || (st = check_ptr(dout, "dout")) ||
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
     return st;
-  const Layout L = workspace_layout(p, mask, true);
-  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256)
-    return fail(FM_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
-  if (ws_bytes < L.total)
-    return fail(FM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
-  const int32_t tq = (int32_t)ceil_div(p->seqlen_q, fm::kBwdBlockQ);
-  const int32_t tk = (int32_t)ceil_div(p->seqlen_k, fm::kBwdBlockK);
-  const int32_t tq_q = (int32_t)ceil_div(p->seqlen_q, fm::kDqBlockQ);
-  const int32_t tk_q = (int32_t)ceil_div(p->seqlen_k, fm::kDqBlockK);
-  if (tk > 65535 || tq_q > 65535) return fail(FM_ERR_INVALID_ARGUMENT, "sequence too long");
-  char* w = static_cast<char*>(ws);
-  uint8_t* classes_t = reinterpret_cast<uint8_t*>(w + L.map);
-  uint8_t* classes_q = reinterpret_cast<uint8_t*>(w + L.map_q);
-  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kBwdBlockQ, fm::kBwdBlockK, 1,
-                     reinterpret_cast<int32_t*>(w + L.summary), classes_t, stream);
-  if (st != FM_OK) return st;
-  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kDqBlockQ, fm::kDqBlockK, 0,
-                     reinterpret_cast<int32_t*>(w + L.summary_q), classes_q, stream);
-  if (st != FM_OK) return st;
-
   fm::BwdArgs a{};
+  Layout L;
+  if ((st = bwd_setup(p, mask, ws, ws_bytes, stream, &a, &L)) != FM_OK) return st;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -323,33 +375,51 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.lse2 = reinterpret_cast<float*>(w + L.lse2);
-  a.drow = reinterpret_cast<float*>(w + L.drow);
-  a.seq_pad = (int32_t)padded_rows(p->seqlen_q);
-  a.q_sb = p->q_stride[0]; a.q_ss = p->q_stride[1]; a.q_sh = p->q_stride[2];
-  a.k_sb = p->k_stride[0]; a.k_ss = p->k_stride[1]; a.k_sh = p->k_stride[2];
-  a.v_sb = p->v_stride[0]; a.v_ss = p->v_stride[1]; a.v_sh = p->v_stride[2];
-  a.o_sb = p->o_stride[0]; a.o_ss = p->o_stride[1]; a.o_sh = p->o_stride[2];
-  a.batch = p->batch;
-  a.heads = p->heads;
-  a.seq_q = p->seqlen_q;
-  a.seq_k = p->seqlen_k;
-  a.scale = p->softmax_scale;
-  a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
-  a.mask = mk;
-  a.classes_t = classes_t;
-  a.tq = tq;
-  a.tk = tk;
-  a.classes_q = classes_q;
-  a.tq_q = tq_q;
-  a.tk_q = tk_q;
+  // Stored dS when the workspace can hold at least the slot map; whether it
+  // holds every dS tile is decided on the device by the plan.
+  char* w = static_cast<char*>(ws);
+  const bool maybe_ds = ws_bytes >= L.ds;
+  if (maybe_ds) {
+    a.slots = reinterpret_cast<int32_t*>(w + L.slots);
+    a.ds = reinterpret_cast<uint16_t*>(w + L.ds);
+    a.ds_capacity = (int64_t)(ws_bytes - L.ds);
+    hipError_t e = run_stage(FM_STAGE_BWD_PLAN, stream, [&] { return fm::launch_bwd_plan(a, true, stream); });
+    if (e != hipSuccess) return hip_fail(e, "stored-dS plan launch");
+  } else {
+    a.plan = nullptr;
+  }
   const bool f32 = p->dtype == FM_FP32;
   hipError_t e = run_stage(FM_STAGE_BWD_PRE, stream, [&] { return fm::launch_bwd_pre(a, p->head_dim, f32, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward pre-pass launch");
   e = run_stage(FM_STAGE_BWD, stream, [&] { return fm::launch_bwd_dkdv(a, p->head_dim, f32, stream); });
   if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+  // both dQ kernels are launched when the dS store may be in use; each exits
+  // at once unless the plan selected its path
   e = run_stage(FM_STAGE_BWD_DQ, stream, [&] { return fm::launch_bwd_dq(a, p->head_dim, f32, stream); });
   if (e != hipSuccess) return hip_fail(e, "dQ launch");
+  if (maybe_ds) {
+    e = run_stage(FM_STAGE_BWD_DQ_DS, stream, [&] { return fm::launch_bwd_dq_ds(a, p->head_dim, f32, stream); });
+    if (e != hipSuccess) return hip_fail(e, "dQ (stored dS) launch");
+  }
+  return FM_OK;
+}
+
+fm_status fm_bwd_workspace_size_ds(const fm_problem* p, const fm_mask* mask, void* ws, size_t ws_bytes,
+                                   hipStream_t stream, size_t* bytes) {
+  if (!bytes) return fail(FM_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  fm::BwdArgs a{};
+  Layout L;
+  fm_status st = bwd_setup(p, mask, ws, ws_bytes, stream, &a, &L);
+  if (st != FM_OK) return st;
+  a.ds_capacity = 0;
+  hipError_t e = run_stage(FM_STAGE_BWD_PLAN, stream, [&] { return fm::launch_bwd_plan(a, false, stream); });
+  if (e != hipSuccess) return hip_fail(e, "stored-dS plan launch");
+  int32_t total = 0;
+  if ((e = hipMemcpyAsync(&total, a.plan, sizeof(total), hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+      (e = hipStreamSynchronize(stream)) != hipSuccess)
+    return hip_fail(e, "reading the tile count");
+  if (total == INT32_MAX) return fail(FM_ERR_UNSUPPORTED, "too many non-SKIP tiles for the dS store");
+  *bytes = L.ds + (size_t)total * (size_t)a.rep * (size_t)fm::kBwdBlockQ * fm::kBwdBlockK * 2;
   return FM_OK;
 }
 

@@ -108,6 +108,8 @@ struct alignas(16) Smem {
   float lse2[NBUF][BQ];          // LSE * log2(e); +inf for rows that see nothing / past the end
   float dd[NBUF][BQ];            // D = rowsum(dO * O)
   uint32_t list[LIST_CAP];
+  uint16_t rank[LIST_CAP];       // ascending rank of each list entry (stored-dS slot)
+  uint16_t dsx[NW][32 * BQ];     // per wavefront: its 32 keys' dS, regrouped for coalesced stores
   int32_t scan[NW];
 };
 }  // namespace kv
@@ -168,6 +170,22 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const uint32_t b_uw = b_ute > b_uts ? (uint32_t)b_ute - (uint32_t)b_uts : 0u;
   const bool ragged_k = (a.seq_k % BK) != 0 && kt == a.tk - 1;
 
+  // Stored dS: when the plan enables it, every processed tile's bf16 dS goes
+  // to slot row_off[mask row][kt] + (rank of its query tile among this key
+  // tile's non-SKIP ones), as [key][column] with the tile's BK keys and BQ
+  // columns. Column c = 32 g + 16 mb + 8 t + j holds row
+  // 32 mb + 16 t + 4 g + (j < 4 ? j : j + 4): the eight rows that one lane
+  // packs for one (mb, t) sit in 16 contiguous bytes.
+  const bool store_ds = a.plan != nullptr && a.plan[1] != 0;
+  const int mrow = bm * a.mask.hm + hm;
+  int64_t slot0 = 0;
+  uint16_t* ds_rep = nullptr;
+  if (store_ds) {
+    const int rep_i = (a.mask.bm > 1 ? 0 : b) * (a.mask.hm > 1 ? 1 : a.heads) + (a.mask.hm > 1 ? 0 : h);
+    slot0 = a.row_off[(int64_t)mrow * a.tk + kt];
+    ds_rep = a.ds + (int64_t)rep_i * a.plan[0] * (BK * BQ);
+  }
+
   f32x16 dvacc[CB], dkacc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
@@ -219,9 +237,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   int it_global = 0;
   for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
     int n_full;
-    const int n_list = compact_classes_split<LIST_CAP, NT>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.scan,
-                                                           tid, ragged_k, &n_full);
+    const int n_list = compact_classes_split<LIST_CAP, NT>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.rank,
+                                                           sm.scan, tid, ragged_k, &n_full);
     if (n_list == 0) continue;
+    const int pass_base = it_global;   // non-SKIP tiles in earlier passes
 
     stage_q((int)(sm.list[0] & ~kPartialBit), it_global % NBUF);
     if (n_list > 1) stage_q((int)(sm.list[1] & ~kPartialBit), (it_global + 1) % NBUF);
@@ -233,13 +252,10 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
       const int buf = it_global % NBUF;
       const int qt = (int)(sm.list[it] & ~kPartialBit);
       const int m0 = qt * BQ;
-      // this tile's loads done (the next tile's may still be in flight)
-      if (it + 1 < n_list) {
-        if (wu < 2) wait_vmem_le<GROUP + 1>();
-        else wait_vmem_le<GROUP>();
-      } else {
-        wait_vmem();
-      }
+      // This tile's loads done. Younger vector-memory operations that may stay
+      // in flight: the next tile's loads and the dS stores of the last two
+      // iterations of this pass (vmcnt counts stores too).
+      wait_vmem_upto((it + 1 < n_list ? GROUP + (wu < 2 ? 1 : 0) : 0) + (store_ds ? 4 * min(it, 2) : 0));
       __syncthreads();   // tile `buf` visible to all; the buffer read last iteration is free
       if (it + 2 < n_list) stage_q((int)(sm.list[it + 2] & ~kPartialBit), (it_global + 2) % NBUF);
       const char* qb = reinterpret_cast<const char*>(sm.q[buf]);
@@ -347,6 +363,31 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_barrier(0);
+
+        if (store_ds) {   // 4 stores per lane, counted by the wait above
+          // Through the wavefront's own LDS block (128-byte key rows, 16-byte
+          // chunk c at c ^ ((row >> 1) & 7), conflict-free both ways): lanes
+          // write their keys' chunks, then 8 lanes per row read whole rows,
+          // so each store writes 1 KiB of consecutive key rows. LDS accesses
+          // of one wavefront execute in order; no barrier is needed.
+          char* xb = reinterpret_cast<char*>(sm.dsx[w]);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int ch = 4 * g + 2 * mb + t;
+              *reinterpret_cast<u32x4*>(xb + lr * 128 + 16 * (ch ^ ((lr >> 1) & 7))) = dsp[mb][t];
+            }
+          const int64_t slot = slot0 + pass_base + sm.rank[it];
+          uint16_t* wtile = ds_rep + slot * (BK * BQ) + (32 * w) * BQ;   // this wavefront's 32 key rows
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + (l >> 3), c = l & 7;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(xb + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(wtile + r * BQ + 8 * c));   // read once, later
+          }
+        }
       }
     };
     int it = 0;
@@ -399,6 +440,7 @@ struct alignas(16) Smem {
 template <int D, bool F32>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(BwdArgs a) {
   using namespace dqk;
+  if (a.plan != nullptr && a.plan[1] != 0) return;   // dQ comes from the stored dS instead
   constexpr int KSTEPS = D / 16;
   constexpr int CB = D / 32;
   constexpr int NB = BK / 32;

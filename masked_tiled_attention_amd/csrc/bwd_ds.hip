@@ -1,0 +1,286 @@
+// Backward with stored dS: slot plan and dQ = scale * dS K.
+//
+// "FlashAttention-2 ... GPU work partitioning" (iplexlaw.co.kr), section
+// "Block processing keeps the global normalization": dQ = scale * dS K with
+// dS = P (dP - D) is exact attention's gradient; how dS reaches the product
+// is an implementation choice. The dK/dV kernel forms every non-SKIP bf16 dS
+// tile anyway (as an MFMA operand); when the workspace holds them all, it
+// writes them out and dQ becomes a plain product over the stored tiles,
+// instead of a second kernel that recomputes S and dP (6 d flops per open
+// pair then, 2 d flops and 2 bytes of dS traffic per pair here).
+//
+// Kernels:
+//   plan_count  non-SKIP tiles per key-tile row of the dK/dV class map;
+//   plan_scan   one workgroup: exclusive prefix sums (slot offsets), the total
+//               and whether the workspace holds every tile for every (b, h);
+//   dq_ds       one workgroup per (b, h, 64-row query tile): for each non-SKIP
+//               key tile, K and the stored dS tile go straight into LDS (three
+//               buffers, two tiles ahead) and dQ^T += K^T dS^T accumulates in
+//               registers, wavefront w owning 32 of the channels.
+#include <climits>
+#include <cmath>
+
+#include "fm_device.hpp"
+#include "fm_internal.hpp"
+#include "fm_tile.hpp"
+
+namespace fm {
+namespace {
+
+constexpr int BQ = kBwdBlockQ;   // rows per dS tile
+constexpr int BK = kBwdBlockK;   // keys per dS tile
+constexpr int NW = 4;
+constexpr int NT = NW * 64;
+constexpr int LIST_CAP = 1024;
+constexpr int NBUF = 3;
+constexpr int64_t kTileBytes = (int64_t)BQ * BK * 2;
+
+// ------------------------------------------------------------------ plan
+// grid (tk, mask rows): row_cnt[mr][kt] = non-SKIP entries of class row (mr, kt).
+__global__ __launch_bounds__(256) void plan_count_kernel(BwdArgs a) {
+  const int kt = blockIdx.x, mr = blockIdx.y;
+  const uint8_t* row = a.classes_t + ((int64_t)mr * a.tk + kt) * a.tq;
+  int c = 0;
+  for (int q = threadIdx.x; q < a.tq; q += 256) c += row[q] != FM_TILE_SKIP;
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  __shared__ int red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) a.row_cnt[(int64_t)mr * a.tk + kt] = red[0] + red[1] + red[2] + red[3];
+}
+
+// grid (tk, mask rows): slots[mr][kt][qt] = row_off[mr][kt] + rank of qt
+// among the row's non-SKIP entries (entries of SKIP tiles are not written).
+__global__ __launch_bounds__(256) void plan_slots_kernel(BwdArgs a) {
+  const int kt = blockIdx.x, mr = blockIdx.y;
+  const int64_t r = (int64_t)mr * a.tk + kt;
+  const uint8_t* row = a.classes_t + r * a.tq;
+  int32_t* out = a.slots + r * a.tq;
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = a.row_off[r];
+  for (int base = 0; base < a.tq; base += 256) {
+    const int q = base + tid;
+    const int v = q < a.tq && row[q] != FM_TILE_SKIP;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int pre = carry, chunk = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < wv) pre += wsum[k];
+      chunk += wsum[k];
+    }
+    if (v) out[q] = pre + incl - 1;
+    carry += chunk;
+    __syncthreads();
+  }
+}
+
+// One workgroup of 1024: row_off = exclusive prefix sums of row_cnt over the
+// nrows = mask rows * tk rows in order, plan[0] = total, plan[1] = 1 when
+// rep * total tiles fit into ds_capacity bytes (and slots fit in int32).
+__global__ __launch_bounds__(1024) void plan_scan_kernel(BwdArgs a, int32_t nrows) {
+  __shared__ int wsum[16];
+  __shared__ int64_t carry;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < nrows; base += 1024) {
+    const int i = base + tid;
+    const int v = i < nrows ? a.row_cnt[i] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int64_t pre = carry;
+    int chunk = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (k < wv) pre += wsum[k];
+      chunk += wsum[k];
+    }
+    if (i < nrows) a.row_off[i] = (int32_t)min(pre + incl - v, (int64_t)INT_MAX);
+    __syncthreads();
+    if (tid == 0) carry += chunk;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int64_t total = carry;
+    a.plan[0] = (int32_t)min(total, (int64_t)INT_MAX);
+    a.plan[1] = (total < INT_MAX && total * a.rep * kTileBytes <= a.ds_capacity) ? 1 : 0;
+  }
+}
+
+// ------------------------------------------------------------------ dQ from dS
+template <int D>
+struct alignas(16) DsSmem {
+  uint16_t k[NBUF][BK * D];    // key tiles, row-major, swizzled
+  uint16_t ds[NBUF][BK * BQ];  // dS tiles [key][row], swizzled
+  uint32_t list[LIST_CAP];
+  int32_t slot[LIST_CAP];      // stored-dS slot of each list entry
+  int32_t scan[NW];
+};
+
+template <int D, bool F32>
+__global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
+  if (a.plan == nullptr || a.plan[1] == 0) return;   // dQ comes from the recompute kernel
+  constexpr int CB = D / 32;              // 32-channel blocks of dQ^T
+  constexpr int BLK = 2 * CB / NW;        // (channel block, row block) pairs per wavefront
+  constexpr int KR = (BK * D / 8) / NT;   // 16-byte chunks per thread of a float32 key tile
+  constexpr int ES = F32 ? 4 : 2;
+  __shared__ DsSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int l = tid & 63;
+  const int lr = l & 31;
+  const int g = l >> 5;
+
+  // later query tiles first (under causal-like masks they see the most keys)
+  const int nbh = a.batch * a.heads;
+  const int qt = a.tq - 1 - (int)(blockIdx.x / nbh);
+  const int bh = blockIdx.x % nbh;
+  const int b = bh / a.heads;
+  const int h = bh % a.heads;
+  const int bm = a.mask.bm > 1 ? b : 0;
+  const int hm = a.mask.hm > 1 ? h : 0;
+  const int mrow = bm * a.mask.hm + hm;
+  const int rep_i = (a.mask.bm > 1 ? 0 : b) * (a.mask.hm > 1 ? 1 : a.heads) + (a.mask.hm > 1 ? 0 : h);
+  const int64_t total = a.plan[0];
+  const uint16_t* ds_rep = a.ds + (int64_t)rep_i * total * (BK * BQ);
+  const uint8_t* ccol = a.classes_t + (int64_t)mrow * a.tk * a.tq + qt;   // stride tq over kt
+  const int32_t* scol = a.slots + (int64_t)mrow * a.tk * a.tq + qt;
+
+  // this wavefront's channel block and row blocks
+  const int cbw = CB == 4 ? w : (w & 1);
+  f32x16 acc[BLK];
+#pragma unroll
+  for (int j = 0; j < BLK; ++j) acc[j] = f32x16{};
+
+  // ---- staging: K (bf16: direct loads; float32: through registers) and dS ----
+  const int64_t k_ld = a.k_ss * ES;
+  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
+  using DmaK = DmaTile<D, BK, NT>;
+  using DmaS = DmaTile<BQ, BK, NT>;
+  constexpr int NOFF = F32 ? KR : 1;
+  uint32_t koff[NOFF];
+  if constexpr (F32) {
+    tile_offsets<D, F32, KR, NT>(koff, k_ld, tid);
+  } else {
+    koff[0] = DmaK::offset(k_ld, tid);
+  }
+  const uint32_t soff = DmaS::offset(BQ * 2, tid);
+  constexpr int GROUP = (F32 ? 0 : DmaK::PER) + DmaS::PER;   // direct loads per tile and wavefront
+  auto stage = [&](int idx, int buf) {   // list entry idx -> buffer buf
+    const int kt = __builtin_amdgcn_readfirstlane((int)(sm.list[idx] & ~kPartialBit));   // uniform
+    const int n0 = kt * BK;
+    if constexpr (F32) {
+      u32x4 rk[KR];
+      load_tile_rows<D, F32, KR, NT>(rk, kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
+      store_tile_rows<D, KR, NT>(reinterpret_cast<char*>(sm.k[buf]), rk, tid);
+    } else {
+      DmaK::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff[0], k_ld, tid, a.seq_k - n0);
+    }
+    const int64_t slot = __builtin_amdgcn_readfirstlane(sm.slot[idx]);   // uniform
+    DmaS::template load<true>(reinterpret_cast<char*>(sm.ds[buf]), reinterpret_cast<const char*>(ds_rep + slot * (BK * BQ)), soff,
+               BQ * 2, tid, BK);
+  };
+
+  int it_global = 0;
+  for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
+    const int n_list = compact_classes<LIST_CAP, NT>(ccol, kt0, min(LIST_CAP, a.tk - kt0), sm.list, sm.scan, tid,
+                                                     (int64_t)a.tq);
+    if (n_list == 0) continue;
+    for (int i = tid; i < n_list; i += NT) sm.slot[i] = scol[(int64_t)(sm.list[i] & ~kPartialBit) * a.tq];
+    __syncthreads();
+    stage(0, it_global % NBUF);
+    if (n_list > 1) stage(1, (it_global + 1) % NBUF);
+
+    for (int it = 0; it < n_list; ++it, ++it_global) {
+      const int buf = it_global % NBUF;
+      if (it + 1 < n_list) wait_vmem_le<GROUP>();   // this tile landed; the next may be in flight
+      else wait_vmem();
+      __syncthreads();   // tile `buf` visible to all; the buffer read last iteration is free
+      if (it + 2 < n_list) stage(it + 2, (it_global + 2) % NBUF);
+      const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
+      const char* sb = reinterpret_cast<const char*>(sm.ds[buf]);
+
+      // dQ^T (channels x rows) += K^T (channels x keys) dS^T (keys x rows),
+      // 16 keys per step; both operands read transposed with the same key
+      // order per lane half.
+#pragma unroll
+      for (int s = 0; s < BK / 16; ++s) {
+        const int r0 = 16 * s + 4 * g;
+        const u32x4 ka = tr_operand<D>(kb, l, 32 * cbw, r0, r0 + 8);
+#pragma unroll
+        for (int j = 0; j < BLK; ++j) {
+          const int rb = CB == 4 ? j : (w >> 1);
+          acc[j] = mfma32(ka, tr_operand<BQ>(sb, l, 32 * rb, r0, r0 + 8), acc[j]);
+        }
+      }
+      sched_lds_mfma<(BK / 16) * BLK, (2 + 2 * BLK) / BLK, 2>();
+    }
+  }
+
+  // ---- epilogue: dQ = scale * (dQ^T)^T; lane = query row, registers = channels ----
+  // Output column c of the stored layout is row 32 mb + 16 t + 4 g + (j < 4 ?
+  // j : j + 4) with g = c / 32, mb, t = bits 4, 3 of c, j = c % 8.
+#pragma unroll
+  for (int j = 0; j < BLK; ++j) {
+    const int rb = CB == 4 ? j : (w >> 1);
+    const int c = 32 * rb + lr;
+    const int jj = c & 7;
+    const int m = qt * BQ + 32 * ((c >> 4) & 1) + 16 * ((c >> 3) & 1) + 4 * (c >> 5) + (jj < 4 ? jj : jj + 4);
+    if (m < a.seq_q) {
+      const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int c0 = 32 * cbw + 8 * q4 + 4 * g;
+        const float x0 = acc[j][4 * q4] * a.scale, x1 = acc[j][4 * q4 + 1] * a.scale;
+        const float x2 = acc[j][4 * q4 + 2] * a.scale, x3 = acc[j][4 * q4 + 3] * a.scale;
+        if constexpr (F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dq) + qoff + c0) = f32x4{x0, x1, x2, x3};
+        } else {
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.dq) + qoff + c0) =
+              u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+        }
+      }
+    }
+  }
+}
+
+template <int D, bool F32>
+hipError_t launch_dq_ds_t(const BwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F32>), dim3(a.tq * a.batch * a.heads), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_plan(const BwdArgs& a, bool with_slots, hipStream_t stream) {
+  const int mrows = a.mask.bm * a.mask.hm;
+  hipLaunchKernelGGL(plan_count_kernel, dim3(a.tk, mrows), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, a, (int32_t)(mrows * a.tk));
+  if ((e = hipGetLastError()) != hipSuccess || !with_slots) return e;
+  hipLaunchKernelGGL(plan_slots_kernel, dim3(a.tk, mrows), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, bool f32, hipStream_t s) {
+  if (head_dim == 128) return f32 ? launch_dq_ds_t<128, true>(a, s) : launch_dq_ds_t<128, false>(a, s);
+  return f32 ? launch_dq_ds_t<64, true>(a, s) : launch_dq_ds_t<64, false>(a, s);
+}
+
+}  // namespace fm

@@ -80,7 +80,19 @@ struct BwdArgs {
   int32_t tq, tk;
   const uint8_t* classes_q;  // [bm][hm][tq_q][tk_q] with the dQ kernel's tiles
   int32_t tq_q, tk_q;
+  // Stored dS (dQ from dS K), with the dK/dV tiling; plan == nullptr when the
+  // workspace cannot hold the slot map at all.
+  int32_t* row_cnt;          // [bm*hm][tk] non-SKIP tiles per key-tile row
+  int32_t* row_off;          // [bm*hm][tk] exclusive prefix sums of row_cnt
+  int32_t* plan;             // [0] total non-SKIP tiles, [1] 1 if the dS store is in use
+  int32_t* slots;            // [bm*hm][tk][tq] slot of each non-SKIP tile
+  uint16_t* ds;              // [rep][total][kBwdBlockK keys][kBwdBlockQ rows] bf16
+  int64_t ds_capacity;       // bytes available at ds
+  int32_t rep;               // (b, h) pairs per mask row
 };
+
+hipError_t launch_bwd_plan(const BwdArgs& a, bool with_slots, hipStream_t stream);
+hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 
 constexpr int kMaxChunks = 64;
 

@@ -61,12 +61,13 @@ __device__ __forceinline__ u32x4 tr_operand(const char* base, int lane, int obas
 }
 
 // Compact the non-SKIP entries of one class-map row (entries [first,
-// first + count)) into sm_list in ascending order, flagging PARTIAL ones;
-// returns the number of entries. CAP / NT entries per thread. Starts and ends
-// with a barrier, so callers may reuse every LDS buffer around it.
+// first + count), entry e at row[e * stride]) into sm_list in ascending
+// order, flagging PARTIAL ones; returns the number of entries. CAP / NT
+// entries per thread. Starts and ends with a barrier, so callers may reuse
+// every LDS buffer around it.
 template <int CAP, int NT>
 __device__ __forceinline__ int compact_classes(const uint8_t* row, int first, int count, uint32_t* sm_list,
-                                               int32_t* sm_scan, int tid) {
+                                               int32_t* sm_scan, int tid, int64_t stride = 1) {
   constexpr int PER = CAP / NT;
   constexpr int NWAVE = NT / 64;
   const int lane = tid & 63, wave = tid >> 6;
@@ -75,7 +76,7 @@ __device__ __forceinline__ int compact_classes(const uint8_t* row, int first, in
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int idx = tid * PER + e;
-    cls[e] = idx < count ? row[first + idx] : (uint8_t)FM_TILE_SKIP;
+    cls[e] = idx < count ? row[(first + idx) * stride] : (uint8_t)FM_TILE_SKIP;
     cnt += cls[e] != FM_TILE_SKIP;
   }
   int incl = cnt;
@@ -107,9 +108,12 @@ __device__ __forceinline__ int compact_classes(const uint8_t* row, int first, in
 // As compact_classes(), but the list holds the FULL entries first and the
 // PARTIAL ones after them (each group ascending); *n_full receives the number
 // of FULL entries. With all_partial, every entry counts as PARTIAL.
+// sm_rank[i] receives list entry i's rank among all non-SKIP entries in
+// ascending order.
 template <int CAP, int NT>
 __device__ __forceinline__ int compact_classes_split(const uint8_t* row, int first, int count, uint32_t* sm_list,
-                                                     int32_t* sm_scan, int tid, bool all_partial, int* n_full) {
+                                                     uint16_t* sm_rank, int32_t* sm_scan, int tid,
+                                                     bool all_partial, int* n_full) {
   constexpr int PER = CAP / NT;
   constexpr int NWAVE = NT / 64;
   const int lane = tid & 63, wave = tid >> 6;
@@ -142,11 +146,17 @@ __device__ __forceinline__ int compact_classes_split(const uint8_t* row, int fir
   }
   const int nf = tot & 0xffff, np = tot >> 16;
   int pf = pos & 0xffff, pp = nf + (pos >> 16);
+  int rank = (pos & 0xffff) + (pos >> 16);
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const uint32_t id = (uint32_t)(first + tid * PER + e);
-    if (cls[e] == FM_TILE_FULL) sm_list[pf++] = id;
-    else if (cls[e] == FM_TILE_PARTIAL) sm_list[pp++] = id | kPartialBit;
+    if (cls[e] == FM_TILE_FULL) {
+      sm_rank[pf] = (uint16_t)rank++;
+      sm_list[pf++] = id;
+    } else if (cls[e] == FM_TILE_PARTIAL) {
+      sm_rank[pp] = (uint16_t)rank++;
+      sm_list[pp++] = id | kPartialBit;
+    }
   }
   __syncthreads();
   *n_full = nf;
@@ -230,13 +240,17 @@ struct DmaTile {
   // Issue the tile's loads; `lds` is the tile's LDS base, `off` = offset().
   // Rows at or past `nvalid` re-read row nvalid - 1. The caller awaits
   // completion with wait_vmem() before the barrier that publishes the tile.
+  template <bool STREAM = false>
   __device__ static __forceinline__ void load(char* lds, const char* tile, uint32_t off, int64_t ld, int tid,
                                               int nvalid) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t base = lds_address(lds) + (uint32_t)w * 1024u;
     if (nvalid >= ROWS) {
 #pragma unroll
-      for (int i = 0; i < PER; ++i) dma16(tile + i * STEP * ld, off, base + (uint32_t)(i * NW) * 1024u);
+      for (int i = 0; i < PER; ++i) {
+        if constexpr (STREAM) dma16_nt(tile + i * STEP * ld, off, base + (uint32_t)(i * NW) * 1024u);
+        else dma16(tile + i * STEP * ld, off, base + (uint32_t)(i * NW) * 1024u);
+      }
     } else {
       const int r0 = row0(tid), ch = chunk(tid);
 #pragma unroll
@@ -263,6 +277,17 @@ struct DmaTile {
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_dst), "v"(voff), "s"(base)
+        : "memory", "m0");
+  }
+  // The same with the non-temporal hint, for data read once (kept out of the
+  // caches' way of reused tiles).
+  __device__ static __forceinline__ void dma16_nt(const char* base, uint32_t voff, uint32_t lds_dst) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt"
         :
         : "s"(lds_dst), "v"(voff), "s"(base)
         : "memory", "m0");
@@ -298,5 +323,25 @@ __device__ __forceinline__ void wait_vmem_le() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
+
+// wait_vmem_le<n>() for a wavefront-uniform n in [0, 31] (larger n: n = 31,
+// which waits for more than asked, never less).
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+  switch (n) {
+#define FM_WAIT_CASE(k) \
+  case k:               \
+    wait_vmem_le<k>();  \
+    break;
+    FM_WAIT_CASE(0) FM_WAIT_CASE(1) FM_WAIT_CASE(2) FM_WAIT_CASE(3) FM_WAIT_CASE(4) FM_WAIT_CASE(5)
+    FM_WAIT_CASE(6) FM_WAIT_CASE(7) FM_WAIT_CASE(8) FM_WAIT_CASE(9) FM_WAIT_CASE(10) FM_WAIT_CASE(11)
+    FM_WAIT_CASE(12) FM_WAIT_CASE(13) FM_WAIT_CASE(14) FM_WAIT_CASE(15) FM_WAIT_CASE(16) FM_WAIT_CASE(17)
+    FM_WAIT_CASE(18) FM_WAIT_CASE(19) FM_WAIT_CASE(20) FM_WAIT_CASE(21) FM_WAIT_CASE(22) FM_WAIT_CASE(23)
+    FM_WAIT_CASE(24) FM_WAIT_CASE(25) FM_WAIT_CASE(26) FM_WAIT_CASE(27) FM_WAIT_CASE(28) FM_WAIT_CASE(29)
+    FM_WAIT_CASE(30)
+#undef FM_WAIT_CASE
+    default:
+      wait_vmem_le<31>();
+  }
+}
 
 }  // namespace fm

@@ -106,3 +106,98 @@ def test_bwd_invariants(gpu_lib):
     scale_ref = np.abs(np64(dk)).sum(axis=1).max()
     assert np.abs(sdk).max() <= 1e-2 * scale_ref, np.abs(sdk).max()
     assert_close(sdv, ref, "sum dV = sum dO", max_abs=0.25, rel_l2=1e-2)
+
+
+# ---------------------------------------------------------------- stored dS
+def _run_ds(fm, q, k, v, do, vec, scale, short=0):
+    """Backward with the workspace that lets it store dS (minus `short` bytes)."""
+    q, k, v, do = (t.cuda() for t in (q, k, v, do))
+    m = dev_mask(vec)
+    o, lse = fm.fm_attn_fwd(q, k, v, m, scale)
+    nbytes = fm.fm_bwd_workspace_size_ds(q, k, v, m, scale) - short
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dq, dk, dv = fm.fm_attn_bwd(q, k, v, o, lse, do, m, scale, workspace=ws)
+    dq0, dk0, dv0 = fm.fm_attn_bwd(q, k, v, o, lse, do, m, scale)   # minimum workspace: recompute
+    torch.cuda.synchronize()
+    return [t.cpu() for t in (dq, dk, dv, dq0, dk0, dv0)]
+
+
+def _compare_ds(fm, q, k, v, do, vec, scale, tag, short=0, out_round=0.0):
+    log(f"bwd stored-dS {tag} q={tuple(q.shape)} k={tuple(k.shape)} dtype={q.dtype} short={short}")
+    dq, dk, dv, dq0, dk0, dv0 = _run_ds(fm, q, k, v, do, vec, scale, short)
+    rq, rk, rv = OA.backward(np64(q), np64(k), np64(v), np64(do), vec, scale)
+    assert_close(np64(dq), rq, f"{tag} dQ", out_round=out_round)
+    assert_close(np64(dk), rk, f"{tag} dK", out_round=out_round)
+    assert_close(np64(dv), rv, f"{tag} dV", out_round=out_round)
+    # dK and dV do not depend on the dQ path
+    assert torch.equal(dk, dk0) and torch.equal(dv, dv0)
+    return dq, dq0
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_bwd_stored_ds_mask_families(gpu_lib, d):
+    rng = np.random.default_rng(300 + d)
+    n = 700
+    for name, v in _families(n, rng).items():
+        q, k, vv, do = ST.qkv(2, n, n, 3, d, seed=d + 7 * len(name), with_do=True)
+        _compare_ds(gpu_lib, q, k, vv, do, tuple(x[None, None] for x in v), 1 / math.sqrt(d), f"{name} d={d}")
+
+
+def test_bwd_stored_ds_per_batch_and_head_masks(gpu_lib):
+    rng = np.random.default_rng(21)
+    n, B, H, d = 520, 2, 3, 128
+    per = [[list(_families(n, rng).values())[(b * H + h + 1) % 6] for h in range(H)] for b in range(B)]
+    vec = SM.stack(per)
+    q, k, v, do = ST.qkv(B, n, n, H, d, seed=25, with_do=True)
+    _compare_ds(gpu_lib, q, k, v, do, vec, 0.09, "per-(b,h) masks")
+
+
+def test_bwd_stored_ds_random_vectors_rectangular(gpu_lib):
+    rng = np.random.default_rng(22)
+    for sq, sk in ((300, 900), (900, 300), (129, 65)):
+        vec = tuple(rng.integers(-20, sq + 20, (1, 1, sk)).astype(np.int32) for _ in range(4))
+        q, k, v, do = ST.qkv(1, sq, sk, 2, 128, seed=sq + 3, with_do=True)
+        _compare_ds(gpu_lib, q, k, v, do, vec, 0.1, f"random {sq}x{sk}")
+
+
+def test_bwd_stored_ds_float32_inputs(gpu_lib):
+    n = 300
+    vec = tuple(x[None, None] for x in SM.causal(n))
+    q, k, v, do = ST.qkv(1, n, n, 2, 64, seed=4, dtype=torch.float32, with_do=True)
+    _compare_ds(gpu_lib, q, k, v, do, vec, 0.125, "fp32 causal")
+
+
+def test_bwd_stored_ds_path_is_taken(gpu_lib):
+    """With the stored-dS workspace the recompute dQ kernel returns at once and
+    the stored-dS one does the work; one byte short, the other way round.
+    (Both paths form the same bf16 dS and sum it in the same key order, so
+    the results alone need not differ; the per-kernel times tell.)"""
+    n, H, d = 4096, 4, 128
+    vec = tuple(x[None, None] for x in SM.causal(n))
+    q, k, v, do = (t.cuda() for t in ST.qkv(1, n, n, H, d, seed=31, with_do=True))
+    m = dev_mask(vec)
+    o, lse = gpu_lib.fm_attn_fwd(q, k, v, m, 0.088)
+    full = gpu_lib.fm_bwd_workspace_size_ds(q, k, v, m, 0.088)
+    times = {}
+    for short in (0, 1):
+        ws = torch.empty(full - short, dtype=torch.uint8, device="cuda")
+        gpu_lib.fm_attn_bwd(q, k, v, o, lse, do, m, 0.088, workspace=ws)
+        torch.cuda.synchronize()
+        gpu_lib.fm_profile_begin(64)
+        gpu_lib.fm_attn_bwd(q, k, v, o, lse, do, m, 0.088, workspace=ws)
+        st = gpu_lib.fm_profile_end()
+        times[short] = (st["bwd_dq"][0], st["bwd_dq_ds"][0])
+    log(f"dQ kernel ms (recompute, stored dS): full workspace {times[0]}, one byte short {times[1]}")
+    assert times[0][0] < 0.2 * times[0][1]
+    assert times[1][1] < 0.2 * times[1][0]
+
+
+def test_bwd_stored_ds_short_workspace_falls_back(gpu_lib):
+    """One byte short of the stored-dS size: the plan keeps the recompute path,
+    bit for bit the result of the minimum workspace."""
+    rng = np.random.default_rng(23)
+    n = 600
+    vec = tuple(x[None, None] for x in SM.document_causal(SM.uniform_doc_lengths(rng, n, 40, 300)))
+    q, k, v, do = ST.qkv(1, n, n, 2, 128, seed=9, with_do=True)
+    dq, dq0 = _compare_ds(gpu_lib, q, k, v, do, vec, 0.088, "short workspace", short=1)
+    assert torch.equal(dq, dq0)
