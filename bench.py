@@ -52,7 +52,7 @@ def measured_traffic(kernel: str, workload: str):
     import hashlib
     import re
     root = os.path.dirname(os.path.abspath(__file__))
-    src = {"fwd": "fwd.hip", "bwd": "bwd.hip", "bwd_dq": "bwd.hip"}.get(kernel)
+    src = {"fwd": "fwd.hip", "bwd": "bwd.hip", "bwd_dq": "bwd.hip", "bwd_dq_ds": "bwd_ds.hip"}.get(kernel)
     if src is None:
         return None
     with open(os.path.join(root, "masked_tiled_attention_amd", "csrc", src), "rb") as f:
