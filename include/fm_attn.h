@@ -160,7 +160,9 @@ fm_status fm_tile_classify(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen
  * Outputs o [B,Sq,H,D] (device, problem dtype) and lse [B,H,Sq] (device,
  * float32). Fully masked (SKIP) tiles are never touched; the mask is
  * evaluated only on PARTIAL tiles. workspace: device, at least
- * fm_workspace_size(.., 0) bytes, 256-byte aligned. */
+ * fm_workspace_size(.., 0) bytes, 256-byte aligned. Tiles are launched
+ * longest first (by their number of non-SKIP partner tiles), here and in the
+ * backward; the order does not change any result. */
 fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, const void* v,
                       const fm_mask* mask, void* o, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -214,7 +216,8 @@ typedef enum {
   FM_STAGE_LOCALIZE = 6,
   FM_STAGE_BWD_PLAN = 7,    /* stored-dS slot plan (count, scan) */
   FM_STAGE_BWD_DQ_DS = 8,   /* dQ from stored dS */
-  FM_NUM_STAGES = 9
+  FM_STAGE_ORDER = 9,       /* launch orders, longest tiles first (count, sort) */
+  FM_NUM_STAGES = 10
 } fm_stage;
 
 fm_status fm_profile_begin(int32_t max_launches);

@@ -14,7 +14,7 @@ FM_OK, FM_ERR_INVALID_ARGUMENT, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_HIP
 FM_BF16, FM_FP32 = 0, 1
 FM_TILE_SKIP, FM_TILE_PARTIAL, FM_TILE_FULL = 0, 1, 2
 STAGES = ("classify_summary", "classify_map", "fwd", "bwd_pre", "bwd", "bwd_dq", "localize",
-          "bwd_plan", "bwd_dq_ds")
+          "bwd_plan", "bwd_dq_ds", "order")
 FM_NUM_STAGES = len(STAGES)
 
 STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_INVALID_ARGUMENT", 2: "FM_ERR_UNSUPPORTED",

@@ -139,6 +139,8 @@ fm_status check_ptr(const void* ptr, const char* name) {
 struct Layout {
   size_t summary = 0, map = 0, summary_q = 0, map_q = 0, lse2 = 0, drow = 0;
   size_t row_cnt = 0, row_off = 0, plan = 0, total = 0, slots = 0, ds = 0;
+  size_t counts = 0, order = 0;   // forward launch order
+  size_t order_k = 0, order_qq = 0;   // backward launch orders (counts, then order)
 };
 
 int64_t padded_rows(int64_t sq) { return ceil_div(sq, 128) * 128; }
@@ -170,10 +172,20 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
     off = align256(off + (size_t)(mrows * tk * 4));
     L.plan = off;
     off = align256(off + 16);
+    const int64_t tq_q = ceil_div(p->seqlen_q, fm::kDqBlockQ);
+    L.order_k = off;   // counts then order, for each of the two launch orders
+    off = align256(off + (size_t)(mrows * tk * 8));
+    L.order_qq = off;
+    off = align256(off + (size_t)(mrows * tq_q * 8));
     L.slots = off;
     L.ds = align256(off + (size_t)(mrows * tk * tq * 4));
   } else {
     add_tiling(fm::kFwdBlockQ, fm::kFwdBlockK, &L.summary, &L.map);
+    const size_t rows = (size_t)(bh * ceil_div(p->seqlen_q, fm::kFwdBlockQ)) * 4;
+    L.counts = off;
+    off = align256(off + rows);
+    L.order = off;
+    off = align256(off + rows);
   }
   L.total = off;
   return L;
@@ -253,6 +265,32 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   a.row_off = reinterpret_cast<int32_t*>(w + L.row_off);
   a.plan = reinterpret_cast<int32_t*>(w + L.plan);
   a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
+  // launch orders: key-tile rows of the transposed dK/dV map and the
+  // query-tile rows of the recompute dQ map
+  const int64_t mrows = (int64_t)mk.bm * mk.hm;
+  auto order = [&](size_t at, const uint8_t* cls, int64_t lines_per_mr, int64_t len, int64_t outer, int64_t line,
+                   int64_t elem) -> const int32_t* {
+    fm::OrderArgs o{};
+    o.classes = cls;
+    o.rows = (int32_t)(mrows * lines_per_mr);
+    o.len = (int32_t)len;
+    o.inner = (int32_t)lines_per_mr;
+    o.outer_stride = outer;
+    o.line_stride = line;
+    o.elem_stride = elem;
+    o.counts = reinterpret_cast<int32_t*>(w + at);
+    o.order = o.counts + o.rows;
+    if (run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_order(o, stream); }) != hipSuccess) return nullptr;
+    return o.order;
+  };
+  a.order_k = order(L.order_k, classes_t, tk, tq, (int64_t)tk * tq, tq, 1);
+  if (!a.order_k) return hip_fail(hipGetLastError(), "backward order launch");
+  // the recompute dQ kernel's order only when its path is certain (the
+  // workspace cannot hold the stored-dS slot map); else it keeps the default
+  if (ws_bytes < L.ds) {
+    a.order_qq = order(L.order_qq, classes_q, tq_q, tk_q, (int64_t)tq_q * tk_q, tk_q, 1);
+    if (!a.order_qq) return hip_fail(hipGetLastError(), "backward order launch");
+  }
   *lay = L;
   return FM_OK;
 }
@@ -348,7 +386,21 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   a.classes = classes;
   a.tq = tq;
   a.tk = tk;
-  hipError_t e = run_stage(FM_STAGE_FWD, stream,
+  fm::OrderArgs oa{};
+  oa.classes = classes;
+  oa.rows = (int32_t)((int64_t)mk.bm * mk.hm * tq);
+  oa.len = tk;
+  oa.inner = tq;
+  oa.outer_stride = (int64_t)tq * tk;
+  oa.line_stride = tk;
+  oa.elem_stride = 1;
+  oa.counts = reinterpret_cast<int32_t*>(w + L.counts);
+  oa.order = reinterpret_cast<int32_t*>(w + L.order);
+  hipError_t e = run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_order(oa, stream); });
+  if (e != hipSuccess) return hip_fail(e, "forward order launch");
+  a.order = oa.order;
+  a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
+  e = run_stage(FM_STAGE_FWD, stream,
                            [&] { return fm::launch_fwd(a, p->head_dim, p->dtype == FM_FP32, stream); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return FM_OK;

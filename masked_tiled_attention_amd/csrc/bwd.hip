@@ -128,15 +128,14 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const int lr = l & 31;
   const int g = l >> 5;
 
-  // Key tiles in ascending order first: under causal-like masks the early
-  // keys are seen by the most query rows.
-  const int nbh = a.batch * a.heads;
-  const int kt = blockIdx.x / nbh;
-  const int bh = blockIdx.x % nbh;
-  const int b = bh / a.heads;
-  const int h = bh % a.heads;
-  const int bm = a.mask.bm > 1 ? b : 0;
-  const int hm = a.mask.hm > 1 ? h : 0;
+  // Key tiles longest first, then the (b, h) pairs sharing the mask row.
+  const int line = __builtin_amdgcn_readfirstlane(a.order_k[blockIdx.x / a.rep]);   // mask row * tk + key tile
+  const int kt = line % a.tk;
+  const int mr = line / a.tk;
+  int b, h;
+  ordered_bh(mr, blockIdx.x % a.rep, a.mask, a.heads, &b, &h);
+  const int bm = mr / a.mask.hm;
+  const int hm = mr % a.mask.hm;
   const int64_t mbase = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
   const uint8_t* ccol = a.classes_t + ((int64_t)(bm * a.mask.hm + hm) * a.tk + kt) * a.tq;
 
@@ -453,14 +452,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int lr = l & 31;
   const int g = l >> 5;
 
-  // Heaviest query tiles first (under causal-like masks later rows see more keys).
-  const int nbh = a.batch * a.heads;
-  const int qt = a.tq_q - 1 - (int)(blockIdx.x / nbh);
-  const int bh = blockIdx.x % nbh;
-  const int b = bh / a.heads;
-  const int h = bh % a.heads;
-  const int bm = a.mask.bm > 1 ? b : 0;
-  const int hm = a.mask.hm > 1 ? h : 0;
+  // Query tiles longest first, then the (b, h) pairs sharing the mask row;
+  // without an order, later tiles first with heads interleaved.
+  int qt, mr, b, h;
+  if (a.order_qq != nullptr) {
+    const int line = __builtin_amdgcn_readfirstlane(a.order_qq[blockIdx.x / a.rep]);   // mask row * tq_q + tile
+    qt = line % a.tq_q;
+    mr = line / a.tq_q;
+    ordered_bh(mr, blockIdx.x % a.rep, a.mask, a.heads, &b, &h);
+  } else {
+    const int nbh = a.batch * a.heads;
+    qt = a.tq_q - 1 - (int)(blockIdx.x / nbh);
+    b = (blockIdx.x % nbh) / a.heads;
+    h = (blockIdx.x % nbh) % a.heads;
+    mr = (a.mask.bm > 1 ? b : 0) * a.mask.hm + (a.mask.hm > 1 ? h : 0);
+  }
+  const int bm = mr / a.mask.hm;
+  const int hm = mr % a.mask.hm;
   const int64_t mbase = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
   const uint8_t* crow = a.classes_q + ((int64_t)(bm * a.mask.hm + hm) * a.tq_q + qt) * a.tk_q;
 

@@ -146,17 +146,17 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   const int lr = l & 31;
   const int g = l >> 5;
 
-  // later query tiles first (under causal-like masks they see the most keys)
+  // Later query tiles first, heads interleaved: neighbouring workgroups work
+  // on nearby rows and share K tiles in L2 (this kernel is bound by memory
+  // traffic, so that beats ordering by length).
   const int nbh = a.batch * a.heads;
   const int qt = a.tq - 1 - (int)(blockIdx.x / nbh);
   const int bh = blockIdx.x % nbh;
   const int b = bh / a.heads;
   const int h = bh % a.heads;
-  const int bm = a.mask.bm > 1 ? b : 0;
-  const int hm = a.mask.hm > 1 ? h : 0;
-  const int mrow = bm * a.mask.hm + hm;
+  const int mrow = (a.mask.bm > 1 ? b : 0) * a.mask.hm + (a.mask.hm > 1 ? h : 0);
   const int rep_i = (a.mask.bm > 1 ? 0 : b) * (a.mask.hm > 1 ? 1 : a.heads) + (a.mask.hm > 1 ? 0 : h);
-  const int64_t total = a.plan[0];
+  const int64_t total = __builtin_amdgcn_readfirstlane(a.plan[0]);   // uniform
   const uint16_t* ds_rep = a.ds + (int64_t)rep_i * total * (BK * BQ);
   const uint8_t* ccol = a.classes_t + (int64_t)mrow * a.tk * a.tq + qt;   // stride tq over kt
   const int32_t* scol = a.slots + (int64_t)mrow * a.tk * a.tq + qt;

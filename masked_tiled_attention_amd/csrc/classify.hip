@@ -117,7 +117,72 @@ __global__ __launch_bounds__(256) void classify_map_kernel(ClassifyArgs a) {
     a.classes[((int64_t)bh * a.tq + qt) * a.tk + kt] = c;
 }
 
+// grid (rows): counts[r] = number of non-SKIP entries of class-map line r.
+__global__ __launch_bounds__(256) void order_count_kernel(OrderArgs a) {
+  const int r = blockIdx.x;
+  const uint8_t* line = a.classes + (int64_t)(r / a.inner) * a.outer_stride + (int64_t)(r % a.inner) * a.line_stride;
+  int c = 0;
+  for (int i = threadIdx.x; i < a.len; i += 256) c += line[i * a.elem_stride] != FM_TILE_SKIP;
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  __shared__ int red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) a.counts[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+// One workgroup of 1024: counting sort of the rows by count, descending, with
+// the counts grouped into at most 4096 buckets (order within a bucket is
+// arbitrary; only the launch order depends on it).
+constexpr int kOrderBuckets = 4096;
+__global__ __launch_bounds__(1024) void order_sort_kernel(OrderArgs a) {
+  __shared__ int hist[kOrderBuckets];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nb = min(a.len + 1, kOrderBuckets);
+  auto key = [&](int r) {   // descending count -> ascending key
+    return nb - 1 - (int)((int64_t)a.counts[r] * nb / ((int64_t)a.len + 1));
+  };
+  for (int i = tid; i < nb; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int r = tid; r < a.rows; r += 1024) atomicAdd(&hist[key(r)], 1);
+  __syncthreads();
+  // exclusive scan: thread t owns buckets 4t .. 4t+3
+  int v[4], s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = 4 * tid + i;
+    v[i] = b < nb ? hist[b] : 0;
+    s += v[i];
+  }
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int pre = incl - s;
+  for (int k = 0; k < wv; ++k) pre += wsum[k];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = 4 * tid + i;
+    if (b < nb) hist[b] = pre;
+    pre += v[i];
+  }
+  __syncthreads();
+  for (int r = tid; r < a.rows; r += 1024) a.order[atomicAdd(&hist[key(r)], 1)] = r;
+}
+
 }  // namespace
+
+hipError_t launch_order(const OrderArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(order_count_kernel, dim3(a.rows), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(order_sort_kernel, dim3(1), dim3(1024), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream) {
   dim3 grid(a.tk, a.mask.bm * a.mask.hm);

@@ -53,7 +53,24 @@ struct FwdArgs {
   MaskArgs mask;
   const uint8_t* classes;  // [bm][hm][tq][tk]
   int32_t tq, tk;
+  // Launch order: workgroup p takes class-map row order[p / rep] (mask row *
+  // tq + query tile), longest first, and (b, h) pair p % rep of that mask row.
+  const int32_t* order;
+  int32_t rep;             // (b, h) pairs per mask row
 };
+
+// Lines of a class map ordered by their non-SKIP count, descending. Line r
+// (r = mask row * inner + i) holds `len` entries starting at
+// (r / inner) * outer_stride + (r % inner) * line_stride, elem_stride apart:
+// rows of a [mr][inner][len] map or columns of a [mr][len][inner] map.
+struct OrderArgs {
+  const uint8_t* classes;
+  int32_t rows, len, inner;
+  int64_t outer_stride, line_stride, elem_stride;
+  int32_t* counts;         // [rows] non-SKIP entries per line
+  int32_t* order;          // [rows] line indices, longest first
+};
+hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
 
 struct BwdArgs {
   const void* q;
@@ -89,7 +106,17 @@ struct BwdArgs {
   uint16_t* ds;              // [rep][total][kBwdBlockK keys][kBwdBlockQ rows] bf16
   int64_t ds_capacity;       // bytes available at ds
   int32_t rep;               // (b, h) pairs per mask row
+  // Launch orders, longest first (see FwdArgs::order): key tiles of the dK/dV
+  // tiling and the recompute dQ kernel's query tiles (may be nullptr).
+  const int32_t* order_k;
+  const int32_t* order_qq;
 };
+
+// (b, h) of workgroup p given the mask row it serves (see FwdArgs::order).
+__device__ __forceinline__ void ordered_bh(int mr, int j, const MaskArgs& m, int heads, int* b, int* h) {
+  *b = m.bm > 1 ? mr / m.hm : j / (m.hm > 1 ? 1 : heads);
+  *h = m.hm > 1 ? mr % m.hm : j % heads;
+}
 
 hipError_t launch_bwd_plan(const BwdArgs& a, bool with_slots, hipStream_t stream);
 hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);

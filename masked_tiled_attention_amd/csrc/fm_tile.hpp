@@ -207,6 +207,15 @@ __device__ __forceinline__ void store_tile_rows(char* lds, const u32x4 (&r)[CHUN
   }
 }
 
+// A wavefront-uniform address moved into scalar registers (the direct loads
+// below take their base there); free when the compiler already keeps it so.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
 // Direct global -> LDS staging (gfx950 global_load_lds, 16 bytes per lane) of
 // a [ROWS][D] bf16 tile into the swizzled row-major layout, without passing
 // through registers. One wave instruction fills one contiguous KiB of LDS
@@ -278,7 +287,7 @@ struct DmaTile {
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, %2"
         :
-        : "s"(lds_dst), "v"(voff), "s"(base)
+        : "s"(lds_dst), "v"(voff), "s"(uniform_ptr(base))
         : "memory", "m0");
   }
   // The same with the non-temporal hint, for data read once (kept out of the
@@ -289,7 +298,7 @@ struct DmaTile {
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, %2 nt"
         :
-        : "s"(lds_dst), "v"(voff), "s"(base)
+        : "s"(lds_dst), "v"(voff), "s"(uniform_ptr(base))
         : "memory", "m0");
   }
 #pragma clang diagnostic pop
@@ -305,7 +314,7 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
       "s_nop 0\n\t"
       "global_load_lds_dword %1, %2"
       :
-      : "s"(lds_dst), "v"(voff), "s"(base)
+      : "s"(lds_dst), "v"(voff), "s"(uniform_ptr(base))
       : "memory", "m0");
 }
 #pragma clang diagnostic pop

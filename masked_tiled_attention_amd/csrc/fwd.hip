@@ -73,14 +73,16 @@ void fwd_kernel(FwdArgs a) {
   const int lr = l & 31;
   const int g = l >> 5;
 
-  // Heaviest query tiles first (for causal-like masks later rows see more keys).
-  const int nbh = a.batch * a.heads;
-  const int qt = a.tq - 1 - (int)(blockIdx.x / nbh);
-  const int bh = blockIdx.x % nbh;
-  const int b = bh / a.heads;
-  const int h = bh % a.heads;
-  const int bm = a.mask.bm > 1 ? b : 0;
-  const int hm = a.mask.hm > 1 ? h : 0;
+  // Query tiles longest first (order from the class map), then the (b, h)
+  // pairs that share the tile's mask row.
+  const int line = __builtin_amdgcn_readfirstlane(a.order[blockIdx.x / a.rep]);   // mask row * tq + query tile
+  const int j = blockIdx.x % a.rep;
+  const int qt = line % a.tq;
+  const int mr = line / a.tq;
+  const int bm = mr / a.mask.hm;
+  const int hm = mr % a.mask.hm;
+  const int b = a.mask.bm > 1 ? bm : j / (a.mask.hm > 1 ? 1 : a.heads);
+  const int h = a.mask.hm > 1 ? hm : j % a.heads;
   const int64_t mbase = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
   const uint8_t* crow = a.classes + ((int64_t)(bm * a.mask.hm + hm) * a.tq + qt) * a.tk;
 

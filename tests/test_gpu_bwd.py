@@ -188,8 +188,10 @@ def test_bwd_stored_ds_path_is_taken(gpu_lib):
         st = gpu_lib.fm_profile_end()
         times[short] = (st["bwd_dq"][0], st["bwd_dq_ds"][0])
     log(f"dQ kernel ms (recompute, stored dS): full workspace {times[0]}, one byte short {times[1]}")
-    assert times[0][0] < 0.2 * times[0][1]
-    assert times[1][1] < 0.2 * times[1][0]
+    # each dQ kernel takes several times longer when its path is the one taken
+    # (an exiting launch still costs a few microseconds)
+    assert times[0][0] < 0.3 * times[1][0]
+    assert times[1][1] < 0.3 * times[0][1]
 
 
 def test_bwd_stored_ds_short_workspace_falls_back(gpu_lib):
