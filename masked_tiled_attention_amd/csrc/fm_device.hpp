@@ -91,6 +91,17 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max / sum of x over the lane pair (l, l ^ 32), one v_permlane32_swap (no
+// LDS round trip). Both lanes of a pair get bit-identical results.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Map a linear workgroup index so that consecutive logical indices land on
 // the same XCD (workgroups are dispatched round-robin over the 8 XCDs).
 // Logical tiles that share K/V then share an L2.

@@ -107,13 +107,14 @@ __device__ __forceinline__ int compact_classes(const uint8_t* row, int first, in
 
 // As compact_classes(), but the list holds the FULL entries first and the
 // PARTIAL ones after them (each group ascending); *n_full receives the number
-// of FULL entries. With all_partial, every entry counts as PARTIAL.
-// sm_rank[i] receives list entry i's rank among all non-SKIP entries in
+// of FULL entries. With all_partial, every entry counts as PARTIAL; entry
+// partial_id (if not negative) counts as PARTIAL too. When sm_rank is not
+// null, sm_rank[i] receives list entry i's rank among all non-SKIP entries in
 // ascending order.
 template <int CAP, int NT>
 __device__ __forceinline__ int compact_classes_split(const uint8_t* row, int first, int count, uint32_t* sm_list,
                                                      uint16_t* sm_rank, int32_t* sm_scan, int tid,
-                                                     bool all_partial, int* n_full) {
+                                                     bool all_partial, int* n_full, int partial_id = -1) {
   constexpr int PER = CAP / NT;
   constexpr int NWAVE = NT / 64;
   const int lane = tid & 63, wave = tid >> 6;
@@ -123,7 +124,7 @@ __device__ __forceinline__ int compact_classes_split(const uint8_t* row, int fir
   for (int e = 0; e < PER; ++e) {
     const int idx = tid * PER + e;
     uint8_t c = idx < count ? row[first + idx] : (uint8_t)FM_TILE_SKIP;
-    if (all_partial && c == FM_TILE_FULL) c = FM_TILE_PARTIAL;
+    if ((all_partial || first + idx == partial_id) && c == FM_TILE_FULL) c = FM_TILE_PARTIAL;
     cls[e] = c;
     cf += c == FM_TILE_FULL;
     cp += c == FM_TILE_PARTIAL;
@@ -151,10 +152,12 @@ __device__ __forceinline__ int compact_classes_split(const uint8_t* row, int fir
   for (int e = 0; e < PER; ++e) {
     const uint32_t id = (uint32_t)(first + tid * PER + e);
     if (cls[e] == FM_TILE_FULL) {
-      sm_rank[pf] = (uint16_t)rank++;
+      if (sm_rank) sm_rank[pf] = (uint16_t)rank;
+      ++rank;
       sm_list[pf++] = id;
     } else if (cls[e] == FM_TILE_PARTIAL) {
-      sm_rank[pp] = (uint16_t)rank++;
+      if (sm_rank) sm_rank[pp] = (uint16_t)rank;
+      ++rank;
       sm_list[pp++] = id | kPartialBit;
     }
   }

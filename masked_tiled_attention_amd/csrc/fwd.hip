@@ -6,8 +6,9 @@
 //     statistics and partial output so that the result is normalised over
 //     the whole key sequence; no score matrix goes to HBM.
 //   - "Three ways to raise GPU utilization": less non-matmul work (the output
-//     is normalised once at the end, the running output is rescaled only
-//     when a row maximum grows by more than a factor 2^8, and the mask is
+//     is normalised once at the end; no per-tile row maximum: probabilities
+//     are formed against a reference that moves, with a rescale of the
+//     running output, only when one of them would exceed 2^8; the mask is
 //     evaluated only on PARTIAL tiles), work split over batch, heads and
 //     query tiles, and the query rows of a tile split among the wavefronts
 //     while K/V are shared.
@@ -26,9 +27,11 @@
 //         A = V^T read with ds_read_b64_tr_b16 from the row-major V tile, with
 //         the contraction index permuted identically on both sides.
 // K and V tiles are double-buffered in LDS; the next tile's global loads are
-// issued before the current tile's math.
+// issued before the current tile's math. Each 64-key tile runs as two 32-key
+// halves so that one half's softmax sits beside the other half's MFMAs.
 #include <climits>
 #include <cmath>
+#include <type_traits>
 
 #include "fm_device.hpp"
 #include "fm_internal.hpp"
@@ -47,6 +50,7 @@ constexpr int LIST_CAP = 1024;   // class bytes compacted per pass (4 per thread
 // smaller maximum (at most 2^kRescaleLog2, far from float overflow). O and the
 // row sum always share the same reference, so the result is unchanged.
 constexpr float kRescaleLog2 = 8.0f;
+constexpr float kRescaleMax = 256.0f;   // 2^kRescaleLog2
 
 template <int D>
 struct alignas(16) FwdSmem {
@@ -164,119 +168,140 @@ void fwd_kernel(FwdArgs a) {
       for (int j = 0; j < 4; ++j) sm.bnd[buf][j][tid] = rb[j];
     }
   };
-  auto masked_of = [&](uint32_t ent) {
-    return (ent & kPartialBit) || (ragged_k && (int)(ent & ~kPartialBit) == a.tk - 1);
+  // Interval mask on one 32-key half of a PARTIAL (or ragged) tile.
+  auto mask_half = [&](f32x16& sc, int nb, int buf) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int nl = nb * 32 + 8 * q4 + 4 * g;   // 4 consecutive keys
+      const i32x4 l0 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][0][nl]);
+      const i32x4 l1 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][1][nl]);
+      const i32x4 u0 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][2][nl]);
+      const i32x4 u1 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][3][nl]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool mk = ((l0[r] <= m) & (m < l1[r])) | ((u0[r] <= m) & (m < u1[r]));
+        sc[4 * q4 + r] = mk ? -INFINITY : sc[4 * q4 + r];
+      }
+    }
+  };
+
+  // Probabilities of one 32-key half against the current reference:
+  // p = 2^(C s + nmC), rounded to bf16 as the MFMA consumes them; returns the
+  // lane's sum of the same rounded values (two per v_dot2c), so O and l share
+  // one set of weights.
+  float nmC = INFINITY;   // -C * reference, or +inf while the row has no reference
+  u32x4 pf[NB][2];
+  auto soft_half = [&](const f32x16& sc, int nb) {
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(fmaf(sc[8 * t + 2 * j], C, nmC));
+        const float p1 = fast_exp2(fmaf(sc[8 * t + 2 * j + 1], C, nmC));
+        pf[nb][t][j] = pack_bf16(p0, p1);
+        if (j & 1) r1 = add_bf16_pair(pf[nb][t][j], r1);
+        else r0 = add_bf16_pair(pf[nb][t][j], r0);
+      }
+    return r0 + r1;
+  };
+  // The common path keeps the reference while every p of the half is at most
+  // 2^kRescaleLog2 (a lane sum within that bound implies it; a row without a
+  // reference yields inf or NaN here). Otherwise, wave-uniformly: the row
+  // maximum of the half, a move of the reference to it when it is larger,
+  // the rescale of O and l, and the half's probabilities again.
+  auto settle_half = [&](const f32x16& sc, int nb, float rs) {
+    if (__any(!(rs <= kRescaleMax))) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      mx = pair_max(mx);
+      const bool move = mx > m_run;   // false while both are -inf
+      const float alpha = move ? fast_exp2((m_run - mx) * C) : 1.f;   // 0 from -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+      m_run = move ? mx : m_run;
+      nmC = m_run == -INFINITY ? 0.f : -m_run * C;   // fully masked so far: p = 0
+      rs = soft_half(sc, nb);
+      if (m_run == -INFINITY) nmC = INFINITY;
+    }
+    l_run += rs;
   };
 
   int it_global = 0;   // iteration count across passes (selects the LDS buffer)
+  auto iteration = [&](auto masked_c, int it, int n_list, uint32_t& ent) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int buf = it_global & 1;
+    store_tile(buf, MASKED);
+    wait_vmem();
+    __syncthreads();   // tile `buf` complete and visible; the other buffer is free
+    if (it + 1 < n_list) {   // next tile's global loads overlap this tile's math
+      ent = __builtin_amdgcn_readfirstlane(sm.list[it + 1]);
+      load_tile((int)(ent & ~kPartialBit), (ent & kPartialBit) != 0, buf ^ 1);
+    }
+    const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
+    const char* vb = reinterpret_cast<const char*>(sm.v[buf]);
+    f32x16 sacc[NB];
+
+    // S^T = K Q^T, first 32 keys
+    sacc[0] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      sacc[0] = mfma32(*reinterpret_cast<const u32x4*>(kb + rm_byte<D>(lr, 16 * s + 8 * g)), qf[s], sacc[0]);
+    sched_lds_mfma<KSTEPS, 1, 4>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // S^T, second 32 keys, under the first half's mask and softmax
+    sacc[1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      sacc[1] = mfma32(*reinterpret_cast<const u32x4*>(kb + rm_byte<D>(32 + lr, 16 * s + 8 * g)), qf[s], sacc[1]);
+    if constexpr (MASKED) mask_half(sacc[0], 0, buf);
+    const float rs0 = soft_half(sacc[0], 0);
+    settle_half(sacc[0], 0, rs0);
+
+    // O^T += V^T P^T over the first 32 keys, under the second half's softmax
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 16 * t + 4 * g;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        oacc[cb] = mfma32(tr_operand<D>(vb, l, cb * 32, r0, r0 + 8), pf[0][t], oacc[cb]);
+    }
+    if constexpr (MASKED) mask_half(sacc[1], 1, buf);
+    const float rs1 = soft_half(sacc[1], 1);
+    settle_half(sacc[1], 1, rs1);
+
+    // O^T += V^T P^T over the second 32 keys
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 32 + 16 * t + 4 * g;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        oacc[cb] = mfma32(tr_operand<D>(vb, l, cb * 32, r0, r0 + 8), pf[1][t], oacc[cb]);
+    }
+    sched_lds_mfma<2 * CB, 2, 3>();
+  };
+
+  // FULL tiles first (no mask), then PARTIAL ones and the ragged last tile.
   for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
-    const int n_list = compact_classes<LIST_CAP, NT>(crow, kt0, min(LIST_CAP, a.tk - kt0), sm.list, sm.scan, tid);
+    int n_full;
+    const int n_list = compact_classes_split<LIST_CAP, NT>(crow, kt0, min(LIST_CAP, a.tk - kt0), sm.list, nullptr,
+                                                           sm.scan, tid, false, &n_full, ragged_k ? a.tk - 1 : -1);
     if (n_list == 0) continue;
 
-    uint32_t ent = sm.list[0];
-    load_tile((int)(ent & ~kPartialBit), masked_of(ent), it_global & 1);
-
-    for (int it = 0; it < n_list; ++it, ++it_global) {
-      const int buf = it_global & 1;
-      const bool masked_tile = masked_of(ent);
-      store_tile(buf, masked_tile);
-      wait_vmem();
-      __syncthreads();   // tile `buf` complete and visible; the other buffer is free
-      if (it + 1 < n_list) {   // next tile's global loads overlap this tile's math
-        ent = sm.list[it + 1];
-        load_tile((int)(ent & ~kPartialBit), masked_of(ent), buf ^ 1);
-      }
-      const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
-      const char* vb = reinterpret_cast<const char*>(sm.v[buf]);
-
-      // ---- S^T = K Q^T ----
-      f32x16 sacc[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        sacc[nb] = f32x16{};
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-          sacc[nb] = mfma32(*reinterpret_cast<const u32x4*>(kb + rm_byte<D>(nb * 32 + lr, 16 * s + 8 * g)), qf[s],
-                            sacc[nb]);
-      }
-      sched_lds_mfma<NB * KSTEPS, 1, 4>();
-
-      // ---- interval mask on PARTIAL (and ragged) tiles only ----
-      if (masked_tile) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int nl = nb * 32 + 8 * q4 + 4 * g;   // 4 consecutive keys
-            const i32x4 l0 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][0][nl]);
-            const i32x4 l1 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][1][nl]);
-            const i32x4 u0 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][2][nl]);
-            const i32x4 u1 = *reinterpret_cast<const i32x4*>(&sm.bnd[buf][3][nl]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const bool mk = ((l0[r] <= m) & (m < l1[r])) | ((u0[r] <= m) & (m < u1[r]));
-              sacc[nb][4 * q4 + r] = mk ? -INFINITY : sacc[nb][4 * q4 + r];
-            }
-          }
-        }
-      }
-
-      // ---- online softmax (per-lane row) ----
-      float mx = -INFINITY;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nb][i]);
-      mx = fmaxf(mx, xor32(mx));
-      const float m_cand = fmaxf(m_run, mx);
-      // move the reference when the maximum grew by more than 2^kRescaleLog2
-      // (also from -inf; a -inf to -inf step gives NaN > x == false: no move)
-      const bool move = (m_cand - m_run) * C > kRescaleLog2;
-      if (__any(move && m_run != -INFINITY)) {   // wave-uniform: some lane holds state to rescale
-        const float alpha = move ? fast_exp2((m_run - m_cand) * C) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
-      }
-      m_run = move ? m_cand : m_run;
-      const float mC = (m_run == -INFINITY ? 0.f : m_run) * C;
-      // P rounded to bf16 as the MFMA consumes it; the row sum adds the same
-      // rounded values (two per v_dot2c), so O and l share one set of weights.
-      u32x4 pf[NB][2];
-      float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p0 = fast_exp2(fmaf(sacc[nb][8 * t + 2 * j], C, -mC));
-            const float p1 = fast_exp2(fmaf(sacc[nb][8 * t + 2 * j + 1], C, -mC));
-            pf[nb][t][j] = pack_bf16(p0, p1);
-            if (j & 1) rs1 = add_bf16_pair(pf[nb][t][j], rs1);
-            else rs0 = add_bf16_pair(pf[nb][t][j], rs0);
-          }
-      l_run += rs0 + rs1;
-
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r0 = nb * 32 + 16 * t + 4 * g;   // first of this lane's 4-key groups
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb)
-            oacc[cb] = mfma32(tr_operand<D>(vb, l, cb * 32, r0, r0 + 8), pf[nb][t], oacc[cb]);
-        }
-      }
-      sched_lds_mfma<NB * 2 * CB, 2, 3>();
-    }
+    uint32_t ent = __builtin_amdgcn_readfirstlane(sm.list[0]);
+    load_tile((int)(ent & ~kPartialBit), (ent & kPartialBit) != 0, it_global & 1);
+    int it = 0;
+    for (; it < n_full; ++it, ++it_global) iteration(std::false_type{}, it, n_list, ent);
+    for (; it < n_list; ++it, ++it_global) iteration(std::true_type{}, it, n_list, ent);
   }
 
   // ---- epilogue: normalise once, write O and LSE ----
-  const float lt = l_run + xor32(l_run);
+  const float lt = pair_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (row_ok) {
     const int64_t ooff = (int64_t)b * a.o_sb + (int64_t)m * a.o_ss + (int64_t)h * a.o_sh;

@@ -164,3 +164,20 @@ def test_fwd_deterministic(gpu_lib):
     o2, l2 = gpu_lib.fm_attn_fwd(q, k, v, m, 0.1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("slope", [4.0, 40.0])
+def test_fwd_growing_scores(gpu_lib, slope):
+    """Scores that grow along the key axis (and a few late spikes), so the
+    running maximum moves in many tiles and in both halves of a tile: the
+    reference moves and rescales of O and l, checked against the oracle."""
+    n, d = 700, 128
+    g = torch.Generator().manual_seed(int(slope))
+    ramp = torch.linspace(0.0, slope, n)
+    q = (torch.ones(1, n, 2, d) + 0.3 * torch.randn(1, n, 2, d, generator=g)).to(torch.bfloat16)
+    k = (ramp[None, :, None, None] / math.sqrt(d) + 0.3 * torch.randn(1, n, 2, d, generator=g))
+    k[:, [333, 517, 690]] += 3.0 * slope / math.sqrt(d)
+    k = k.to(torch.bfloat16)
+    v = torch.randn(1, n, 2, d, generator=g).to(torch.bfloat16)
+    for name, vec in (("none", SM.no_mask(n, n)), ("causal", SM.causal(n))):
+        _compare_fwd(gpu_lib, q, k, v, tuple(x[None, None] for x in vec), 1 / math.sqrt(d), f"growing {name} s={slope}")
