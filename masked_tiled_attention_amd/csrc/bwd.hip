@@ -109,7 +109,7 @@ struct alignas(16) Smem {
   float dd[NBUF][BQ];            // D = rowsum(dO * O)
   uint32_t list[LIST_CAP];
   uint16_t rank[LIST_CAP];       // ascending rank of each list entry (stored-dS slot)
-  uint16_t dsx[NW][32 * BQ];     // per wavefront: its 32 keys' dS, regrouped for coalesced stores
+  uint16_t dsx[NW][32 * BQ];     // per wavefront: its 32 keys' dS, [key][column], regrouped for the stores
   int32_t scan[NW];
 };
 }  // namespace kv
@@ -365,27 +365,31 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 
         if (store_ds) {   // 4 stores per lane, counted by the wait above
-          // Through the wavefront's own LDS block (128-byte key rows, 16-byte
-          // chunk c at c ^ ((row >> 1) & 7), conflict-free both ways): lanes
-          // write their keys' chunks, then 8 lanes per row read whole rows,
-          // so each store writes 1 KiB of consecutive key rows. LDS accesses
-          // of one wavefront execute in order; no barrier is needed.
+          // The stored tile is 16 MFMA operand fragments of 1 KiB, fragment
+          // (rb, s) = columns 32 rb .. 32 rb + 31 x keys 16 s .. 16 s + 15,
+          // lane L's 16 bytes at L * 16 holding column 32 rb + L % 32 and keys
+          // 16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3 (h = L / 32), the order
+          // in which the dQ kernel's transposing K^T reads take the keys.
+          // The wavefront's 32 keys go through its own LDS block as a
+          // row-major [key][column] tile; transposing reads of it yield whole
+          // fragment lanes, so each store writes 1 KiB of consecutive bytes.
+          // LDS accesses of one wavefront execute in order; no barrier is needed.
           char* xb = reinterpret_cast<char*>(sm.dsx[w]);
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int ch = 4 * g + 2 * mb + t;
-              *reinterpret_cast<u32x4*>(xb + lr * 128 + 16 * (ch ^ ((lr >> 1) & 7))) = dsp[mb][t];
-            }
+            for (int t = 0; t < 2; ++t)
+              *reinterpret_cast<u32x4*>(xb + rm_byte<BQ>(lr, 8 * (4 * g + 2 * mb + t))) = dsp[mb][t];
           const int64_t slot = slot0 + pass_base + sm.rank[it];
-          uint16_t* wtile = ds_rep + slot * (BK * BQ) + (32 * w) * BQ;   // this wavefront's 32 key rows
+          char* tile = reinterpret_cast<char*>(ds_rep + slot * (BK * BQ));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 8 * i + (l >> 3), c = l & 7;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(xb + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
-            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(wtile + r * BQ + 8 * c));   // read once, later
-          }
+          for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+              const int r0 = 16 * sp + 4 * g;
+              const u32x4 x = tr_operand<BQ>(xb, l, 32 * rb, r0, r0 + 8);
+              __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(tile + (rb * 8 + 2 * w + sp) * 1024 + l * 16));
+            }
         }
       }
     };

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(BwdArgs a, int32_t nrow
 template <int D>
 struct alignas(16) DsSmem {
   uint16_t k[NBUF][BK * D];    // key tiles, row-major, swizzled
-  uint16_t ds[NBUF][BK * BQ];  // dS tiles [key][row], swizzled
+  uint16_t ds[NBUF][BK * BQ];  // dS tiles as stored: 16 MFMA operand fragments of 1 KiB
   uint32_t list[LIST_CAP];
   int32_t slot[LIST_CAP];      // stored-dS slot of each list entry
   int32_t scan[NW];
@@ -171,7 +171,6 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   const int64_t k_ld = a.k_ss * ES;
   const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
   using DmaK = DmaTile<D, BK, NT>;
-  using DmaS = DmaTile<BQ, BK, NT>;
   constexpr int NOFF = F32 ? KR : 1;
   uint32_t koff[NOFF];
   if constexpr (F32) {
@@ -179,8 +178,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   } else {
     koff[0] = DmaK::offset(k_ld, tid);
   }
-  const uint32_t soff = DmaS::offset(BQ * 2, tid);
-  constexpr int GROUP = (F32 ? 0 : DmaK::PER) + DmaS::PER;   // direct loads per tile and wavefront
+  constexpr int SPER = BK * BQ * 2 / 1024 / NW;                 // dS fragments per wavefront
+  constexpr int GROUP = (F32 ? 0 : DmaK::PER) + SPER;         // direct loads per tile and wavefront
+  const uint32_t sdst = lds_address(sm.ds) + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
   auto stage = [&](int idx, int buf) {   // list entry idx -> buffer buf
     const int kt = __builtin_amdgcn_readfirstlane((int)(sm.list[idx] & ~kPartialBit));   // uniform
     const int n0 = kt * BK;
@@ -192,8 +192,12 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
       DmaK::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff[0], k_ld, tid, a.seq_k - n0);
     }
     const int64_t slot = __builtin_amdgcn_readfirstlane(sm.slot[idx]);   // uniform
-    DmaS::template load<true>(reinterpret_cast<char*>(sm.ds[buf]), reinterpret_cast<const char*>(ds_rep + slot * (BK * BQ)), soff,
-               BQ * 2, tid, BK);
+    // the tile is copied as stored, fragment i * NW + w by this wavefront
+    const char* src = reinterpret_cast<const char*>(ds_rep + slot * (BK * BQ)) + w * 1024;
+    const uint32_t dst = sdst + (uint32_t)buf * (BK * BQ * 2);
+#pragma unroll
+    for (int i = 0; i < SPER; ++i)
+      DmaK::dma16_nt(src + i * NW * 1024, 16u * (uint32_t)l, dst + (uint32_t)(i * NW) * 1024u);
   };
 
   int it_global = 0;
@@ -216,8 +220,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
       const char* sb = reinterpret_cast<const char*>(sm.ds[buf]);
 
       // dQ^T (channels x rows) += K^T (channels x keys) dS^T (keys x rows),
-      // 16 keys per step; both operands read transposed with the same key
-      // order per lane half.
+      // 16 keys per step: K^T read transposed, dS^T as the stored fragment
+      // lane, both with the same key order per lane half.
 #pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
         const int r0 = 16 * s + 4 * g;
@@ -225,10 +229,10 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < BLK; ++j) {
           const int rb = CB == 4 ? j : (w >> 1);
-          acc[j] = mfma32(ka, tr_operand<BQ>(sb, l, 32 * rb, r0, r0 + 8), acc[j]);
+          acc[j] = mfma32(ka, *reinterpret_cast<const u32x4*>(sb + (rb * 8 + s) * 1024 + l * 16), acc[j]);
         }
       }
-      sched_lds_mfma<(BK / 16) * BLK, (2 + 2 * BLK) / BLK, 2>();
+      sched_lds_mfma<(BK / 16) * BLK, (2 + BLK) / BLK, 2>();
     }
   }
 
