@@ -16,6 +16,13 @@ the number of local rows whose global index is below x. Then local row r lies
 in [S', E') exactly when g_r lies in [S, E), so every interval maps to one
 contiguous local interval.
 
+Transfer set: the same page (contributions paragraph and "Key facts") pairs
+the overlap of computation and communication with dropping the transfers the
+mask makes useless; it gives no rule or granularity. The reading adopted: a
+rank needs key tile kt (keys [kt*Bc, min((kt+1)*Bc, Sk))) exactly when at
+least one of its rows attends at least one key of the tile, which the oracle
+takes from the dense mask over the rank's rows.
+
 Tile classes: the pages do not describe a tile pre-pass. The rule here is the
 reading adopted for it. Per K/V tile, the minimum and maximum of each bound
 vector over the tile's columns are reduced; a (Q tile, K tile) pair with rows
@@ -60,6 +67,28 @@ def localize(vectors, chunk_start, chunk_len):
         x = np.asarray(x, dtype=np.int64)
         out.append(np.searchsorted(rows, x, side="left").astype(np.int32))
     return tuple(out)
+
+
+def transfer_set(vectors, seq_q, seq_k, block_k):
+    """Mask-pruned K/V transfer set: uint8 [Bm, Hm, Tk], 1 where some row in
+    [0, seq_q) attends some key of tile kt (dense truth, row block by row
+    block). ``vectors`` are the rank's own (localized) vectors; a missing pair
+    hides nothing. Bm, Hm come from the vectors' shapes (1, 1 if all missing).
+    """
+    ref = next((np.asarray(x) for x in vectors if x is not None), None)
+    bm, hm = (1, 1) if ref is None else (ref.shape[0], ref.shape[1])
+    tk = -(-seq_k // block_k)
+    out = np.zeros((bm, hm, tk), dtype=np.uint8)
+    for b in range(bm):
+        for h in range(hm):
+            v = vectors_for(vectors, b, h)
+            open_key = np.zeros(seq_k, dtype=bool)
+            for r0 in range(0, seq_q, 4096):
+                rows = np.arange(r0, min(r0 + 4096, seq_q))
+                open_key |= ~dense_mask(*v, rows, seq_k).all(axis=0)
+            for t in range(tk):
+                out[b, h, t] = open_key[t * block_k:min((t + 1) * block_k, seq_k)].any()
+    return out
 
 
 def _canonical(vec, seq_q, n_keys):

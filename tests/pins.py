@@ -485,4 +485,97 @@ def pin_classes_exact_on_families():
                               OM.tile_classes_dense(loc, 128, 512, br, bc)), (br, bc)
 
 
+# ---------------------------------------------------------------------------
+# Mask-pruned K/V transfer set
+# ---------------------------------------------------------------------------
+
+def _tiles_of_keys(needed_keys, sk, bc):
+    tk = -(-sk // bc)
+    out = np.zeros(tk, dtype=np.uint8)
+    for j in np.flatnonzero(needed_keys):
+        out[j // bc] = 1
+    return out
+
+
+def pin_transfer_set_brute_force():
+    """Element-by-element loops on tiny random vectors (any int values, a
+    missing pair, broadcast shapes) against the oracle."""
+    rng = np.random.default_rng(131)
+    for it in range(40):
+        sq, sk = int(rng.integers(1, 12)), int(rng.integers(1, 20))
+        bc = int(rng.choice([1, 3, 4, 7]))
+        bm, hm = (1, 1) if it % 3 else (2, 3)
+        vec = [rng.integers(-4, sq + 5, (bm, hm, sk)) for _ in range(4)]
+        if it % 5 == 0:
+            vec[0] = vec[1] = None
+        got = OM.transfer_set(tuple(vec), sq, sk, bc)
+        tk = -(-sk // bc)
+        assert got.shape == (bm, hm, tk)
+        for b in range(bm):
+            for h in range(hm):
+                for t in range(tk):
+                    want = 0
+                    for j in range(t * bc, min((t + 1) * bc, sk)):
+                        for i in range(sq):
+                            lo = vec[0] is not None and vec[0][b, h, j] <= i < vec[1][b, h, j]
+                            up = vec[2][b, h, j] <= i < vec[3][b, h, j]
+                            if not (lo or up):
+                                want = 1
+                    assert got[b, h, t] == want, (it, b, h, t)
+
+
+def pin_transfer_set_closed_forms():
+    """The rank's rows R (dual-chunk assignment) and closed forms of the keys
+    they reach: causal, keys 0 .. max R; document-causal, per document the
+    keys from its start to its last row in R; sliding window W, keys j with
+    some row of R in [j, j + W); no mask, every key."""
+    n, bc = 96, 8
+    for degree, rank in ((2, 0), (2, 1), (4, 3), (3, 2)):
+        if n % (2 * degree):
+            continue
+        cs, cl = SM.dual_chunk(n, degree, rank)
+        rows = OM.local_rows(cs, cl)
+        sq = len(rows)
+        # causal
+        loc = OM.localize(_vec3(SM.causal(n)), cs, cl)
+        need = np.arange(n) <= rows.max()
+        assert np.array_equal(OM.transfer_set(loc, sq, n, bc)[0, 0], _tiles_of_keys(need, n, bc))
+        # document-causal
+        docs = [11, 30, 7, 26, 22]
+        starts = np.concatenate([[0], np.cumsum(docs)[:-1]])
+        loc = OM.localize(_vec3(SM.document_causal(docs)), cs, cl)
+        need = np.zeros(n, dtype=bool)
+        for s0, ln in zip(starts, docs):
+            mine = rows[(rows >= s0) & (rows < s0 + ln)]
+            if len(mine):
+                need[s0:mine.max() + 1] = True
+        assert np.array_equal(OM.transfer_set(loc, sq, n, bc)[0, 0], _tiles_of_keys(need, n, bc))
+        # sliding window
+        w = 13
+        loc = OM.localize(_vec3(SM.sliding_window_causal(n, w)), cs, cl)
+        need = np.array([np.any((rows >= j) & (rows < j + w)) for j in range(n)])
+        assert np.array_equal(OM.transfer_set(loc, sq, n, bc)[0, 0], _tiles_of_keys(need, n, bc))
+    # no mask
+    assert OM.transfer_set((None, None, None, None), 5, 37, 8).tolist() == [[[1] * 5]]
+
+
+def pin_transfer_set_matches_classes():
+    """Where the tile classes are exact (every mask family, and a localized
+    dual-chunk document mask), a key tile is needed exactly when some row
+    tile's class for it is not SKIP."""
+    for _, vec, _, n in _family_cases():
+        v3 = _vec3(vec)
+        for br, bc in ((4, 4), (8, 16), (16, 8)):
+            cls = OM.tile_classes(v3, n, n, br, bc)
+            assert np.array_equal(OM.transfer_set(v3, n, n, bc)[0, 0],
+                                  (cls != oracle.SKIP).any(axis=0).astype(np.uint8)), (br, bc)
+    docs = SM.lognormal_doc_lengths(np.random.default_rng(4), 512, 32, 1.0, 4, 256)
+    vec = _vec3(SM.document_causal(docs))
+    cs, cl = SM.dual_chunk(512, 4, 1)
+    loc = OM.localize(vec, cs, cl)
+    cls = OM.tile_classes(loc, 128, 512, 32, 16)
+    assert np.array_equal(OM.transfer_set(loc, 128, 512, 16)[0, 0],
+                          (cls != oracle.SKIP).any(axis=0).astype(np.uint8))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

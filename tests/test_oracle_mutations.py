@@ -157,7 +157,30 @@ def _classes_factory(variant):
     return tile_classes
 
 
+def _transfer_factory(variant):
+    def transfer_set(vectors, seq_q, seq_k, block_k):
+        ref = next((np.asarray(x) for x in vectors if x is not None), None)
+        bm, hm = (1, 1) if ref is None else (ref.shape[0], ref.shape[1])
+        tk = -(-seq_k // block_k)
+        out = np.zeros((bm, hm, tk), dtype=np.uint8)
+        for b in range(bm):
+            for h in range(hm):
+                v = OA.vectors_for(vectors, b, h)
+                m = OA.dense_mask(*v, np.arange(seq_q), seq_k)
+                if variant == "any_masked":
+                    key = m.any(axis=0)
+                else:
+                    key = ~m.all(axis=0)
+                for t in range(tk):
+                    hi = (t + 1) * block_k + (1 if variant == "tile_overlap" else 0)
+                    out[b, h, t] = key[t * block_k:min(hi, seq_k)].any()
+        return out
+    return transfer_set
+
+
 MUTATIONS = {
+    "transfer_any_masked": (OM, "transfer_set", _transfer_factory("any_masked")),
+    "transfer_tile_overlap": (OM, "transfer_set", _transfer_factory("tile_overlap")),
     "fwd_no_scale": (OA, "_rows_forward", _fwd_factory("no_scale")),
     "fwd_inverted_mask": (OA, "_rows_forward", _fwd_factory("inverted_mask")),
     "fwd_block_normalised": (OA, "_rows_forward", _fwd_factory("block_normalised")),
