@@ -81,6 +81,10 @@ class Runner:
             torch.cuda.synchronize()
             self.vectors = tuple(x.cpu().numpy() for x in (self.mask.lts, self.mask.lte,
                                                            self.mask.uts, self.mask.ute))
+            # the rank's mask-pruned K/V transfer set over the backward's key tiles
+            self.transfer_bk = fm.fm_kernel_tile(w.head_dim, True)[1]
+            need, count = fm.fm_kv_transfer_set(self.mask, w.seq_q, self.transfer_bk)
+            self.kv_tiles = (int(count.sum()), int(need.numel()))
         else:
             self.gmask = None
             self.mask = fm.Mask.from_vectors(w.vectors, dev)
@@ -103,6 +107,7 @@ class Runner:
         fm, w = self.fm, self.w
         if self.gmask is not None:
             self.mask = fm.fm_mask_localize(self.gmask, w.seq_q_global, w.chunk_start, w.chunk_len)
+            fm.fm_kv_transfer_set(self.mask, w.seq_q, self.transfer_bk)
         fm.fm_attn_fwd(self.q, self.k, self.v, self.mask, w.scale, o=self.o, lse=self.lse,
                        workspace=self.ws_f)
         if w.backward:
@@ -292,6 +297,8 @@ def main():
                 item["bwd_tflops"] = round(b / (bwd_x * 1e-3) / 1e12, 2)
             if wx.global_vectors is not None:
                 item["localize_ms"] = round(pf("localize"), 4)
+                item["transfer_set_ms"] = round(pf("transfer"), 4)
+                item["kv_tiles_needed"] = f"{rx.kv_tiles[0]} of {rx.kv_tiles[1]} ({rx.transfer_bk}-key tiles)"
             sweep.append(item)
             del rx
             torch.cuda.empty_cache()

@@ -200,6 +200,22 @@ fm_status fm_mask_localize(const fm_mask* global, int32_t seqlen_k, int32_t seql
                            const int32_t* chunk_start, const int32_t* chunk_len,
                            int32_t num_chunks, int32_t* const out[4], hipStream_t stream);
 
+/* Mask-pruned K/V transfer set of one context-parallel rank (FlashMask-3
+ * page, contributions paragraph and "Key facts": the overlap of computation
+ * with communication drops the transfers that the mask makes useless; the
+ * pages give no rule or granularity, the reading is stated here). `mask`
+ * holds the rank's own bound vectors (e.g. from fm_mask_localize) for its
+ * seqlen_q local rows. Key tile kt, keys [kt*block_k, min((kt+1)*block_k,
+ * seqlen_k)), is needed exactly when some row in [0, seqlen_q) is unmasked for
+ * some key of the tile; the test is exact for any bound values (it does not
+ * go through the tile classes, which are exact on the structural mask
+ * families and conservative otherwise). 1 <= block_k <= 2^30.
+ * Outputs (device): need uint8 [Bm][Hm][Tk], Tk = ceil(seqlen_k / block_k),
+ * 1 = needed, 0 = not; count int32 [Bm][Hm], the number of needed tiles per
+ * mask row (may be NULL). */
+fm_status fm_kv_transfer_set(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen_k, int32_t block_k,
+                             uint8_t* need, int32_t* count, hipStream_t stream);
+
 /* Per-kernel timing. Between fm_profile_begin and fm_profile_end the library
  * records a HIP event pair on the launch stream around each of its kernel
  * launches (at most max_launches pairs; later launches are not recorded).
@@ -217,7 +233,8 @@ typedef enum {
   FM_STAGE_BWD_PLAN = 7,    /* stored-dS slot plan (count, scan) */
   FM_STAGE_BWD_DQ_DS = 8,   /* dQ from stored dS */
   FM_STAGE_ORDER = 9,       /* launch orders, longest tiles first (count, sort) */
-  FM_NUM_STAGES = 10
+  FM_STAGE_TRANSFER = 10,   /* mask-pruned K/V transfer set */
+  FM_NUM_STAGES = 11
 } fm_stage;
 
 fm_status fm_profile_begin(int32_t max_launches);

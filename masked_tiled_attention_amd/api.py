@@ -227,6 +227,21 @@ def fm_mask_localize(mask: Mask, seq_q_global: int, chunk_start, chunk_len, stre
     return Mask(*out)
 
 
+def fm_kv_transfer_set(mask: Mask, seq_q: int, block_k: int, with_count: bool = True, stream=None):
+    """Mask-pruned K/V transfer set of a rank whose own (localized) vectors
+    are `mask`, over its seq_q rows: (need uint8 [Bm, Hm, Tk], count int32
+    [Bm, Hm] or None)."""
+    m = mask._c()
+    ref = mask.first()
+    bm, hm, sk = ref.shape
+    tk = -(-int(sk) // int(block_k))
+    need = torch.empty((bm, hm, tk), dtype=torch.uint8, device=ref.device)
+    count = torch.empty((bm, hm), dtype=torch.int32, device=ref.device) if with_count else None
+    L.check(L.load().fm_kv_transfer_set(C.byref(m), int(seq_q), int(sk), int(block_k), need.data_ptr(),
+                                        None if count is None else count.data_ptr(), _stream(stream)))
+    return need, count
+
+
 def fm_profile_begin(max_launches: int = 4096) -> None:
     L.check(L.load().fm_profile_begin(int(max_launches)))
 

@@ -523,6 +523,32 @@ fm_status fm_mask_localize(const fm_mask* global, int32_t seqlen_k, int32_t seql
   return FM_OK;
 }
 
+fm_status fm_kv_transfer_set(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen_k, int32_t block_k,
+                             uint8_t* need, int32_t* count, hipStream_t stream) {
+  fm::MaskArgs mk;
+  if (!mask) return fail(FM_ERR_INVALID_ARGUMENT, "mask is NULL");
+  fm_status st = check_mask(mask, mask->batch, mask->heads, &mk);
+  if (st != FM_OK) return st;
+  if (mask->batch < 1 || mask->heads < 1 || (int64_t)mask->batch * mask->heads > 65535)
+    return fail(FM_ERR_INVALID_ARGUMENT, "mask batch*heads must be in [1, 65535]");
+  if (seqlen_q < 1 || seqlen_q > kMaxSeq) return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_q out of range");
+  if (seqlen_k < 1 || seqlen_k > kMaxSeq) return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_k out of range");
+  if (block_k < 1 || block_k > (1 << 30)) return fail(FM_ERR_INVALID_ARGUMENT, "block_k must be in [1, 2^30]");
+  if (!need) return fail(FM_ERR_INVALID_ARGUMENT, "need is NULL");
+  if (count && reinterpret_cast<uintptr_t>(count) % 4) return fail(FM_ERR_INVALID_ARGUMENT, "count not 4-byte aligned");
+  fm::TransferArgs a{};
+  a.mask = mk;
+  a.seq_q = seqlen_q;
+  a.seq_k = seqlen_k;
+  a.block_k = block_k;
+  a.tk = (int32_t)ceil_div(seqlen_k, block_k);
+  a.need = need;
+  a.count = count;
+  hipError_t e = run_stage(FM_STAGE_TRANSFER, stream, [&] { return fm::launch_transfer_set(a, stream); });
+  if (e != hipSuccess) return hip_fail(e, "transfer set launch");
+  return FM_OK;
+}
+
 fm_status fm_profile_begin(int32_t max_launches) {
   if (max_launches < 1 || max_launches > (1 << 20))
     return fail(FM_ERR_INVALID_ARGUMENT, "max_launches must be in [1, 2^20]");

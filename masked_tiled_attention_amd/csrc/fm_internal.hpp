@@ -132,6 +132,13 @@ struct LocalizeArgs {
   int32_t* out[4];
 };
 
+struct TransferArgs {
+  MaskArgs mask;
+  int32_t seq_q, seq_k, block_k, tk;
+  uint8_t* need;           // [bm][hm][tk]
+  int32_t* count;          // [bm][hm] or null
+};
+
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream);
 hipError_t launch_classify_map(const ClassifyArgs& a, hipStream_t stream);
@@ -140,5 +147,6 @@ hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool f32, hipStream_t 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_localize(const LocalizeArgs& a, hipStream_t stream);
+hipError_t launch_transfer_set(const TransferArgs& a, hipStream_t stream);
 
 }  // namespace fm

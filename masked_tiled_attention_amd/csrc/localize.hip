@@ -43,7 +43,64 @@ __global__ __launch_bounds__(256) void localize_kernel(LocalizeArgs a) {
   }
 }
 
+// Mask-pruned K/V transfer set of one rank. Same page, contributions
+// paragraph and "Key facts": the overlap of computation with communication
+// drops the transfers that the mask makes useless. With the rank's (localized)
+// vectors, key j is needed when some row of [0, Sq) escapes both of its
+// intervals. The first open row is found by stepping from row 0 past an
+// interval that contains it; two passes over the two intervals suffice (once
+// the row has stepped past an interval it never re-enters it). A key tile is
+// needed when any of its keys is. Pure int32, exact for any bound values.
+__device__ __forceinline__ bool key_needed(int32_t n, int32_t a0, int32_t a1, int32_t b0, int32_t b1) {
+  int32_t r = 0;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (a0 <= r && r < a1) r = a1;
+    if (b0 <= r && r < b1) r = b1;
+  }
+  return r < n;
+}
+
+// grid (key tiles, bm * hm): one flag per key tile
+__global__ __launch_bounds__(256) void transfer_set_kernel(TransferArgs a) {
+  const int bh = blockIdx.y;
+  const int bm = bh / a.mask.hm, hm = bh % a.mask.hm;
+  const int64_t base = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
+  const int64_t j0 = (int64_t)blockIdx.x * a.block_k;
+  const int64_t j1 = min(j0 + a.block_k, (int64_t)a.seq_k);
+  bool any = false;
+  for (int64_t j = j0 + threadIdx.x; j < j1 && !any; j += 256) {
+    const int32_t a0 = a.mask.has_lower ? a.mask.lts[base + j] : 0;
+    const int32_t a1 = a.mask.has_lower ? a.mask.lte[base + j] : 0;
+    const int32_t b0 = a.mask.has_upper ? a.mask.uts[base + j] : 0;
+    const int32_t b1 = a.mask.has_upper ? a.mask.ute[base + j] : 0;
+    any = key_needed(a.seq_q, a0, a1, b0, b1);
+  }
+  any = __syncthreads_or(any);
+  if (threadIdx.x == 0) a.need[(int64_t)bh * a.tk + blockIdx.x] = any ? 1 : 0;
+}
+
+// grid (bm * hm): number of needed tiles per mask row
+__global__ __launch_bounds__(256) void transfer_count_kernel(TransferArgs a) {
+  const uint8_t* row = a.need + (int64_t)blockIdx.x * a.tk;
+  int c = 0;
+  for (int t = threadIdx.x; t < a.tk; t += 256) c += row[t];
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+  __shared__ int red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) a.count[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
 }  // namespace
+
+hipError_t launch_transfer_set(const TransferArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(transfer_set_kernel, dim3(a.tk, a.mask.bm * a.mask.hm), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.count) return e;
+  hipLaunchKernelGGL(transfer_count_kernel, dim3(a.mask.bm * a.mask.hm), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_localize(const LocalizeArgs& a, hipStream_t stream) {
   dim3 grid((a.seq_k + 255) / 256, a.mask.bm * a.mask.hm);

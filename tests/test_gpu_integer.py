@@ -152,3 +152,73 @@ def test_localize_dual_chunk_full_size(gpu_lib):
         _, cls = fm.fm_tile_classify(got, w.seq_q, w.seq_k, bq, bk)
         dense = OM.tile_classes_dense(ref, w.seq_q, w.seq_k, bq, bk)
         assert np.array_equal(cls.cpu().numpy()[0, 0], dense), "classes exact on the localized mask"
+
+
+def _check_transfer(vec, sq, sk, bk, fm, tag):
+    log(f"transfer set {tag} sq={sq} sk={sk} block_k={bk}")
+    need, count = fm.fm_kv_transfer_set(dev_mask(vec), sq, bk)
+    torch.cuda.synchronize()
+    ref = OM.transfer_set(vec, sq, sk, bk)
+    assert np.array_equal(need.cpu().numpy(), ref), f"need {tag}"
+    assert np.array_equal(count.cpu().numpy(), ref.sum(axis=2).astype(np.int32)), f"count {tag}"
+    return ref
+
+
+@pytest.mark.parametrize("n", [700, 64, 1])
+def test_transfer_set_mask_families(gpu_lib, n):
+    """Bit-exact need flags and counts on every mask family, for all rows and
+    for localized dual-chunk ranks, with kernel and odd key tiles."""
+    fm = gpu_lib
+    rng = np.random.default_rng(n + 1)
+    fams = _family_vectors(n, rng) if n > 8 else {"causal": SM.causal(n)}
+    for name, v in fams.items():
+        vec = tuple(x[None, None] for x in v)
+        for bk in sorted({fm.fm_kernel_tile(128, False)[1], fm.fm_kernel_tile(128, True)[1], 1, 7, 200}):
+            if bk > n:
+                continue
+            _check_transfer(vec, n, n, bk, fm, f"{name} all rows")
+        if n % 8 == 0:
+            for degree, rank in ((2, 1), (4, 0), (4, 3)):
+                cs, cl = SM.dual_chunk(n, degree, rank)
+                loc = OM.localize(vec, cs, cl)
+                _check_transfer(loc, int(sum(cl)), n, 16, fm, f"{name} rank {rank}/{degree}")
+
+
+def test_transfer_set_random_and_extreme(gpu_lib):
+    """Random and int32-limit bounds, broadcast shapes, a missing pair, one
+    key per tile and a single tile."""
+    fm = gpu_lib
+    rng = np.random.default_rng(29)
+    lo, hi = np.iinfo(np.int32).min, np.iinfo(np.int32).max
+    for trial in range(8):
+        sq, sk = int(rng.integers(1, 600)), int(rng.integers(1, 900))
+        bm, hm = int(rng.choice([1, 2])), int(rng.choice([1, 3]))
+        vec = [rng.integers(-50, sq + 50, (bm, hm, sk)).astype(np.int32) for _ in range(4)]
+        if trial % 2:
+            pick = np.array([lo, hi, 0, 1, sq - 1, sq, sq + 1, -1], np.int32)
+            vec = [rng.choice(pick, (bm, hm, sk)) for _ in range(4)]
+        if trial == 4:
+            vec[0] = vec[1] = None
+        if trial == 5:
+            vec[2] = vec[3] = None
+        for bk in (1, 64, sk):
+            _check_transfer(tuple(vec), sq, sk, bk, fm, f"random trial={trial}")
+
+
+def test_transfer_set_rank_share_full_size(gpu_lib):
+    """The context-parallel rank share (rank 3 of 8, dual-chunk, global 65536,
+    document-causal) at full size with the kernels' key tiles: bit-exact
+    against the dense truth, and equal to the OR of the exact tile classes."""
+    fm = gpu_lib
+    w = SC.build("c5_cp_rank3_of_8", 0, tensors=False)
+    loc = fm.fm_mask_localize(dev_mask(w.global_vectors), w.seq_q_global, w.chunk_start, w.chunk_len)
+    ref_loc = OM.localize(w.global_vectors, w.chunk_start, w.chunk_len)
+    for bwd in (False, True):
+        bq, bk = fm.fm_kernel_tile(128, bwd)
+        need, count = fm.fm_kv_transfer_set(loc, w.seq_q, bk)
+        ref = OM.transfer_set(ref_loc, w.seq_q, w.seq_k, bk)
+        assert np.array_equal(need.cpu().numpy(), ref)
+        assert int(count.cpu()[0, 0]) == int(ref.sum())
+        _, cls = fm.fm_tile_classify(loc, w.seq_q, w.seq_k, bq, bk)
+        assert np.array_equal(ref[0, 0], (cls.cpu().numpy()[0, 0] != 0).any(axis=0).astype(np.uint8))
+        log(f"rank share: {int(ref.sum())} of {ref.shape[2]} key tiles of {bk} keys needed")
