@@ -31,8 +31,15 @@ names and no API):
     A missing (None) pair is the empty interval.
   * softmax scale as given; LSE is the natural-log logsumexp of the scaled
     scores; a row with no open key has O = 0, LSE = -inf and zero gradients.
+  * grouped-query attention: "Современное состояние Flash Attention на ROCm"
+    (kripta.biz), ranking paragraph, names GQA among the features of the FA2
+    Triton backend without defining it. The usual reading is taken: k and v
+    may hold H_kv heads with H_kv dividing H; query head h uses K/V head
+    h // (H / H_kv) (groups of consecutive query heads), and a shared K/V
+    head's gradients are the sums over its group (the chain rule for a
+    shared input).
 
-Array conventions: q, o, do are [B, Sq, H, D]; k, v are [B, Sk, H, D]; each
+Array conventions: q, o, do are [B, Sq, H, D]; k, v are [B, Sk, H_kv, D]; each
 bound vector is an integer array [Bm, Hm, Sk] with Bm in {1, B} and Hm in
 {1, H} (size 1 broadcasts) or None. Inputs of any float dtype are upcast
 exactly to float64.
@@ -147,6 +154,13 @@ def _rows_forward(qrows, k, v, maskrows, scale):
     return o, lse
 
 
+def kv_head(q_heads, kv_heads, h):
+    """K/V head of query head h (grouped-query attention reading above)."""
+    if kv_heads < 1 or q_heads % kv_heads:
+        raise ValueError(f"{kv_heads} K/V heads do not divide {q_heads} query heads")
+    return h // (q_heads // kv_heads)
+
+
 def forward(q, k, v, vectors, scale, block=1024):
     """Masked attention forward. Returns O [B, Sq, H, D] and LSE [B, H, Sq]."""
     q = np.asarray(q, dtype=F64)
@@ -158,7 +172,8 @@ def forward(q, k, v, vectors, scale, block=1024):
     for b in range(B):
         for h in range(H):
             vec = vectors_for(vectors, b, h)
-            kb, vb = k[b, :, h], v[b, :, h]
+            hk = kv_head(H, k.shape[2], h)
+            kb, vb = k[b, :, hk], v[b, :, hk]
             for r0 in range(0, Sq, block):
                 rows = np.arange(r0, min(r0 + block, Sq))
                 ob, lb = _rows_forward(q[b, rows, h], kb, vb,
@@ -202,7 +217,8 @@ def backward(q, k, v, do, vectors, scale, block=1024):
     for b in range(B):
         for h in range(H):
             vec = vectors_for(vectors, b, h)
-            kb, vb = k[b, :, h], v[b, :, h]
+            hk = kv_head(H, k.shape[2], h)
+            kb, vb = k[b, :, hk], v[b, :, hk]
             for r0 in range(0, Sq, block):
                 rows = np.arange(r0, min(r0 + block, Sq))
                 p = _rows_probs(q[b, rows, h], kb, dense_mask(*vec, rows, kb.shape[0]), scale)
@@ -210,8 +226,8 @@ def backward(q, k, v, do, vectors, scale, block=1024):
                 dp = dob @ vb.T
                 ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
                 dq[b, rows, h] = scale * (ds @ kb)
-                dk[b, :, h] += scale * (ds.T @ q[b, rows, h])
-                dv[b, :, h] += p.T @ dob
+                dk[b, :, hk] += scale * (ds.T @ q[b, rows, h])
+                dv[b, :, hk] += p.T @ dob
     return dq, dk, dv
 
 
@@ -224,8 +240,9 @@ def forward_rows(q, k, v, vectors, scale, b, h, rows):
     """O [R, D] and LSE [R] for the listed query rows of (b, h)."""
     rows = np.asarray(rows, dtype=np.int64)
     vec = vectors_for(vectors, b, h)
-    kb = np.asarray(k[b, :, h], dtype=F64)
-    vb = np.asarray(v[b, :, h], dtype=F64)
+    hk = kv_head(q.shape[2], k.shape[2], h)
+    kb = np.asarray(k[b, :, hk], dtype=F64)
+    vb = np.asarray(v[b, :, hk], dtype=F64)
     qr = np.asarray(q[b, rows, h], dtype=F64)
     return _rows_forward(qr, kb, vb, dense_mask(*vec, rows, kb.shape[0]), scale)
 
@@ -234,8 +251,9 @@ def backward_rows(q, k, v, do, vectors, scale, b, h, rows):
     """dQ [R, D] for the listed query rows of (b, h)."""
     rows = np.asarray(rows, dtype=np.int64)
     vec = vectors_for(vectors, b, h)
-    kb = np.asarray(k[b, :, h], dtype=F64)
-    vb = np.asarray(v[b, :, h], dtype=F64)
+    hk = kv_head(q.shape[2], k.shape[2], h)
+    kb = np.asarray(k[b, :, hk], dtype=F64)
+    vb = np.asarray(v[b, :, hk], dtype=F64)
     p = _rows_probs(np.asarray(q[b, rows, h], dtype=F64), kb,
                     dense_mask(*vec, rows, kb.shape[0]), scale)
     dp = np.asarray(do[b, rows, h], dtype=F64) @ vb.T
@@ -244,7 +262,8 @@ def backward_rows(q, k, v, do, vectors, scale, b, h, rows):
 
 
 def backward_cols(q, k, v, do, vectors, scale, b, h, cols, block=512):
-    """dK [C, D] and dV [C, D] for the listed key columns of (b, h).
+    """Query head h's share of dK [C, D] and dV [C, D] for the listed key
+    columns of (b, h) (the whole of them without grouped K/V heads).
 
     Only the query rows that attend at least one listed key contribute; each
     such row's softmax is still taken over all of its keys.
@@ -252,8 +271,9 @@ def backward_cols(q, k, v, do, vectors, scale, b, h, cols, block=512):
     cols = np.asarray(cols, dtype=np.int64)
     vec = vectors_for(vectors, b, h)
     Sq = q.shape[1]
-    kb = np.asarray(k[b, :, h], dtype=F64)
-    vb = np.asarray(v[b, :, h], dtype=F64)
+    hk = kv_head(q.shape[2], k.shape[2], h)
+    kb = np.asarray(k[b, :, hk], dtype=F64)
+    vb = np.asarray(v[b, :, hk], dtype=F64)
     # rows touching the listed columns
     colvec = tuple(None if x is None else x[cols] for x in vec)
     touching = []

@@ -327,6 +327,44 @@ def pin_backward_autograd():
         _close(dv[0, :, 0], tv.grad[0, 0].numpy(), 1e-10, "autograd dV")
 
 
+def pin_gqa_autograd():
+    """Grouped K/V heads: O and the gradients equal torch float64 SDPA with
+    the K/V heads expanded by repeat_interleave (autograd sums the gradients
+    of a shared head over its group); per-head masks, 6 query heads on 2 and
+    on 1 K/V heads."""
+    rng = np.random.default_rng(67)
+    sq = sk = 40
+    d, H = 6, 6
+    fams = [SM.causal(sq), SM.sliding_window_causal(sq, 9), SM.prefix_lm(sq, 12),
+            SM.document_causal([9, 17, 14]), SM.no_mask(sq, sq),
+            tuple(rng.integers(-2, sq + 2, sk) for _ in range(4))]
+    vec = SM.stack([[fams[h] for h in range(H)]])
+    for hkv in (2, 1):
+        g = H // hkv
+        q, do = _rand((1, sq, H, d), 68), _rand((1, sq, H, d), 69)
+        k, v = _rand((1, sk, hkv, d), 70), _rand((1, sk, hkv, d), 71)
+        allowed = np.stack([~OA.dense_mask(*[np.asarray(x[0, h], np.int64) for x in vec], np.arange(sq), sk)
+                            for h in range(H)])
+        rows = allowed.any(axis=2)                 # [H, Sq]
+        for h in range(H):
+            do[0, ~rows[h], h] = 0.0
+        tq = torch.from_numpy(q[0].transpose(1, 0, 2).copy())[None].requires_grad_(True)
+        tk = torch.from_numpy(k[0].transpose(1, 0, 2).copy())[None].requires_grad_(True)
+        tv = torch.from_numpy(v[0].transpose(1, 0, 2).copy())[None].requires_grad_(True)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1),
+            attn_mask=torch.from_numpy(allowed)[None], scale=0.45)
+        o = torch.nan_to_num(o, nan=0.0)
+        (o * torch.from_numpy(do[0].transpose(1, 0, 2).copy())[None]).sum().backward()
+        oo, _ = OA.forward(q, k, v, vec, 0.45)
+        dq, dk, dv = OA.backward(q, k, v, do, vec, 0.45, block=16)
+        for h in range(H):
+            _close(oo[0, rows[h], h], o.detach()[0, h].numpy()[rows[h]], 1e-10, "GQA O")
+            _close(dq[0, rows[h], h], tq.grad[0, h].numpy()[rows[h]], 1e-10, "GQA dQ")
+        _close(dk[0].transpose(1, 0, 2), tk.grad[0].numpy(), 1e-10, "GQA dK")
+        _close(dv[0].transpose(1, 0, 2), tv.grad[0].numpy(), 1e-10, "GQA dV")
+
+
 def pin_backward_invariants():
     """Softmax is shift invariant, so sum_j dK_j = 0; and sum_j dV_j equals the
     sum of dO over rows with an open key."""

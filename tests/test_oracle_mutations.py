@@ -178,7 +178,12 @@ def _transfer_factory(variant):
     return transfer_set
 
 
+def _kv_head_mod(q_heads, kv_heads, h):
+    return h % kv_heads
+
+
 MUTATIONS = {
+    "gqa_head_modulo": (OA, "kv_head", _kv_head_mod),
     "transfer_any_masked": (OM, "transfer_set", _transfer_factory("any_masked")),
     "transfer_tile_overlap": (OM, "transfer_set", _transfer_factory("tile_overlap")),
     "fwd_no_scale": (OA, "_rows_forward", _fwd_factory("no_scale")),
