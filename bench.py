@@ -274,16 +274,21 @@ def main():
         sweep = []
         del r
         torch.cuda.empty_cache()
-        for name in SC.NAMES:
-            if name == args.workload:
-                continue
-            log(f"[bench] sweep {name}")
+        # the other workloads, then grouped-query attention on the prefix-LM
+        # workload (8 query heads on 2 K/V heads)
+        jobs = [(name, None) for name in SC.NAMES if name != args.workload] + [("c3b_prefix_lm_32k", 2)]
+        for name, kv_heads in jobs:
+            log(f"[bench] sweep {name}" + (f" with {kv_heads} K/V heads" if kv_heads else ""))
             wx = SC.build(name, args.seed)
+            if kv_heads:
+                wx.k = wx.k[:, :, :kv_heads].contiguous()
+                wx.v = wx.v[:, :, :kv_heads].contiguous()
             rx = Runner(fm, wx, torch, store_ds)
             msx, st = time_steps(rx, 5, 2, torch)
             a, b = rx.flops()
             pf = lambda s: st[s][0] / 5
-            item = {"workload": name, "nnz": rx.nnz, "ms_per_step": round(msx, 4),
+            item = {"workload": name + (f" ({wx.heads} query heads on {kv_heads} K/V heads)" if kv_heads else ""),
+                    "nnz": rx.nnz, "ms_per_step": round(msx, 4),
                     "tflops": round((a + b) / (msx * 1e-3) / 1e12, 2),
                     "fwd_kernel_tflops": round(a / (pf("fwd") * 1e-3) / 1e12, 2)}
             if wx.backward:

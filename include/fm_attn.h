@@ -39,8 +39,14 @@
  *     FM_ERR_HIP, which reports a HIP error raised by a launch. The message
  *     of the last failure on the calling thread is fm_last_error().
  *   - Tensor layout: Q, O, dO, dQ are [B, Sq, H, D] and K, V, dK, dV are
- *     [B, Sk, H, D], addressed by (b, s, h) element strides with the head
+ *     [B, Sk, H_kv, D], addressed by (b, s, h) element strides with the head
  *     dimension D contiguous. LSE is [B, H, Sq] float32, contiguous.
+ *   - Grouped-query attention ("Современное состояние Flash Attention на
+ *     ROCm", kripta.biz, ranking paragraph, names GQA as a feature of the
+ *     FA2 Triton backend; the usual reading is taken): H_kv divides H, query
+ *     head h uses K/V head h / (H / H_kv), and dK, dV of a K/V head are the
+ *     sums over the query heads of its group. H_kv = H is plain multi-head
+ *     attention, H_kv = 1 multi-query attention.
  *   - Mask vectors are int32 [Bm, Hm, Sk] with the key axis contiguous and
  *     element strides (stride_b, stride_h); Bm in {1, B}, Hm in {1, H}; a
  *     size of 1 broadcasts over batch / heads.
@@ -105,9 +111,10 @@ typedef struct {
   fm_dtype dtype;
   float softmax_scale;   /* > 0 and finite, e.g. 1/sqrt(D) */
   int64_t q_stride[3];
-  int64_t k_stride[3];
-  int64_t v_stride[3];
+  int64_t k_stride[3];   /* of K and dK, whose head axis has H_kv entries */
+  int64_t v_stride[3];   /* of V and dV */
   int64_t o_stride[3];
+  int32_t heads_kv;      /* H_kv: 0 (meaning H) or a divisor of H */
 } fm_problem;
 
 /* Tile sizes (rows of Q, columns of K) used by the forward (bwd = 0) or the

@@ -37,7 +37,7 @@ class fm_problem(C.Structure):
                 ("seqlen_k", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32),
                 ("softmax_scale", C.c_float),
                 ("q_stride", C.c_int64 * 3), ("k_stride", C.c_int64 * 3),
-                ("v_stride", C.c_int64 * 3), ("o_stride", C.c_int64 * 3)]
+                ("v_stride", C.c_int64 * 3), ("o_stride", C.c_int64 * 3), ("heads_kv", C.c_int32)]
 
 
 class FmError(RuntimeError):

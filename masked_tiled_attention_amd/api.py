@@ -5,8 +5,9 @@ their pointers and strides are handed to the C ABI, and outputs / workspace
 are allocated with torch (device memory and streams are torch's job here).
 Every step of the computation runs in the HIP kernels.
 
-Layout: q, o, do, dq are [B, Sq, H, D]; k, v, dk, dv are [B, Sk, H, D]; the
-last dimension must be contiguous. lse is [B, H, Sq] float32. Mask vectors are
+Layout: q, o, do, dq are [B, Sq, H, D]; k, v, dk, dv are [B, Sk, H_kv, D]
+with H_kv dividing H (grouped-query attention when H_kv < H); the last
+dimension must be contiguous. lse is [B, H, Sq] float32. Mask vectors are
 int32 [Bm, Hm, Sk] with the key axis contiguous (see ``Mask``).
 """
 from __future__ import annotations
@@ -93,14 +94,16 @@ def _problem(q, k, v, o, scale) -> L.fm_problem:
     if q.dtype not in _DTYPES or any(t.dtype != q.dtype for t in (k, v, o)):
         raise ValueError("q, k, v, o must share dtype bfloat16 or float32")
     B, Sq, H, D = q.shape
-    Sk = k.shape[1]
-    if k.shape != (B, Sk, H, D) or v.shape != (B, Sk, H, D) or o.shape != (B, Sq, H, D):
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Sk, Hkv, D) or v.shape != (B, Sk, Hkv, D) or o.shape != (B, Sq, H, D):
         raise ValueError("shape mismatch between q, k, v, o")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{Hkv} K/V heads do not divide {H} query heads")
     if scale is None:
         scale = D ** -0.5
     st = lambda t: (C.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
     return L.fm_problem(B, H, Sq, Sk, D, _DTYPES[q.dtype], float(scale),
-                        st(q), st(k), st(v), st(o))
+                        st(q), st(k), st(v), st(o), Hkv)
 
 
 def fm_kernel_tile(head_dim: int, bwd: bool = False):

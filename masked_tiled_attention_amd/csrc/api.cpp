@@ -101,6 +101,8 @@ fm_status check_problem(const fm_problem* p) {
     return fail(FM_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)p->dtype);
   if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale))
     return fail(FM_ERR_INVALID_ARGUMENT, "softmax_scale must be positive and finite");
+  if (p->heads_kv < 0 || (p->heads_kv > 0 && p->heads % p->heads_kv))
+    return fail(FM_ERR_INVALID_ARGUMENT, "heads_kv %d must be 0 or divide heads %d", p->heads_kv, p->heads);
   const int64_t es = p->dtype == FM_BF16 ? 2 : 4;
   const int64_t* st[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
   const char* nm[4] = {"q", "k", "v", "o"};
@@ -144,6 +146,8 @@ struct Layout {
 };
 
 int64_t padded_rows(int64_t sq) { return ceil_div(sq, 128) * 128; }
+
+int32_t kv_heads(const fm_problem* p) { return p->heads_kv > 0 ? p->heads_kv : p->heads; }
 
 Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
   Layout L;
@@ -250,6 +254,8 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   a.o_sb = p->o_stride[0]; a.o_ss = p->o_stride[1]; a.o_sh = p->o_stride[2];
   a.batch = p->batch;
   a.heads = p->heads;
+  a.heads_kv = kv_heads(p);
+  a.group = p->heads / a.heads_kv;
   a.seq_q = p->seqlen_q;
   a.seq_k = p->seqlen_k;
   a.scale = p->softmax_scale;
@@ -265,30 +271,37 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   a.row_off = reinterpret_cast<int32_t*>(w + L.row_off);
   a.plan = reinterpret_cast<int32_t*>(w + L.plan);
   a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
-  // launch orders: key-tile rows of the transposed dK/dV map and the
-  // query-tile rows of the recompute dQ map
+  a.rep_kv = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : a.heads_kv);
+  // launch orders: key-tile rows of the transposed dK/dV map (one line per
+  // K/V mask row and key tile, counting the class rows of the K/V head's
+  // query heads when the mask has a row per head) and the query-tile rows of
+  // the recompute dQ map
   const int64_t mrows = (int64_t)mk.bm * mk.hm;
-  auto order = [&](size_t at, const uint8_t* cls, int64_t lines_per_mr, int64_t len, int64_t outer, int64_t line,
-                   int64_t elem) -> const int32_t* {
+  auto order = [&](size_t at, const uint8_t* cls, int64_t nrows, int64_t lines_per_mr, int64_t len, int64_t outer,
+                   int64_t line, int64_t elem, int32_t group, int64_t group_stride) -> const int32_t* {
     fm::OrderArgs o{};
     o.classes = cls;
-    o.rows = (int32_t)(mrows * lines_per_mr);
+    o.rows = (int32_t)(nrows * lines_per_mr);
     o.len = (int32_t)len;
     o.inner = (int32_t)lines_per_mr;
     o.outer_stride = outer;
     o.line_stride = line;
     o.elem_stride = elem;
+    o.group = group;
+    o.group_stride = group_stride;
     o.counts = reinterpret_cast<int32_t*>(w + at);
     o.order = o.counts + o.rows;
     if (run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_order(o, stream); }) != hipSuccess) return nullptr;
     return o.order;
   };
-  a.order_k = order(L.order_k, classes_t, tk, tq, (int64_t)tk * tq, tq, 1);
+  const int32_t kv_group = mk.hm > 1 ? a.group : 1;   // class rows per K/V mask row
+  a.order_k = order(L.order_k, classes_t, (int64_t)mk.bm * (mk.hm > 1 ? a.heads_kv : 1), tk, tq,
+                    (int64_t)kv_group * tk * tq, tq, 1, kv_group, (int64_t)tk * tq);
   if (!a.order_k) return hip_fail(hipGetLastError(), "backward order launch");
   // the recompute dQ kernel's order only when its path is certain (the
   // workspace cannot hold the stored-dS slot map); else it keeps the default
   if (ws_bytes < L.ds) {
-    a.order_qq = order(L.order_qq, classes_q, tq_q, tk_q, (int64_t)tq_q * tk_q, tk_q, 1);
+    a.order_qq = order(L.order_qq, classes_q, mrows, tq_q, tk_q, (int64_t)tq_q * tk_q, tk_q, 1, 1, 0);
     if (!a.order_qq) return hip_fail(hipGetLastError(), "backward order launch");
   }
   *lay = L;
@@ -394,12 +407,14 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   oa.outer_stride = (int64_t)tq * tk;
   oa.line_stride = tk;
   oa.elem_stride = 1;
+  oa.group = 1;
   oa.counts = reinterpret_cast<int32_t*>(w + L.counts);
   oa.order = reinterpret_cast<int32_t*>(w + L.order);
   hipError_t e = run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_order(oa, stream); });
   if (e != hipSuccess) return hip_fail(e, "forward order launch");
   a.order = oa.order;
   a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
+  a.group = p->heads / kv_heads(p);
   e = run_stage(FM_STAGE_FWD, stream,
                            [&] { return fm::launch_fwd(a, p->head_dim, p->dtype == FM_FP32, stream); });
   if (e != hipSuccess) return hip_fail(e, "forward launch");

@@ -114,7 +114,9 @@ struct alignas(16) Smem {
 };
 }  // namespace kv
 
-template <int D, bool F32>
+// GROUPED: more than one query head per K/V head (the head loop runs
+// a.group times); without it the loop has one trip and folds away.
+template <int D, bool F32, bool GROUPED>
 __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   using namespace kv;
   constexpr int KSTEPS = D / 16;
@@ -128,16 +130,19 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const int lr = l & 31;
   const int g = l >> 5;
 
-  // Key tiles longest first, then the (b, h) pairs sharing the mask row.
-  const int line = __builtin_amdgcn_readfirstlane(a.order_k[blockIdx.x / a.rep]);   // mask row * tk + key tile
-  const int kt = line % a.tk;
-  const int mr = line / a.tk;
-  int b, h;
-  ordered_bh(mr, blockIdx.x % a.rep, a.mask, a.heads, &b, &h);
-  const int bm = mr / a.mask.hm;
-  const int hm = mr % a.mask.hm;
-  const int64_t mbase = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
-  const uint8_t* ccol = a.classes_t + ((int64_t)(bm * a.mask.hm + hm) * a.tk + kt) * a.tq;
+  // Key tiles longest first, then the (b, K/V head) pairs sharing the K/V
+  // mask row; the workgroup runs the `group` query heads of its K/V head one
+  // after the other, with dK, dV accumulating over all of them.
+  const int line = __builtin_amdgcn_readfirstlane(a.order_k[blockIdx.x / a.rep_kv]);   // K/V mask row * tk + key tile
+  // (integer divisions by launch constants expand to vector code: the results
+  // are taken back to scalar registers so that the addresses stay scalar)
+  const int kt = __builtin_amdgcn_readfirstlane(line % a.tk);
+  const int kr = __builtin_amdgcn_readfirstlane(line / a.tk);
+  const int hkm = a.mask.hm > 1 ? a.heads_kv : 1;   // K/V mask rows per batch row
+  const int jr = __builtin_amdgcn_readfirstlane(blockIdx.x % a.rep_kv);
+  const int b = __builtin_amdgcn_readfirstlane(a.mask.bm > 1 ? kr / hkm : jr / (a.mask.hm > 1 ? 1 : a.heads_kv));
+  const int hk = __builtin_amdgcn_readfirstlane(a.mask.hm > 1 ? kr % hkm : jr % a.heads_kv);
+  const int bm = __builtin_amdgcn_readfirstlane(kr / hkm);
 
   const int n = kt * BK + 32 * w + lr;   // this lane's key
   const bool key_ok = n < a.seq_k;
@@ -147,44 +152,26 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   u32x4 kf[KSTEPS], vf[KSTEPS];
   {
     const int nk = min(n, a.seq_k - 1);
-    const int64_t koff = (int64_t)b * a.k_sb + (int64_t)nk * a.k_ss + (int64_t)h * a.k_sh + 8 * g;
-    const int64_t voff = (int64_t)b * a.v_sb + (int64_t)nk * a.v_ss + (int64_t)h * a.v_sh + 8 * g;
+    const int64_t koff = (int64_t)b * a.k_sb + (int64_t)nk * a.k_ss + (int64_t)hk * a.k_sh + 8 * g;
+    const int64_t voff = (int64_t)b * a.v_sb + (int64_t)nk * a.v_ss + (int64_t)hk * a.v_sh + 8 * g;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       kf[s] = load8_as_bf16<F32>(a.k, koff + 16 * s);
       vf[s] = load8_as_bf16<F32>(a.v, voff + 16 * s);
     }
   }
-  // The lane's key bounds (keys past the end are masked for every row).
-  int32_t b_lts = INT_MIN, b_lte = INT_MAX, b_uts = 0, b_ute = 0;
-  if (key_ok) {
-    b_lts = a.mask.has_lower ? a.mask.lts[mbase + n] : a.seq_q;
-    b_lte = a.mask.has_lower ? a.mask.lte[mbase + n] : a.seq_q;
-    b_uts = a.mask.has_upper ? a.mask.uts[mbase + n] : 0;
-    b_ute = a.mask.has_upper ? a.mask.ute[mbase + n] : 0;
-  }
-  // Interval widths (0 for empty intervals): row mm is masked by [s, e) iff
-  // (uint)(mm - s) < width, exact for every int32 s, e.
-  const uint32_t b_lw = b_lte > b_lts ? (uint32_t)b_lte - (uint32_t)b_lts : 0u;
-  const uint32_t b_uw = b_ute > b_uts ? (uint32_t)b_ute - (uint32_t)b_uts : 0u;
   const bool ragged_k = (a.seq_k % BK) != 0 && kt == a.tk - 1;
-
-  // Stored dS: when the plan enables it, every processed tile's bf16 dS goes
-  // to slot row_off[mask row][kt] + (rank of its query tile among this key
-  // tile's non-SKIP ones), as [key][column] with the tile's BK keys and BQ
-  // columns. Column c = 32 g + 16 mb + 8 t + j holds row
-  // 32 mb + 16 t + 4 g + (j < 4 ? j : j + 4): the eight rows that one lane
-  // packs for one (mb, t) sit in 16 contiguous bytes.
   const bool store_ds = a.plan != nullptr && a.plan[1] != 0;
-  const int mrow = bm * a.mask.hm + hm;
-  int64_t slot0 = 0;
-  uint16_t* ds_rep = nullptr;
-  if (store_ds) {
-    const int rep_i = (a.mask.bm > 1 ? 0 : b) * (a.mask.hm > 1 ? 1 : a.heads) + (a.mask.hm > 1 ? 0 : h);
-    slot0 = a.row_off[(int64_t)mrow * a.tk + kt];
-    ds_rep = a.ds + (int64_t)rep_i * a.plan[0] * (BK * BQ);
-  }
 
+  // Per query head (set at the start of each head): the lane's key bounds
+  // and interval widths, the class column, the stored-dS slot base and
+  // stream, the LSE / D rows and the Q / dO bases.
+  int h = 0;
+  uint32_t b_lw = 0, b_uw = 0;
+  int32_t b_lts = 0, b_uts = 0;
+  const uint8_t* ccol = nullptr;
+  int64_t slot0 = 0, lrow = 0;
+  uint16_t* ds_rep = nullptr;
   f32x16 dvacc[CB], dkacc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
@@ -192,7 +179,6 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     dkacc[cb] = f32x16{};
   }
   const float C = a.scale_log2;
-  const int64_t lrow = ((int64_t)b * a.heads + h) * a.seq_pad;
 
   // ---- query tile staging ----
   // Q and dO (bf16) and the rows' LSE*log2(e) and D go straight from global
@@ -201,8 +187,8 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   // the end re-read the last row; their LSE*log2(e) is +inf, so P = dS = 0.
   constexpr int ES = F32 ? 4 : 2;
   const int64_t q_ld = a.q_ss * ES, o_ld = a.o_ss * ES;
-  const char* qbh = reinterpret_cast<const char*>(a.q) + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ES;
-  const char* dbh = reinterpret_cast<const char*>(a.dout) + ((int64_t)b * a.o_sb + (int64_t)h * a.o_sh) * ES;
+  const char* qbh = nullptr;
+  const char* dbh = nullptr;
   using Dma = DmaTile<D, BQ, NT>;
   constexpr int NOFF = F32 ? QR : 1;
   uint32_t qoff[NOFF], doff[NOFF];
@@ -233,175 +219,211 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     else if (wu == 1) dma4(a.drow + lrow + m0, 4u * (uint32_t)l, lds_address(sm.dd[buf]));
   };
 
-  int it_global = 0;
-  for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
-    int n_full;
-    const int n_list = compact_classes_split<LIST_CAP, NT>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.rank,
-                                                           sm.scan, tid, ragged_k, &n_full);
-    if (n_list == 0) continue;
-    const int pass_base = it_global;   // non-SKIP tiles in earlier passes
-
-    stage_q((int)(sm.list[0] & ~kPartialBit), it_global % NBUF);
-    if (n_list > 1) stage_q((int)(sm.list[1] & ~kPartialBit), (it_global + 1) % NBUF);
-
-    // FULL tiles first, then PARTIAL ones, each with its own straight-line
-    // body (one branch-free basic block per query tile).
-    auto iteration = [&](auto masked_c, int it) {
-      constexpr bool MASKED = decltype(masked_c)::value;
-      const int buf = it_global % NBUF;
-      const int qt = (int)(sm.list[it] & ~kPartialBit);
-      const int m0 = qt * BQ;
-      // This tile's loads done. Younger vector-memory operations that may stay
-      // in flight: the next tile's loads and the dS stores of the last two
-      // iterations of this pass (vmcnt counts stores too).
-      wait_vmem_upto((it + 1 < n_list ? GROUP + (wu < 2 ? 1 : 0) : 0) + (store_ds ? 4 * min(it, 2) : 0));
-      __syncthreads();   // tile `buf` visible to all; the buffer read last iteration is free
-      if (it + 2 < n_list) stage_q((int)(sm.list[it + 2] & ~kPartialBit), (it_global + 2) % NBUF);
-      const char* qb = reinterpret_cast<const char*>(sm.q[buf]);
-      const char* db = reinterpret_cast<const char*>(sm.dout[buf]);
-
-      // One 64-row query tile as two 32-row halves (A: rows 0-31, B: 32-63),
-      // ordered so that each half's elementwise work runs beside the other
-      // half's matrix products (the MFMA unit works while the same wavefront
-      // issues independent VALU instructions):
-      //   S,dP(A) | S,dP(B) + P,dS(A) | dV,dK(A) + P,dS(B) | dV,dK(B)
-      {
-        f32x16 sacc[2], dpacc[2];
-        u32x4 pp[2][2], dsp[2][2];
-        // S = Q K^T and dP = dO V^T (lane = key, registers = query rows)
-        auto sdp = [&](int mb) {
-          sacc[mb] = f32x16{};
-          dpacc[mb] = f32x16{};
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            const int off = rm_byte<D>(32 * mb + lr, 16 * s + 8 * g);
-            sacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(qb + off), kf[s], sacc[mb]);
-            dpacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(db + off), vf[s], dpacc[mb]);
-          }
-        };
-        // P = exp2(S * scale * log2(e) - LSE * log2(e)), dS = P (dP - D),
-        // both rounded to bf16 MFMA operands
-        auto softmax = [&](int mb) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int ml = 32 * mb + 8 * q4 + 4 * g;
-            const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
-            const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = 4 * q4 + r;
-              float p = fast_exp2(fmaf(sacc[mb][i], C, -l2[r]));
-              if constexpr (MASKED) {
-                const int mm = m0 + ml + r;
-                const bool mk = ((uint32_t)(mm - b_lts) < b_lw) | ((uint32_t)(mm - b_uts) < b_uw);
-                p = mk ? 0.f : p;
-              }
-              sacc[mb][i] = p;
-              dpacc[mb][i] = p * (dpacc[mb][i] - dd[r]);
-            }
-          }
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              pp[mb][t][j] = pack_bf16(sacc[mb][8 * t + 2 * j], sacc[mb][8 * t + 2 * j + 1]);
-              dsp[mb][t][j] = pack_bf16(dpacc[mb][8 * t + 2 * j], dpacc[mb][8 * t + 2 * j + 1]);
-            }
-        };
-        // dV^T += dO^T P, dK^T += Q^T dS (contraction over the half's rows)
-        auto dvdk = [&](int mb) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int r0 = 32 * mb + 16 * t + 4 * g;
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-              dvacc[cb] = mfma32(tr_operand<D>(db, l, 32 * cb, r0, r0 + 8), pp[mb][t], dvacc[cb]);
-              dkacc[cb] = mfma32(tr_operand<D>(qb, l, 32 * cb, r0, r0 + 8), dsp[mb][t], dkacc[cb]);
-            }
-          }
-        };
-        // Four scheduling regions; in each, operand reads run ahead of their
-        // MFMAs and the other half's elementwise work sits between MFMAs.
-        sdp(0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int j = 0; j < 2 * KSTEPS - 4; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_barrier(0);
-
-        sdp(1);
-        softmax(0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int j = 0; j < 2 * KSTEPS; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 9 : 6, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        dvdk(0);
-        softmax(1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int j = 0; j < 4 * CB; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 9 : 6, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-
-        dvdk(1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int j = 0; j < 4 * CB - 3; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-        __builtin_amdgcn_sched_barrier(0);
-
-        if (store_ds) {   // 4 stores per lane, counted by the wait above
-          // The stored tile is 16 MFMA operand fragments of 1 KiB, fragment
-          // (rb, s) = columns 32 rb .. 32 rb + 31 x keys 16 s .. 16 s + 15,
-          // lane L's 16 bytes at L * 16 holding column 32 rb + L % 32 and keys
-          // 16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3 (h = L / 32), the order
-          // in which the dQ kernel's transposing K^T reads take the keys.
-          // The wavefront's 32 keys go through its own LDS block as a
-          // row-major [key][column] tile; transposing reads of it yield whole
-          // fragment lanes, so each store writes 1 KiB of consecutive bytes.
-          // LDS accesses of one wavefront execute in order; no barrier is needed.
-          char* xb = reinterpret_cast<char*>(sm.dsx[w]);
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-              *reinterpret_cast<u32x4*>(xb + rm_byte<BQ>(lr, 8 * (4 * g + 2 * mb + t))) = dsp[mb][t];
-          const int64_t slot = slot0 + pass_base + sm.rank[it];
-          char* tile = reinterpret_cast<char*>(ds_rep + slot * (BK * BQ));
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int sp = 0; sp < 2; ++sp) {
-              const int r0 = 16 * sp + 4 * g;
-              const u32x4 x = tr_operand<BQ>(xb, l, 32 * rb, r0, r0 + 8);
-              __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(tile + (rb * 8 + 2 * w + sp) * 1024 + l * 16));
-            }
-        }
+  int it_global = 0;   // iteration count over heads and passes (selects the LDS buffer)
+  const int ngroup = GROUPED ? a.group : 1;
+  for (int gi = 0; gi < ngroup; ++gi) {
+    h = hk * ngroup + gi;
+    {
+      const int hm = a.mask.hm > 1 ? h : 0;
+      const int64_t mbase = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
+      const int mrow = bm * a.mask.hm + hm;
+      ccol = a.classes_t + ((int64_t)mrow * a.tk + kt) * a.tq;
+      // The lane's key bounds (keys past the end are masked for every row) and
+      // interval widths (0 for empty intervals): row mm is masked by [s, e) iff
+      // (uint)(mm - s) < width, exact for every int32 s, e.
+      int32_t lte = INT_MAX, ute = 0;
+      b_lts = INT_MIN;
+      b_uts = 0;
+      if (key_ok) {
+        b_lts = a.mask.has_lower ? a.mask.lts[mbase + n] : a.seq_q;
+        lte = a.mask.has_lower ? a.mask.lte[mbase + n] : a.seq_q;
+        b_uts = a.mask.has_upper ? a.mask.uts[mbase + n] : 0;
+        ute = a.mask.has_upper ? a.mask.ute[mbase + n] : 0;
       }
-    };
-    int it = 0;
-    for (; it < n_full; ++it, ++it_global) iteration(std::false_type{}, it);
-    for (; it < n_list; ++it, ++it_global) iteration(std::true_type{}, it);
+      b_lw = lte > b_lts ? (uint32_t)lte - (uint32_t)b_lts : 0u;
+      b_uw = ute > b_uts ? (uint32_t)ute - (uint32_t)b_uts : 0u;
+      // Stored dS: when the plan enables it, every processed tile's bf16 dS goes
+      // to slot row_off[mask row][kt] + (rank of its query tile among this key
+      // tile's non-SKIP ones) of the (b, h) pair's tile stream.
+      if (store_ds) {
+        const int rep_i = (a.mask.bm > 1 ? 0 : b) * (a.mask.hm > 1 ? 1 : a.heads) + (a.mask.hm > 1 ? 0 : h);
+        slot0 = a.row_off[(int64_t)mrow * a.tk + kt];
+        ds_rep = a.ds + (int64_t)rep_i * a.plan[0] * (BK * BQ);
+      }
+      lrow = ((int64_t)b * a.heads + h) * a.seq_pad;
+      qbh = reinterpret_cast<const char*>(a.q) + ((int64_t)b * a.q_sb + (int64_t)h * a.q_sh) * ES;
+      dbh = reinterpret_cast<const char*>(a.dout) + ((int64_t)b * a.o_sb + (int64_t)h * a.o_sh) * ES;
+    }
+    const int head_base = it_global;   // non-SKIP tiles of earlier heads
+    for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
+      int n_full;
+      const int n_list = compact_classes_split<LIST_CAP, NT>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.rank,
+                                                             sm.scan, tid, ragged_k, &n_full);
+      if (n_list == 0) continue;
+      const int pass_base = it_global - head_base;   // this head's non-SKIP tiles in earlier passes
+
+      stage_q((int)(sm.list[0] & ~kPartialBit), it_global % NBUF);
+      if (n_list > 1) stage_q((int)(sm.list[1] & ~kPartialBit), (it_global + 1) % NBUF);
+
+      // FULL tiles first, then PARTIAL ones, each with its own straight-line
+      // body (one branch-free basic block per query tile).
+      auto iteration = [&](auto masked_c, int it) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        const int buf = it_global % NBUF;
+        const int qt = (int)(sm.list[it] & ~kPartialBit);
+        const int m0 = qt * BQ;
+        // This tile's loads done. Younger vector-memory operations that may stay
+        // in flight: the next tile's loads and the dS stores of the last two
+        // iterations of this pass (vmcnt counts stores too).
+        wait_vmem_upto((it + 1 < n_list ? GROUP + (wu < 2 ? 1 : 0) : 0) + (store_ds ? 4 * min(it, 2) : 0));
+        __syncthreads();   // tile `buf` visible to all; the buffer read last iteration is free
+        if (it + 2 < n_list) stage_q((int)(sm.list[it + 2] & ~kPartialBit), (it_global + 2) % NBUF);
+        const char* qb = reinterpret_cast<const char*>(sm.q[buf]);
+        const char* db = reinterpret_cast<const char*>(sm.dout[buf]);
+
+        // One 64-row query tile as two 32-row halves (A: rows 0-31, B: 32-63),
+        // ordered so that each half's elementwise work runs beside the other
+        // half's matrix products (the MFMA unit works while the same wavefront
+        // issues independent VALU instructions):
+        //   S,dP(A) | S,dP(B) + P,dS(A) | dV,dK(A) + P,dS(B) | dV,dK(B)
+        {
+          f32x16 sacc[2], dpacc[2];
+          u32x4 pp[2][2], dsp[2][2];
+          // S = Q K^T and dP = dO V^T (lane = key, registers = query rows)
+          auto sdp = [&](int mb) {
+            sacc[mb] = f32x16{};
+            dpacc[mb] = f32x16{};
+  #pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+              const int off = rm_byte<D>(32 * mb + lr, 16 * s + 8 * g);
+              sacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(qb + off), kf[s], sacc[mb]);
+              dpacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(db + off), vf[s], dpacc[mb]);
+            }
+          };
+          // P = exp2(S * scale * log2(e) - LSE * log2(e)), dS = P (dP - D),
+          // both rounded to bf16 MFMA operands
+          auto softmax = [&](int mb) {
+  #pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int ml = 32 * mb + 8 * q4 + 4 * g;
+              const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
+              const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int i = 4 * q4 + r;
+                float p = fast_exp2(fmaf(sacc[mb][i], C, -l2[r]));
+                if constexpr (MASKED) {
+                  const int mm = m0 + ml + r;
+                  const bool mk = ((uint32_t)(mm - b_lts) < b_lw) | ((uint32_t)(mm - b_uts) < b_uw);
+                  p = mk ? 0.f : p;
+                }
+                sacc[mb][i] = p;
+                dpacc[mb][i] = p * (dpacc[mb][i] - dd[r]);
+              }
+            }
+  #pragma unroll
+            for (int t = 0; t < 2; ++t)
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                pp[mb][t][j] = pack_bf16(sacc[mb][8 * t + 2 * j], sacc[mb][8 * t + 2 * j + 1]);
+                dsp[mb][t][j] = pack_bf16(dpacc[mb][8 * t + 2 * j], dpacc[mb][8 * t + 2 * j + 1]);
+              }
+          };
+          // dV^T += dO^T P, dK^T += Q^T dS (contraction over the half's rows)
+          auto dvdk = [&](int mb) {
+  #pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int r0 = 32 * mb + 16 * t + 4 * g;
+  #pragma unroll
+              for (int cb = 0; cb < CB; ++cb) {
+                dvacc[cb] = mfma32(tr_operand<D>(db, l, 32 * cb, r0, r0 + 8), pp[mb][t], dvacc[cb]);
+                dkacc[cb] = mfma32(tr_operand<D>(qb, l, 32 * cb, r0, r0 + 8), dsp[mb][t], dkacc[cb]);
+              }
+            }
+          };
+          // Four scheduling regions; in each, operand reads run ahead of their
+          // MFMAs and the other half's elementwise work sits between MFMAs.
+          sdp(0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  #pragma unroll
+          for (int j = 0; j < 2 * KSTEPS - 4; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_barrier(0);
+
+          sdp(1);
+          softmax(0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  #pragma unroll
+          for (int j = 0; j < 2 * KSTEPS; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 9 : 6, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+
+          dvdk(0);
+          softmax(1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  #pragma unroll
+          for (int j = 0; j < 4 * CB; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 9 : 6, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+
+          dvdk(1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  #pragma unroll
+          for (int j = 0; j < 4 * CB - 3; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          __builtin_amdgcn_sched_barrier(0);
+
+          if (store_ds) {   // 4 stores per lane, counted by the wait above
+            // The stored tile is 16 MFMA operand fragments of 1 KiB, fragment
+            // (rb, s) = columns 32 rb .. 32 rb + 31 x keys 16 s .. 16 s + 15,
+            // lane L's 16 bytes at L * 16 holding column 32 rb + L % 32 and keys
+            // 16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3 (h = L / 32), the order
+            // in which the dQ kernel's transposing K^T reads take the keys.
+            // The wavefront's 32 keys go through its own LDS block as a
+            // row-major [key][column] tile; transposing reads of it yield whole
+            // fragment lanes, so each store writes 1 KiB of consecutive bytes.
+            // LDS accesses of one wavefront execute in order; no barrier is needed.
+            char* xb = reinterpret_cast<char*>(sm.dsx[w]);
+  #pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+              for (int t = 0; t < 2; ++t)
+                *reinterpret_cast<u32x4*>(xb + rm_byte<BQ>(lr, 8 * (4 * g + 2 * mb + t))) = dsp[mb][t];
+            const int64_t slot = slot0 + pass_base + sm.rank[it];
+            char* tile = reinterpret_cast<char*>(ds_rep + slot * (BK * BQ));
+  #pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+  #pragma unroll
+              for (int sp = 0; sp < 2; ++sp) {
+                const int r0 = 16 * sp + 4 * g;
+                const u32x4 x = tr_operand<BQ>(xb, l, 32 * rb, r0, r0 + 8);
+                __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(tile + (rb * 8 + 2 * w + sp) * 1024 + l * 16));
+              }
+          }
+        }
+      };
+      int it = 0;
+      for (; it < n_full; ++it, ++it_global) iteration(std::false_type{}, it);
+      for (; it < n_list; ++it, ++it_global) iteration(std::true_type{}, it);
+    }
   }
 
   // ---- epilogue: dK = scale * dK^T, dV = dV^T, transposed back on store ----
   if (key_ok) {
-    const int64_t koff = (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)h * a.k_sh;
-    const int64_t voff = (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)h * a.v_sh;
+    const int64_t koff = (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)hk * a.k_sh;
+    const int64_t voff = (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)hk * a.v_sh;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -508,8 +530,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   // rounded to bf16 on the way.
   constexpr int ES = F32 ? 4 : 2;
   const int64_t k_ld = a.k_ss * ES, v_ld = a.v_ss * ES;
-  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
-  const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * ES;
+  const int hk = __builtin_amdgcn_readfirstlane(h / a.group);   // K/V head (grouped-query attention)
+  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh) * ES;
+  const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh) * ES;
   using Dma = DmaTile<D, BK, NT>;
   constexpr int NOFF = F32 ? KR : 1;
   constexpr int NREG = F32 ? KR : 1;
@@ -672,7 +695,10 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
 
 template <int D, bool F32>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32>), dim3(a.tk * a.batch * a.heads), dim3(NT), 0, s, a);
+  if (a.group > 1)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, true>), dim3(a.tk * a.batch * a.heads_kv), dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, false>), dim3(a.tk * a.batch * a.heads_kv), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

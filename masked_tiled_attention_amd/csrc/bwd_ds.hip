@@ -169,7 +169,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
 
   // ---- staging: K (bf16: direct loads; float32: through registers) and dS ----
   const int64_t k_ld = a.k_ss * ES;
-  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
+  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)__builtin_amdgcn_readfirstlane(h / a.group) * a.k_sh) * ES;
   using DmaK = DmaTile<D, BK, NT>;
   constexpr int NOFF = F32 ? KR : 1;
   uint32_t koff[NOFF];

@@ -122,7 +122,8 @@ __global__ __launch_bounds__(256) void order_count_kernel(OrderArgs a) {
   const int r = blockIdx.x;
   const uint8_t* line = a.classes + (int64_t)(r / a.inner) * a.outer_stride + (int64_t)(r % a.inner) * a.line_stride;
   int c = 0;
-  for (int i = threadIdx.x; i < a.len; i += 256) c += line[i * a.elem_stride] != FM_TILE_SKIP;
+  for (int gi = 0; gi < a.group; ++gi)
+    for (int i = threadIdx.x; i < a.len; i += 256) c += line[gi * a.group_stride + i * a.elem_stride] != FM_TILE_SKIP;
   for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
   __shared__ int red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
@@ -138,9 +139,12 @@ __global__ __launch_bounds__(1024) void order_sort_kernel(OrderArgs a) {
   __shared__ int hist[kOrderBuckets];
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nb = min(a.len + 1, kOrderBuckets);
-  auto key = [&](int r) {   // descending count -> ascending key
-    return nb - 1 - (int)((int64_t)a.counts[r] * nb / ((int64_t)a.len + 1));
+  // a line counts up to len entries in each of its `group` class-map lines
+  const int64_t cmax = (int64_t)a.len * a.group;
+  const int nb = (int)min(cmax + 1, (int64_t)kOrderBuckets);
+  auto key = [&](int r) {   // descending count -> ascending key in [0, nb)
+    const int64_t c = min(max((int64_t)a.counts[r], (int64_t)0), cmax);
+    return nb - 1 - (int)(c * nb / (cmax + 1));
   };
   for (int i = tid; i < nb; i += 1024) hist[i] = 0;
   __syncthreads();

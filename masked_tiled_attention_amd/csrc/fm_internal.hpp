@@ -57,6 +57,7 @@ struct FwdArgs {
   // tq + query tile), longest first, and (b, h) pair p % rep of that mask row.
   const int32_t* order;
   int32_t rep;             // (b, h) pairs per mask row
+  int32_t group;           // query heads per K/V head: K/V head = h / group
 };
 
 // Lines of a class map ordered by their non-SKIP count, descending. Line r
@@ -67,6 +68,8 @@ struct OrderArgs {
   const uint8_t* classes;
   int32_t rows, len, inner;
   int64_t outer_stride, line_stride, elem_stride;
+  int32_t group;           // a line counts `group` class-map lines, group_stride apart
+  int64_t group_stride;
   int32_t* counts;         // [rows] non-SKIP entries per line
   int32_t* order;          // [rows] line indices, longest first
 };
@@ -90,6 +93,7 @@ struct BwdArgs {
   int64_t v_sb, v_ss, v_sh;
   int64_t o_sb, o_ss, o_sh;
   int32_t batch, heads, seq_q, seq_k;
+  int32_t heads_kv, group;   // K/V heads; query heads per K/V head
   float scale;
   float scale_log2;
   MaskArgs mask;
@@ -106,6 +110,11 @@ struct BwdArgs {
   uint16_t* ds;              // [rep][total][kBwdBlockK keys][kBwdBlockQ rows] bf16
   int64_t ds_capacity;       // bytes available at ds
   int32_t rep;               // (b, h) pairs per mask row
+  // The dK/dV kernel works per (b, K/V head, key tile) over the `group` query
+  // heads of the K/V head; its lines are K/V mask rows (bm * hkm + hk with
+  // hkm = heads_kv when the mask has a row per head, else 1) times key
+  // tiles, and rep_kv (b, K/V head) pairs share one.
+  int32_t rep_kv;
   // Launch orders, longest first (see FwdArgs::order): key tiles of the dK/dV
   // tiling and the recompute dQ kernel's query tiles (may be nullptr).
   const int32_t* order_k;

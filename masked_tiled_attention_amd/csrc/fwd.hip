@@ -115,8 +115,9 @@ void fwd_kernel(FwdArgs a) {
   // bf16: straight from global memory into LDS (no staging registers);
   // float32: through registers, rounded to bf16 on the way.
   const int64_t k_ld = a.k_ss * ES, v_ld = a.v_ss * ES;
-  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)h * a.k_sh) * ES;
-  const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)h * a.v_sh) * ES;
+  const int hk = __builtin_amdgcn_readfirstlane(h / a.group);   // K/V head (grouped-query attention)
+  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)hk * a.k_sh) * ES;
+  const char* vbh = reinterpret_cast<const char*>(a.v) + ((int64_t)b * a.v_sb + (int64_t)hk * a.v_sh) * ES;
   using Dma = DmaTile<D, BK, NT>;
   constexpr int NOFF = F32 ? KR : 1;
   constexpr int NREG = F32 ? KR : 1;

@@ -42,11 +42,12 @@ def test_kernel_tile():
 FAKE = 0x10000  # an aligned address that is never dereferenced: every case fails validation first
 
 
-def _problem(B=1, H=2, Sq=100, Sk=120, D=128, dtype=L.FM_BF16, scale=0.1, strides=None):
+def _problem(B=1, H=2, Sq=100, Sk=120, D=128, dtype=L.FM_BF16, scale=0.1, strides=None, hkv=0):
     st = strides or (Sq * H * D, H * D, D)
-    sk = (Sk * H * D, H * D, D)
+    nk = hkv or H
+    sk = (Sk * nk * D, nk * D, D)
     arr = lambda s: (C.c_int64 * 3)(*s)
-    return L.fm_problem(B, H, Sq, Sk, D, dtype, scale, arr(st), arr(sk), arr(sk), arr(st))
+    return L.fm_problem(B, H, Sq, Sk, D, dtype, scale, arr(st), arr(sk), arr(sk), arr(st), hkv)
 
 
 def _mask(bm=1, hm=1, lower=True, upper=True, one_null=False):
@@ -77,6 +78,8 @@ def _fwd(prob, mask, ws_bytes=1 << 30, ptrs=None):
     ("null_q", L.FM_ERR_INVALID_ARGUMENT),
     ("misaligned_q", L.FM_ERR_INVALID_ARGUMENT),
     ("small_workspace", L.FM_ERR_WORKSPACE),
+    ("kv_heads_not_dividing", L.FM_ERR_INVALID_ARGUMENT),
+    ("kv_heads_negative", L.FM_ERR_INVALID_ARGUMENT),
 ])
 def test_fwd_rejects(case, expect):
     prob, mask, ws, ptrs = _problem(), _mask(), 1 << 30, None
@@ -104,6 +107,10 @@ def test_fwd_rejects(case, expect):
         ptrs = (FAKE + 8, FAKE, FAKE, FAKE, FAKE)
     elif case == "small_workspace":
         ws = 16
+    elif case == "kv_heads_not_dividing":
+        prob = _problem(H=6, hkv=4)
+    elif case == "kv_heads_negative":
+        prob = _problem(hkv=-1)
     assert _fwd(prob, mask, ws, ptrs) == expect
     assert L.load().fm_last_error()
 
