@@ -23,6 +23,11 @@ rank needs key tile kt (keys [kt*Bc, min((kt+1)*Bc, Sk))) exactly when at
 least one of its rows attends at least one key of the tile, which the oracle
 takes from the dense mask over the rank's rows.
 
+Chunk work: the same page names a sparsity-aware load balancer (HCC-IPO) for
+context parallelism and nothing more. What it must balance is taken to be
+the attention work of a rank, i.e. its open (row, key) pairs; the oracle
+counts them per chunk of the global query axis from the dense mask.
+
 Tile classes: the pages do not describe a tile pre-pass. The rule here is the
 reading adopted for it. Per K/V tile, the minimum and maximum of each bound
 vector over the tile's columns are reduced; a (Q tile, K tile) pair with rows
@@ -89,6 +94,55 @@ def transfer_set(vectors, seq_q, seq_k, block_k):
             for t in range(tk):
                 out[b, h, t] = open_key[t * block_k:min((t + 1) * block_k, seq_k)].any()
     return out
+
+
+def chunk_work(vectors, seq_k, chunk_start, chunk_len):
+    """Open (row, key) pairs per mask row and chunk: int64 [Bm * Hm, C], the
+    rows of chunk c being [chunk_start[c], chunk_start[c] + chunk_len[c])
+    (dense truth, 4096 rows at a time)."""
+    ref = next((np.asarray(x) for x in vectors if x is not None), None)
+    bm, hm = (1, 1) if ref is None else (ref.shape[0], ref.shape[1])
+    out = np.zeros((bm * hm, len(chunk_start)), dtype=np.int64)
+    for b in range(bm):
+        for h in range(hm):
+            v = vectors_for(vectors, b, h)
+            for c, (s0, ln) in enumerate(zip(chunk_start, chunk_len)):
+                for r0 in range(int(s0), int(s0) + int(ln), 4096):
+                    rows = np.arange(r0, min(r0 + 4096, int(s0) + int(ln)))
+                    out[b * hm + h, c] += int((~dense_mask(*v, rows, seq_k)).sum())
+    return out
+
+
+def plan_loads(work, rank_of_chunk, num_ranks):
+    """Per-rank load of an assignment (work summed over its chunks)."""
+    loads = np.zeros(num_ranks, dtype=np.int64)
+    for c, r in enumerate(rank_of_chunk):
+        loads[r] += int(work[c])
+    return loads
+
+
+def best_plan_max(work, num_ranks):
+    """Smallest possible maximum rank load with len(work) / num_ranks chunks
+    per rank, by exhaustive search (tiny inputs only)."""
+    work = [int(x) for x in work]
+    per = len(work) // num_ranks
+    best = [None]
+
+    def rec(rest, loads):
+        if not rest:
+            m = max(loads)
+            if best[0] is None or m < best[0]:
+                best[0] = m
+            return
+        first, others = rest[0], rest[1:]
+        # the group holding the lowest-index remaining chunk (no symmetric repeats)
+        from itertools import combinations
+        for comb in combinations(range(len(others)), per - 1):
+            grp = [first] + [others[i] for i in comb]
+            left = [x for i, x in enumerate(others) if i not in comb]
+            rec(left, loads + [sum(work[g] for g in grp)])
+    rec(list(range(len(work))), [])
+    return best[0]
 
 
 def _canonical(vec, seq_q, n_keys):

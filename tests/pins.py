@@ -616,4 +616,64 @@ def pin_transfer_set_matches_classes():
                           (cls != oracle.SKIP).any(axis=0).astype(np.uint8))
 
 
+# ---------------------------------------------------------------------------
+# Chunk work and the chunk -> rank plan
+# ---------------------------------------------------------------------------
+
+def pin_chunk_work_closed_forms():
+    """Per-chunk open pairs against row-by-row closed forms: causal (row i
+    sees i + 1 keys), document-causal (row i sees i - start(doc) + 1),
+    sliding window W (min(i + 1, W)), no mask (all Sk keys)."""
+    n = 120
+    starts, lens = [0, 17, 40, 77, 90], [17, 23, 37, 13, 30]
+    docs = [25, 8, 40, 47]
+    doc_start = np.repeat(np.concatenate([[0], np.cumsum(docs)[:-1]]), docs)
+    w = 19
+    cases = [(SM.causal(n), lambda i: i + 1),
+             (SM.document_causal(docs), lambda i: i - doc_start[i] + 1),
+             (SM.sliding_window_causal(n, w), lambda i: min(i + 1, w)),
+             (SM.no_mask(n, n), lambda i: n)]
+    for vec, per_row in cases:
+        got = OM.chunk_work(_vec3(vec), n, starts, lens)[0]
+        want = [sum(per_row(i) for i in range(s0, s0 + ln)) for s0, ln in zip(starts, lens)]
+        assert got.tolist() == want
+
+
+def pin_chunk_work_partition_sums_to_nnz():
+    """Chunks that partition the query axis add up to the O(Sk) closed-form
+    count of open pairs (random vectors, broadcast shapes, a missing pair)."""
+    rng = np.random.default_rng(141)
+    for it in range(20):
+        sq, sk = int(rng.integers(1, 60)), int(rng.integers(1, 40))
+        bm, hm = (1, 1) if it % 2 else (2, 3)
+        vec = [rng.integers(-5, sq + 6, (bm, hm, sk)) for _ in range(4)]
+        if it % 4 == 0:
+            vec[2] = vec[3] = None
+        cuts = np.unique(np.concatenate([[0, sq], rng.integers(0, sq + 1, 3)]))
+        starts, lens = cuts[:-1], np.diff(cuts)
+        got = OM.chunk_work(tuple(vec), sk, starts, lens)
+        for b in range(bm):
+            for h in range(hm):
+                sub = tuple(None if x is None else x[b:b + 1, h:h + 1] for x in vec)
+                assert int(got[b * hm + h].sum()) == OA.nnz_closed_form(sub, sq)
+
+
+def pin_best_plan_exhaustive():
+    """The pruned exhaustive search equals plain enumeration of every
+    assignment with len / ranks chunks per rank (tiny random works)."""
+    import itertools
+    rng = np.random.default_rng(151)
+    for c, r in ((4, 2), (6, 3), (6, 2), (8, 4)):
+        for _ in range(4):
+            work = rng.integers(0, 100, c)
+            per = c // r
+            best = None
+            for assign in itertools.product(range(r), repeat=c):
+                if any(assign.count(k) != per for k in range(r)):
+                    continue
+                m = int(OM.plan_loads(work, assign, r).max())
+                best = m if best is None else min(best, m)
+            assert OM.best_plan_max(work, r) == best, (c, r, work)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -178,12 +178,30 @@ def _transfer_factory(variant):
     return transfer_set
 
 
+def _chunk_work_factory(variant):
+    def chunk_work(vectors, seq_k, chunk_start, chunk_len):
+        ref = next((np.asarray(x) for x in vectors if x is not None), None)
+        bm, hm = (1, 1) if ref is None else (ref.shape[0], ref.shape[1])
+        out = np.zeros((bm * hm, len(chunk_start)), dtype=np.int64)
+        for b in range(bm):
+            for h in range(hm):
+                v = OA.vectors_for(vectors, b, h)
+                for c, (s0, ln) in enumerate(zip(chunk_start, chunk_len)):
+                    end = int(s0) + int(ln) + (1 if variant == "chunk_end_inclusive" else 0)
+                    m = OA.dense_mask(*v, np.arange(int(s0), end), seq_k)
+                    out[b * hm + h, c] = int(m.sum() if variant == "counts_masked" else (~m).sum())
+        return out
+    return chunk_work
+
+
 def _kv_head_mod(q_heads, kv_heads, h):
     return h % kv_heads
 
 
 MUTATIONS = {
     "gqa_head_modulo": (OA, "kv_head", _kv_head_mod),
+    "chunk_work_end_inclusive": (OM, "chunk_work", _chunk_work_factory("chunk_end_inclusive")),
+    "chunk_work_counts_masked": (OM, "chunk_work", _chunk_work_factory("counts_masked")),
     "transfer_any_masked": (OM, "transfer_set", _transfer_factory("any_masked")),
     "transfer_tile_overlap": (OM, "transfer_set", _transfer_factory("tile_overlap")),
     "fwd_no_scale": (OA, "_rows_forward", _fwd_factory("no_scale")),
