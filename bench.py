@@ -85,6 +85,38 @@ class Runner:
             self.transfer_bk = fm.fm_kernel_tile(w.head_dim, True)[1]
             need, count = fm.fm_kv_transfer_set(self.mask, w.seq_q, self.transfer_bk)
             self.kv_tiles = (int(count.sum()), int(need.numel()))
+            # chunk -> rank planning for the whole context-parallel layout:
+            # open pairs per chunk (device), then the host plan vs dual-chunk
+            nck = 16   # 8 ranks, two chunks each
+            cl = w.seq_q_global // nck
+            starts, lens = [i * cl for i in range(nck)], [cl] * nck
+            fm.fm_chunk_work(self.gmask, w.seq_q_global, starts, lens)
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            cw = fm.fm_chunk_work(self.gmask, w.seq_q_global, starts, lens)
+            t1.record()
+            torch.cuda.synchronize()
+            work = cw.sum(dim=0).cpu().tolist()
+            ranks = nck // 2
+            plan, mx = fm.fm_cp_plan(work, ranks)
+            dual = [0] * ranks
+            for c in range(nck):
+                dual[min(c, nck - 1 - c)] += work[c]
+            self.cp_plan = {"chunks": nck, "ranks": ranks, "chunk_work_ms": round(t0.elapsed_time(t1), 4),
+                            "mean_load": sum(work) // ranks, "dual_chunk_max_load": max(dual),
+                            "planned_max_load": mx}
+            # finer chunks (8 per rank): the snake order vs the plan
+            nf = 64
+            clf = w.seq_q_global // nf
+            wf = fm.fm_chunk_work(self.gmask, w.seq_q_global, [i * clf for i in range(nf)], [clf] * nf)
+            wf = wf.sum(dim=0).cpu().tolist()
+            _, mxf = fm.fm_cp_plan(wf, ranks)
+            snake = [0] * ranks
+            for c in range(nf):
+                k, p_ = divmod(c, ranks)
+                snake[p_ if k % 2 == 0 else ranks - 1 - p_] += wf[c]
+            self.cp_plan["chunks_64"] = {"snake_max_load": max(snake), "planned_max_load": mxf}
         else:
             self.gmask = None
             self.mask = fm.Mask.from_vectors(w.vectors, dev)
@@ -304,6 +336,7 @@ def main():
                 item["localize_ms"] = round(pf("localize"), 4)
                 item["transfer_set_ms"] = round(pf("transfer"), 4)
                 item["kv_tiles_needed"] = f"{rx.kv_tiles[0]} of {rx.kv_tiles[1]} ({rx.transfer_bk}-key tiles)"
+                item["cp_plan"] = rx.cp_plan
             sweep.append(item)
             del rx
             torch.cuda.empty_cache()

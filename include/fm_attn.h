@@ -223,6 +223,32 @@ fm_status fm_mask_localize(const fm_mask* global, int32_t seqlen_k, int32_t seql
 fm_status fm_kv_transfer_set(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen_k, int32_t block_k,
                              uint8_t* need, int32_t* count, hipStream_t stream);
 
+/* Work per chunk of the global query axis, for a sparsity-aware chunk ->
+ * rank assignment (FlashMask-3 page, contributions paragraph and "Key facts"
+ * name the HCC-IPO load balancer and nothing more; the work measure is this
+ * library's reading): work[mr][c] = the number of open (row, key) pairs of
+ * mask row mr (= bm * Hm + hm) whose row lies in chunk c = [chunk_start[c],
+ * chunk_start[c] + chunk_len[c]), exact for any bound values (int64).
+ * Chunks (host arrays) as for fm_mask_localize: ascending, not overlapping,
+ * chunk_len >= 1, inside [0, seqlen_q_global], 1 <= num_chunks <= 64.
+ * work: device int64 [Bm*Hm][num_chunks], 8-byte aligned. */
+fm_status fm_chunk_work(const fm_mask* global, int32_t seqlen_k, int32_t seqlen_q_global,
+                        const int32_t* chunk_start, const int32_t* chunk_len, int32_t num_chunks, int64_t* work,
+                        hipStream_t stream);
+
+/* Chunk -> rank plan (host only; no device memory, no stream). Gives each of
+ * num_ranks ranks exactly num_chunks / num_ranks chunks so that the largest
+ * rank load (sum of chunk_work over its chunks; host array, >= 0) is small:
+ * with two chunks per rank, sorted pairing (largest with smallest), which is
+ * optimal; otherwise longest first into the least loaded rank with room; in
+ * both cases and from the snake order (the dual-chunk assignment for two per
+ * rank), single-chunk exchanges with the most loaded rank while they lower
+ * it. The better plan is returned (never worse than the snake order).
+ * rank_of_chunk: host int32 [num_chunks]; max_load (may be NULL) receives the
+ * largest rank load. num_chunks must be a multiple of num_ranks, <= 4096. */
+fm_status fm_cp_plan(const int64_t* chunk_work, int32_t num_chunks, int32_t num_ranks, int32_t* rank_of_chunk,
+                     int64_t* max_load);
+
 /* Per-kernel timing. Between fm_profile_begin and fm_profile_end the library
  * records a HIP event pair on the launch stream around each of its kernel
  * launches (at most max_launches pairs; later launches are not recorded).
@@ -241,7 +267,8 @@ typedef enum {
   FM_STAGE_BWD_DQ_DS = 8,   /* dQ from stored dS */
   FM_STAGE_ORDER = 9,       /* launch orders, longest tiles first (count, sort) */
   FM_STAGE_TRANSFER = 10,   /* mask-pruned K/V transfer set */
-  FM_NUM_STAGES = 11
+  FM_STAGE_CHUNK_WORK = 11, /* open pairs per chunk of the query axis */
+  FM_NUM_STAGES = 12
 } fm_stage;
 
 fm_status fm_profile_begin(int32_t max_launches);

@@ -14,7 +14,7 @@ FM_OK, FM_ERR_INVALID_ARGUMENT, FM_ERR_UNSUPPORTED, FM_ERR_WORKSPACE, FM_ERR_HIP
 FM_BF16, FM_FP32 = 0, 1
 FM_TILE_SKIP, FM_TILE_PARTIAL, FM_TILE_FULL = 0, 1, 2
 STAGES = ("classify_summary", "classify_map", "fwd", "bwd_pre", "bwd", "bwd_dq", "localize",
-          "bwd_plan", "bwd_dq_ds", "order", "transfer")
+          "bwd_plan", "bwd_dq_ds", "order", "transfer", "chunk_work")
 FM_NUM_STAGES = len(STAGES)
 
 STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_INVALID_ARGUMENT", 2: "FM_ERR_UNSUPPORTED",
@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_INVALID_ARGUMENT", 2: "FM_ERR_UNSUPPORTED
 
 # Every symbol the header declares (checked by the CPU test-suite).
 EXPORTS = ("fm_kernel_tile", "fm_workspace_size", "fm_bwd_workspace_size_ds", "fm_tile_classify",
-           "fm_attn_fwd", "fm_attn_bwd", "fm_mask_localize", "fm_kv_transfer_set", "fm_profile_begin",
+           "fm_attn_fwd", "fm_attn_bwd", "fm_mask_localize", "fm_kv_transfer_set", "fm_chunk_work", "fm_cp_plan",
+           "fm_profile_begin",
            "fm_profile_end", "fm_last_error")
 
 
@@ -76,6 +77,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
                                 vp, sz, vp]
     lib.fm_mask_localize.restype = C.c_int
     lib.fm_mask_localize.argtypes = [P(fm_mask), i32, i32, P(i32), P(i32), i32, P(vp), vp]
+    lib.fm_chunk_work.restype = C.c_int
+    lib.fm_chunk_work.argtypes = [P(fm_mask), i32, i32, P(i32), P(i32), i32, vp, vp]
+    lib.fm_cp_plan.restype = C.c_int
+    lib.fm_cp_plan.argtypes = [P(C.c_int64), i32, i32, P(i32), P(C.c_int64)]
     lib.fm_kv_transfer_set.restype = C.c_int
     lib.fm_kv_transfer_set.argtypes = [P(fm_mask), i32, i32, i32, vp, vp, vp]
     lib.fm_profile_begin.restype = C.c_int

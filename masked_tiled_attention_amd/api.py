@@ -230,6 +230,36 @@ def fm_mask_localize(mask: Mask, seq_q_global: int, chunk_start, chunk_len, stre
     return Mask(*out)
 
 
+def fm_chunk_work(mask: Mask, seq_q_global: int, chunk_start, chunk_len, stream=None) -> torch.Tensor:
+    """Open (row, key) pairs per mask row and chunk of the global query axis:
+    int64 [Bm * Hm, C] on the mask's device."""
+    m = mask._c()
+    ref = mask.first()
+    bm, hm, sk = ref.shape
+    starts = [int(x) for x in chunk_start]
+    lens = [int(x) for x in chunk_len]
+    if len(starts) != len(lens):
+        raise ValueError("chunk_start and chunk_len differ in length")
+    nck = len(starts)
+    cs = (C.c_int32 * max(nck, 1))(*starts)
+    cl = (C.c_int32 * max(nck, 1))(*lens)
+    work = torch.empty((bm * hm, nck), dtype=torch.int64, device=ref.device)
+    L.check(L.load().fm_chunk_work(C.byref(m), int(sk), int(seq_q_global), cs, cl, nck, work.data_ptr(),
+                                   _stream(stream)))
+    return work
+
+
+def fm_cp_plan(chunk_work, num_ranks: int):
+    """Chunk -> rank plan (host): (rank_of_chunk list, largest rank load)."""
+    w = [int(x) for x in chunk_work]
+    n = len(w)
+    arr = (C.c_int64 * max(n, 1))(*w)
+    out = (C.c_int32 * max(n, 1))()
+    mx = C.c_int64()
+    L.check(L.load().fm_cp_plan(arr, n, int(num_ranks), out, C.byref(mx)))
+    return list(out[:n]), mx.value
+
+
 def fm_kv_transfer_set(mask: Mask, seq_q: int, block_k: int, with_count: bool = True, stream=None):
     """Mask-pruned K/V transfer set of a rank whose own (localized) vectors
     are `mask`, over its seq_q rows: (need uint8 [Bm, Hm, Tk], count int32

@@ -538,6 +538,57 @@ fm_status fm_mask_localize(const fm_mask* global, int32_t seqlen_k, int32_t seql
   return FM_OK;
 }
 
+fm_status fm_chunk_work(const fm_mask* global, int32_t seqlen_k, int32_t seqlen_q_global,
+                        const int32_t* chunk_start, const int32_t* chunk_len, int32_t num_chunks, int64_t* work,
+                        hipStream_t stream) {
+  fm::MaskArgs mk;
+  if (!global) return fail(FM_ERR_INVALID_ARGUMENT, "mask is NULL");
+  fm_status st = check_mask(global, global->batch, global->heads, &mk);
+  if (st != FM_OK) return st;
+  if (global->batch < 1 || global->heads < 1 || (int64_t)global->batch * global->heads > 65535)
+    return fail(FM_ERR_INVALID_ARGUMENT, "mask batch*heads must be in [1, 65535]");
+  if (seqlen_k < 1 || seqlen_k > kMaxSeq) return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_k out of range");
+  if (seqlen_q_global < 1 || seqlen_q_global > kMaxSeq)
+    return fail(FM_ERR_INVALID_ARGUMENT, "seqlen_q_global out of range");
+  if (num_chunks < 1 || num_chunks > fm::kMaxChunks)
+    return fail(FM_ERR_INVALID_ARGUMENT, "num_chunks must be in [1, %d]", fm::kMaxChunks);
+  if (!chunk_start || !chunk_len) return fail(FM_ERR_INVALID_ARGUMENT, "chunk list is NULL");
+  if (!work || reinterpret_cast<uintptr_t>(work) % 8) return fail(FM_ERR_INVALID_ARGUMENT, "work is NULL or not 8-byte aligned");
+  fm::ChunkWorkArgs a{};
+  a.mask = mk;
+  a.seq_k = seqlen_k;
+  a.num_chunks = num_chunks;
+  int64_t prev_end = 0;
+  for (int c = 0; c < num_chunks; ++c) {
+    const int64_t s = chunk_start[c], l = chunk_len[c];
+    if (l < 1) return fail(FM_ERR_INVALID_ARGUMENT, "chunk %d has length %lld", c, (long long)l);
+    if (s < prev_end)
+      return fail(FM_ERR_INVALID_ARGUMENT, "chunk %d starts at %lld: chunks must ascend without overlap", c,
+                  (long long)s);
+    if (s + l > seqlen_q_global) return fail(FM_ERR_INVALID_ARGUMENT, "chunk %d ends past seqlen_q_global", c);
+    a.chunk_start[c] = (int32_t)s;
+    a.chunk_len[c] = (int32_t)l;
+    prev_end = s + l;
+  }
+  a.work = work;
+  hipError_t e = run_stage(FM_STAGE_CHUNK_WORK, stream, [&] { return fm::launch_chunk_work(a, stream); });
+  if (e != hipSuccess) return hip_fail(e, "chunk work launch");
+  return FM_OK;
+}
+
+fm_status fm_cp_plan(const int64_t* chunk_work, int32_t num_chunks, int32_t num_ranks, int32_t* rank_of_chunk,
+                     int64_t* max_load) {
+  if (!chunk_work || !rank_of_chunk) return fail(FM_ERR_INVALID_ARGUMENT, "chunk_work or rank_of_chunk is NULL");
+  if (num_ranks < 1 || num_chunks < 1 || num_chunks > 4096 || num_chunks % num_ranks)
+    return fail(FM_ERR_INVALID_ARGUMENT, "num_chunks (%d) must be a multiple of num_ranks (%d), at most 4096",
+                num_chunks, num_ranks);
+  for (int c = 0; c < num_chunks; ++c)
+    if (chunk_work[c] < 0) return fail(FM_ERR_INVALID_ARGUMENT, "chunk_work[%d] is negative", c);
+  const int64_t m = fm::plan_chunks(chunk_work, num_chunks, num_ranks, rank_of_chunk);
+  if (max_load) *max_load = m;
+  return FM_OK;
+}
+
 fm_status fm_kv_transfer_set(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen_k, int32_t block_k,
                              uint8_t* need, int32_t* count, hipStream_t stream) {
   fm::MaskArgs mk;

@@ -148,6 +148,14 @@ struct TransferArgs {
   int32_t* count;          // [bm][hm] or null
 };
 
+struct ChunkWorkArgs {
+  MaskArgs mask;
+  int32_t seq_k, num_chunks;
+  int32_t chunk_start[kMaxChunks];
+  int32_t chunk_len[kMaxChunks];
+  int64_t* work;           // [bm * hm][num_chunks]
+};
+
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream);
 hipError_t launch_classify_map(const ClassifyArgs& a, hipStream_t stream);
@@ -157,5 +165,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, bool f32, hipStream_t
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_localize(const LocalizeArgs& a, hipStream_t stream);
 hipError_t launch_transfer_set(const TransferArgs& a, hipStream_t stream);
+hipError_t launch_chunk_work(const ChunkWorkArgs& a, hipStream_t stream);
+// Host: chunk -> rank plan (plan.cpp); returns the largest rank load.
+int64_t plan_chunks(const int64_t* work, int num_chunks, int num_ranks, int32_t* rank_of_chunk);
 
 }  // namespace fm

@@ -92,7 +92,81 @@ __global__ __launch_bounds__(256) void transfer_count_kernel(TransferArgs a) {
   if (threadIdx.x == 0) a.count[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
+// Open (row, key) pairs per chunk of the global query axis, the work that a
+// sparsity-aware chunk -> rank assignment balances (same page: the HCC-IPO
+// balancer is named, nothing more). For key j, the masked rows are the union
+// of its two intervals A and B, so within chunk [s, e) it hides
+// |A n [s,e)| + |B n [s,e)| - |A n B n [s,e)| rows; the rest are open.
+// Workgroups take kWorkKeys keys of one mask row each and add their int64
+// sums into the (zeroed) output with atomics: exact for any bounds, and the
+// integer sums do not depend on the order.
+constexpr int kWorkThreads = 256;
+constexpr int kWorkKeys = 4096;
+constexpr int kWorkChunks = 8;
+
+__device__ __forceinline__ int64_t overlap(int64_t a, int64_t b, int64_t s, int64_t e) {
+  return max((int64_t)0, min(b, e) - max(a, s));
+}
+
+__global__ __launch_bounds__(256) void chunk_work_zero_kernel(ChunkWorkArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < (int64_t)a.mask.bm * a.mask.hm * a.num_chunks) a.work[i] = 0;
+}
+
+// grid (key blocks, bm * hm)
+__global__ __launch_bounds__(kWorkThreads) void chunk_work_kernel(ChunkWorkArgs a) {
+  const int mr = blockIdx.y;
+  const int bm = mr / a.mask.hm, hm = mr % a.mask.hm;
+  const int64_t base = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
+  const int j0 = blockIdx.x * kWorkKeys, j1 = min(j0 + kWorkKeys, a.seq_k);
+  __shared__ int64_t red[kWorkThreads / 64][kWorkChunks];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int c0 = 0; c0 < a.num_chunks; c0 += kWorkChunks) {
+    int64_t acc[kWorkChunks];
+#pragma unroll
+    for (int k = 0; k < kWorkChunks; ++k) acc[k] = 0;
+    for (int j = j0 + threadIdx.x; j < j1; j += kWorkThreads) {
+      const int64_t a0 = a.mask.has_lower ? a.mask.lts[base + j] : 0;
+      const int64_t a1 = a.mask.has_lower ? a.mask.lte[base + j] : 0;
+      const int64_t b0 = a.mask.has_upper ? a.mask.uts[base + j] : 0;
+      const int64_t b1 = a.mask.has_upper ? a.mask.ute[base + j] : 0;
+      const int64_t i0 = max(a0, b0), i1 = min(a1, b1);   // A n B
+#pragma unroll
+      for (int k = 0; k < kWorkChunks; ++k) {
+        if (c0 + k < a.num_chunks) {
+          const int64_t s = a.chunk_start[c0 + k], e = s + a.chunk_len[c0 + k];
+          acc[k] += (e - s) - overlap(a0, a1, s, e) - overlap(b0, b1, s, e) + overlap(i0, i1, s, e);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kWorkChunks; ++k) {
+      int64_t v = acc[k];
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0) red[wv][k] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < kWorkChunks && c0 + (int)threadIdx.x < a.num_chunks) {
+      int64_t t = 0;
+      for (int w = 0; w < kWorkThreads / 64; ++w) t += red[w][threadIdx.x];
+      atomicAdd(reinterpret_cast<unsigned long long*>(a.work + (int64_t)mr * a.num_chunks + c0 + threadIdx.x),
+                (unsigned long long)t);
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
+
+hipError_t launch_chunk_work(const ChunkWorkArgs& a, hipStream_t stream) {
+  const int64_t n = (int64_t)a.mask.bm * a.mask.hm * a.num_chunks;
+  hipLaunchKernelGGL(chunk_work_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chunk_work_kernel, dim3((a.seq_k + kWorkKeys - 1) / kWorkKeys, a.mask.bm * a.mask.hm),
+                     dim3(kWorkThreads), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_transfer_set(const TransferArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(transfer_set_kernel, dim3(a.tk, a.mask.bm * a.mask.hm), dim3(256), 0, stream, a);

@@ -222,3 +222,57 @@ def test_transfer_set_rank_share_full_size(gpu_lib):
         _, cls = fm.fm_tile_classify(loc, w.seq_q, w.seq_k, bq, bk)
         assert np.array_equal(ref[0, 0], (cls.cpu().numpy()[0, 0] != 0).any(axis=0).astype(np.uint8))
         log(f"rank share: {int(ref.sum())} of {ref.shape[2]} key tiles of {bk} keys needed")
+
+
+def _check_chunk_work(vec, sq, sk, starts, lens, fm, tag):
+    log(f"chunk work {tag} sq={sq} sk={sk} chunks={len(starts)}")
+    got = fm.fm_chunk_work(dev_mask(vec), sq, starts, lens).cpu().numpy()
+    ref = OM.chunk_work(vec, sk, starts, lens)
+    assert np.array_equal(got, ref), tag
+
+
+def test_chunk_work_families_and_random(gpu_lib):
+    """Bit-exact open-pair counts per chunk: every mask family under
+    dual-chunk layouts and random chunk lists, random and int32-limit bounds,
+    broadcast shapes and a missing pair."""
+    fm = gpu_lib
+    rng = np.random.default_rng(37)
+    n = 640
+    for name, v in _family_vectors(n, rng).items():
+        vec = tuple(x[None, None] for x in v)
+        for degree, rank in ((2, 0), (4, 3), (8, 5)):
+            cs, cl = SM.dual_chunk(n, degree, rank)
+            _check_chunk_work(vec, n, n, list(cs), list(cl), fm, f"{name} rank {rank}/{degree}")
+        _check_chunk_work(vec, n, n, [i * 40 for i in range(16)], [40] * 16, fm, f"{name} 16 chunks")
+    lo, hi = np.iinfo(np.int32).min, np.iinfo(np.int32).max
+    for trial in range(6):
+        sq, sk = int(rng.integers(2, 700)), int(rng.integers(1, 900))
+        bm, hm = int(rng.choice([1, 2])), int(rng.choice([1, 3]))
+        vec = [rng.integers(-50, sq + 50, (bm, hm, sk)).astype(np.int32) for _ in range(4)]
+        if trial % 2:
+            pick = np.array([lo, hi, 0, 1, sq - 1, sq, sq + 1, -1], np.int32)
+            vec = [rng.choice(pick, (bm, hm, sk)) for _ in range(4)]
+        if trial == 4:
+            vec[0] = vec[1] = None
+        cuts = np.unique(np.concatenate([[0, sq], rng.integers(0, sq + 1, int(rng.integers(1, 12)))]))
+        _check_chunk_work(tuple(vec), sq, sk, list(cuts[:-1]), list(np.diff(cuts)), fm, f"random trial={trial}")
+
+
+def test_chunk_work_and_plan_full_size(gpu_lib):
+    """The global 64K document-causal mask in 16 chunks of 4096 (the rank-share
+    layout): the chunks add up to the closed-form pair count, two chunks match
+    the dense truth, and the plan for 8 ranks is no worse than dual-chunk."""
+    fm = gpu_lib
+    from oracle import attention as OA
+    w = SC.build("c5_cp_rank3_of_8", 0, tensors=False)
+    n = w.seq_q_global
+    starts, lens = [i * 4096 for i in range(16)], [4096] * 16
+    got = fm.fm_chunk_work(dev_mask(w.global_vectors), n, starts, lens).cpu().numpy()[0]
+    assert int(got.sum()) == OA.nnz_closed_form(w.global_vectors, n)
+    for c in (3, 12):
+        assert got[c] == OM.chunk_work(w.global_vectors, w.seq_k, [starts[c]], [lens[c]])[0, 0]
+    plan, mx = fm.fm_cp_plan(got, 8)
+    dual = [min(i, 15 - i) for i in range(16)]
+    dual_max = int(OM.plan_loads(got, dual, 8).max())
+    assert mx <= dual_max
+    log(f"rank loads: mean {got.sum() / 8:.4g}, dual-chunk max {dual_max:.4g}, planned max {mx:.4g}")
