@@ -25,3 +25,12 @@ def qkv(batch, seq_q, seq_k, heads, head_dim, seed, dtype=torch.bfloat16, with_d
         return q, k, v
     do = randn("do", (batch, seq_q, heads, head_dim), seed, dtype)
     return q, k, v, do
+
+
+def fp8_codes(name: str, shape, seed: int, gain: float = 64.0) -> torch.Tensor:
+    """uint8 codes of the OCP E4M3 format (torch.float8_e4m3fn) for
+    N(0, 1) draws (clipped to +-6.5) times ``gain``; the matching descale
+    factor is 1 / gain. With gain <= 64 every product stays below 448, the
+    format's largest finite value."""
+    x = randn(name, shape, seed, torch.float32).clamp_(-6.5, 6.5) * float(gain)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)

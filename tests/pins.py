@@ -16,6 +16,7 @@ import torch
 
 import oracle
 from oracle import attention as OA
+from oracle import fp8 as OF
 from oracle import masks as OM
 from synth import masks as SM
 
@@ -675,5 +676,100 @@ def pin_best_plan_exhaustive():
                 best = m if best is None else min(best, m)
             assert OM.best_plan_max(work, r) == best, (c, r, work)
 
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) inputs
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3(codes):
+    """torch's own float8_e4m3fn -> float64 conversion (a library routine)."""
+    t = torch.as_tensor(np.asarray(codes, dtype=np.uint8))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_e4m3_decode_library():
+    """Every one of the 256 codes decodes as torch.float8_e4m3fn does,
+    signs of zero and NaN positions included."""
+    codes = np.arange(256)
+    a, b = OF.e4m3_decode(codes), _torch_e4m3(codes)
+    assert np.array_equal(np.isnan(a), np.isnan(b)), "NaN codes differ"
+    fin = ~np.isnan(b)
+    assert np.array_equal(a[fin], b[fin]), "decoded values differ"
+    assert np.array_equal(np.signbit(a[fin]), np.signbit(b[fin])), "signed zeros differ"
+
+
+def pin_e4m3_decode_hand_values():
+    """Values fixed by the format's definition: 1.0, the largest finite
+    value 448, the smallest normal 2^-6 and subnormal 2^-9, a subnormal
+    7/8 * 2^-6, -2, 1.875, NaN at the all-ones code."""
+    table = {0x38: 1.0, 0x7E: 448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 / 8 * 2.0 ** -6,
+             0xC0: -2.0, 0x3F: 1.875, 0x00: 0.0}
+    got = OF.e4m3_decode(list(table))
+    assert np.array_equal(got, np.array(list(table.values()))), got
+    assert np.isnan(OF.e4m3_decode([0x7F, 0xFF])).all()
+
+
+def _fp8_case(n, d, seed, hkv=1):
+    rng = np.random.default_rng(seed)
+    q8 = rng.integers(0, 256, (1, n, 1, d)).astype(np.uint8)
+    k8 = rng.integers(0, 256, (1, n, hkv, d)).astype(np.uint8)
+    v8 = rng.integers(0, 256, (1, n, hkv, d)).astype(np.uint8)
+    for x in (q8, k8, v8):   # no NaN codes
+        x[(x & 0x7F) == 0x7F] = 0x38
+    return q8, k8, v8
+
+
+def pin_fp8_forward_equal_keys():
+    """All keys carry the same code vector: every open key scores the same,
+    so O_i is the mean of the open V rows (decoded by torch, times the V
+    descale) and LSE_i = scale * dq * dk * (q_i . k) + ln(open count)."""
+    for _, vec, _, n in _family_cases():
+        d = 4
+        q8, _, v8 = _fp8_case(n, d, 11)
+        k8 = np.broadcast_to(np.array([0x3C, 0xB0, 0x44, 0x28], np.uint8), (1, n, 1, d)).copy()
+        ds = (0.5, 0.25, 1.5)
+        o, lse = OF.forward(q8, k8, v8, ds, _vec3(vec), 0.3)
+        vt = _torch_e4m3(v8)[0, :, 0] * 1.5
+        qk = (_torch_e4m3(q8)[0, :, 0] * 0.5) @ (_torch_e4m3(k8)[0, 0, 0] * 0.25)
+        allowed = ~OA.dense_mask(*vec, np.arange(n))
+        for i in range(n):
+            cnt = allowed[i].sum()
+            if cnt == 0:
+                continue
+            _close(o[0, i, 0], vt[allowed[i]].mean(axis=0), 1e-12, "fp8 equal keys O")
+            _close(lse[0, 0, i], 0.3 * qk[i] + math.log(cnt), 1e-12, "fp8 equal keys LSE")
+
+
+def pin_fp8_forward_diagonal():
+    """Diagonal-only mask: O_i = v_i * dv and LSE_i = scale * dq * dk * q_i . k_i,
+    with every code decoded by torch."""
+    n, d = 19, 8
+    j = np.arange(n)
+    vec = (j + 1, np.full(n, n), np.zeros(n, int), j)
+    q8, k8, v8 = _fp8_case(n, d, 12)
+    ds = (0.125, 2.0, 0.75)
+    o, lse = OF.forward(q8, k8, v8, ds, _vec3(vec), 0.9)
+    qd, kd, vd = (_torch_e4m3(x)[0, :, 0] for x in (q8, k8, v8))
+    _close(o[0, :, 0], vd * 0.75, 1e-12, "fp8 diag O")
+    _close(lse[0, 0], 0.9 * 0.125 * 2.0 * np.einsum("id,id->i", qd, kd), 1e-12, "fp8 diag LSE")
+
+
+def pin_fp8_forward_descale_invariants():
+    """Only the product dq * dk enters the scores, and O is linear in dv:
+    (dq, dk, dv) = (2, 0.5, 3) gives LSE(1, 1, 1) and 3 * O(1, 1, 1); a
+    permutation of the keys (with their bound vectors) changes nothing."""
+    n, d = 29, 6
+    q8, k8, v8 = _fp8_case(n, d, 13)
+    vec = SM.sliding_window_causal(n, 7)
+    o1, l1 = OF.forward(q8, k8, v8, (1.0, 1.0, 1.0), _vec3(vec), 0.2)
+    o2, l2 = OF.forward(q8, k8, v8, (2.0, 0.5, 3.0), _vec3(vec), 0.2)
+    _close(o2, 3.0 * o1, 1e-12, "fp8 dv linear")
+    _close(l2, l1, 1e-12, "fp8 dq*dk")
+    perm = np.random.default_rng(3).permutation(n)
+    vp = tuple(None if x is None else np.asarray(x)[perm] for x in vec)
+    o3, l3 = OF.forward(q8, k8[:, perm], v8[:, perm], (1.0, 1.0, 1.0), _vec3(vp), 0.2)
+    _close(o3, o1, 1e-12, "fp8 key permutation O")
+    _close(l3, l1, 1e-12, "fp8 key permutation LSE")
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -10,6 +10,7 @@ import pytest
 
 import pins
 from oracle import attention as OA
+from oracle import fp8 as OF
 from oracle import masks as OM
 
 F64 = np.float64
@@ -194,11 +195,42 @@ def _chunk_work_factory(variant):
     return chunk_work
 
 
+
+def _e4m3_factory(variant):
+    def e4m3_decode(codes):
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        sign = np.where(c & 0x80, -1.0, 1.0)
+        e = (c >> 3) & 0xF
+        m = (c & 0x7).astype(F64)
+        bias = 8.0 if variant == "bias_8" else 7.0
+        normal = (1.0 + m / 8.0) * np.exp2(e.astype(F64) - bias)
+        sub = (1.0 + m / 8.0) * 2.0 ** -6 if variant == "subnormal_implicit_one" else (m / 8.0) * 2.0 ** -6
+        val = np.where(e == 0, sub, normal)
+        val = np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
+        return sign * val
+    return e4m3_decode
+
+
+def _fp8_forward_factory(variant):
+    def forward(q8, k8, v8, descales, vectors, scale, block=1024):
+        dq, dk, dv = descales
+        if variant == "v_descale_dropped":
+            dv = 1.0
+        if variant == "k_descale_for_v":
+            dv = dk
+        return OA.forward(OF.dequantize(q8, dq), OF.dequantize(k8, dk), OF.dequantize(v8, dv), vectors, scale,
+                          block=block)
+    return forward
+
 def _kv_head_mod(q_heads, kv_heads, h):
     return h % kv_heads
 
 
 MUTATIONS = {
+    "e4m3_bias_8": (OF, "e4m3_decode", _e4m3_factory("bias_8")),
+    "e4m3_subnormal_implicit_one": (OF, "e4m3_decode", _e4m3_factory("subnormal_implicit_one")),
+    "fp8_v_descale_dropped": (OF, "forward", _fp8_forward_factory("v_descale_dropped")),
+    "fp8_k_descale_for_v": (OF, "forward", _fp8_forward_factory("k_descale_for_v")),
     "gqa_head_modulo": (OA, "kv_head", _kv_head_mod),
     "chunk_work_end_inclusive": (OM, "chunk_work", _chunk_work_factory("chunk_end_inclusive")),
     "chunk_work_counts_masked": (OM, "chunk_work", _chunk_work_factory("counts_masked")),
