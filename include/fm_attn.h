@@ -72,8 +72,11 @@ typedef enum {
 
 typedef enum {
   FM_BF16 = 0,   /* bfloat16 inputs and outputs */
-  FM_FP32 = 1    /* float32 inputs and outputs; rounded to bf16 on load for the
+  FM_FP32 = 1,   /* float32 inputs and outputs; rounded to bf16 on load for the
                     matrix products (fp32 accumulation, fp32 softmax state) */
+  FM_FP8_E4M3 = 2 /* forward only (fm_attn_fwd_fp8): q, k, v as OCP E4M3 codes,
+                    one byte each, with one descale factor per tensor; o is
+                    bfloat16 */
 } fm_dtype;
 
 /* Tile classes of the classification pre-pass. */
@@ -98,7 +101,7 @@ typedef struct {
   int64_t stride_h;   /* element stride between head rows of each vector  */
 } fm_mask;
 
-/* Problem description. Strides are in elements, ordered (b, s, h); the head
+/* Problem description. Strides are in elements (bytes for FP8 codes), ordered (b, s, h); the head
  * dimension is contiguous. dO, dQ share the strides of O, Q; dK, dV share
  * those of K, V. Every tensor base pointer must be 16-byte aligned and every
  * (b, s, h) row must start 16-byte aligned. */
@@ -173,6 +176,29 @@ fm_status fm_tile_classify(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen
 fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, const void* v,
                       const fm_mask* mask, void* o, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Forward on 8-bit floating-point inputs ("Современное состояние Flash
+ * Attention на ROCm", kripta.biz, paragraphs on the attention variants and
+ * their ranking: the fastest variant is the FP8 forward; the page names no
+ * format or scaling, the readings here are this library's).
+ * problem->dtype must be FM_FP8_E4M3 and head_dim 128. q [B,Sq,H,128],
+ * k, v [B,Sk,H_kv,128]: device, OCP E4M3 codes (1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; no infinities; the NaN codes 0x7F and 0xFF give
+ * NaN results), strides in bytes, rows 16-byte aligned. descale: host array
+ * of 3 floats (q, k, v), each positive and finite; the operand is code value
+ * times descale. Computes the masked attention of these operands, as
+ * fm_attn_fwd does, with both products on the FP8 matrix cores (fp32
+ * accumulation) and the probabilities rounded to E4M3 for the second product
+ * (they are at most 2^8 there); softmax state, row sums and LSE in fp32.
+ * Outputs: o [B,Sq,H,128] bfloat16 (o_stride in elements), lse [B,H,Sq]
+ * float32. workspace: device, at least fm_workspace_size(.., 0) bytes for
+ * this problem (it includes a V^T copy of B * H_kv * ceil(Sk/64) * 8 KiB),
+ * 256-byte aligned. Errors as fm_attn_fwd; FM_ERR_UNSUPPORTED for another
+ * head_dim. fm_attn_bwd and fm_workspace_size(.., 1) reject FP8 problems
+ * with FM_ERR_UNSUPPORTED. */
+fm_status fm_attn_fwd_fp8(const fm_problem* problem, const void* q, const void* k, const void* v,
+                          const float* descale, const fm_mask* mask, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward. Inputs q, k, v, o (the forward output), lse (the forward LSE),
  * dout (gradient of o), all device. Outputs dq, dk, dv (device, problem
@@ -268,7 +294,8 @@ typedef enum {
   FM_STAGE_ORDER = 9,       /* launch orders, longest tiles first (count, sort) */
   FM_STAGE_TRANSFER = 10,   /* mask-pruned K/V transfer set */
   FM_STAGE_CHUNK_WORK = 11, /* open pairs per chunk of the query axis */
-  FM_NUM_STAGES = 12
+  FM_STAGE_VT = 12,         /* FP8 forward: V^T tile pre-pass */
+  FM_NUM_STAGES = 13
 } fm_stage;
 
 fm_status fm_profile_begin(int32_t max_launches);

@@ -106,6 +106,71 @@ def _problem(q, k, v, o, scale) -> L.fm_problem:
                         st(q), st(k), st(v), st(o), Hkv)
 
 
+def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    """E4M3 codes as a uint8 view (float8_e4m3fn tensors are viewed)."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise ValueError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    return t
+
+
+def _problem_fp8(q, k, v, o, scale) -> L.fm_problem:
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _check_bshd(t, n)
+    if o.dtype != torch.bfloat16:
+        raise ValueError("o must be bfloat16")
+    B, Sq, H, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Sk, Hkv, D) or v.shape != (B, Sk, Hkv, D) or o.shape != (B, Sq, H, D):
+        raise ValueError("shape mismatch between q, k, v, o")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError(f"{Hkv} K/V heads do not divide {H} query heads")
+    if scale is None:
+        scale = D ** -0.5
+    st = lambda t: (C.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+    return L.fm_problem(B, H, Sq, Sk, D, L.FM_FP8_E4M3, float(scale), st(q), st(k), st(v), st(o), Hkv)
+
+
+def fm_attn_fwd_fp8(q, k, v, descale, mask: "Mask", scale=None, o=None, lse=None, workspace=None, stream=None):
+    """Masked attention forward on E4M3 inputs (uint8 codes or
+    float8_e4m3fn tensors) with descale = (q, k, v) factors. Returns (o, lse),
+    o in bfloat16."""
+    q, k, v = _codes(q, "q"), _codes(k, "k"), _codes(v, "v")
+    B, Sq, H, D = q.shape
+    if o is None:
+        o = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq):
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+    ds = [float(x) for x in descale]
+    if len(ds) != 3:
+        raise ValueError("descale must hold 3 factors (q, k, v)")
+    prob = _problem_fp8(q, k, v, o, scale)
+    m = mask._c()
+    lib = L.load()
+    n = C.c_size_t()
+    L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 0, C.byref(n)))
+    ws = _workspace(n.value, q.device, workspace)
+    dsc = (C.c_float * 3)(*ds)
+    L.check(lib.fm_attn_fwd_fp8(C.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), dsc, C.byref(m),
+                                o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return o, lse
+
+
+def fm_workspace_size_fp8(q, k, v, mask: "Mask", scale=None) -> int:
+    """Workspace bytes of fm_attn_fwd_fp8 (includes the V^T tile copy)."""
+    q, k, v = _codes(q, "q"), _codes(k, "k"), _codes(v, "v")
+    B, Sq, H, D = q.shape
+    o = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q.device)
+    prob = _problem_fp8(q, k, v, o, scale)
+    m = mask._c()
+    n = C.c_size_t()
+    L.check(L.load().fm_workspace_size(C.byref(prob), C.byref(m), 0, C.byref(n)))
+    return n.value
+
+
 def fm_kernel_tile(head_dim: int, bwd: bool = False):
     """(block_q, block_k) of the forward or backward kernel."""
     bq, bk = C.c_int32(), C.c_int32()

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfmattn.so")
-SOURCES = ["api.cpp", "plan.cpp", "classify.hip", "localize.hip", "fwd.hip", "bwd.hip", "bwd_ds.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "classify.hip", "localize.hip", "fwd.hip", "fwd_fp8.hip", "bwd.hip", "bwd_ds.hip"]
 ARCH = "gfx950"
 
 

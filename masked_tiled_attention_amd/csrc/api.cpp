@@ -97,17 +97,23 @@ fm_status check_problem(const fm_problem* p) {
     return fail(FM_ERR_INVALID_ARGUMENT, "sequence lengths must be <= %lld", (long long)kMaxSeq);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(FM_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
-  if (p->dtype != FM_BF16 && p->dtype != FM_FP32)
+  if (p->dtype != FM_BF16 && p->dtype != FM_FP32 && p->dtype != FM_FP8_E4M3)
     return fail(FM_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)p->dtype);
+  if (p->dtype == FM_FP8_E4M3 && p->head_dim != 128)
+    return fail(FM_ERR_UNSUPPORTED, "FP8 inputs need head_dim 128 (got %d)", p->head_dim);
   if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale))
     return fail(FM_ERR_INVALID_ARGUMENT, "softmax_scale must be positive and finite");
   if (p->heads_kv < 0 || (p->heads_kv > 0 && p->heads % p->heads_kv))
     return fail(FM_ERR_INVALID_ARGUMENT, "heads_kv %d must be 0 or divide heads %d", p->heads_kv, p->heads);
-  const int64_t es = p->dtype == FM_BF16 ? 2 : 4;
+  // element bytes: inputs and output share the dtype, except that FP8
+  // inputs give a bf16 output
+  const int64_t es_in = p->dtype == FM_BF16 ? 2 : p->dtype == FM_FP32 ? 4 : 1;
+  const int64_t es_out = p->dtype == FM_FP32 ? 4 : 2;
   const int64_t* st[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
   const char* nm[4] = {"q", "k", "v", "o"};
   for (int t = 0; t < 4; ++t)
     for (int i = 0; i < 3; ++i) {
+      const int64_t es = t == 3 ? es_out : es_in;
       if (st[t][i] < 0) return fail(FM_ERR_INVALID_ARGUMENT, "%s stride %d is negative", nm[t], i);
       if ((st[t][i] * es) % 16)
         return fail(FM_ERR_INVALID_ARGUMENT, "%s stride %d (%lld elements) breaks 16-byte row alignment",
@@ -115,7 +121,7 @@ fm_status check_problem(const fm_problem* p) {
     }
   // kernels address one tile (at most 256 rows) with 32-bit byte offsets
   for (int t = 0; t < 4; ++t)
-    if (st[t][1] * es * 256 > INT32_MAX)
+    if (st[t][1] * (t == 3 ? es_out : es_in) * 256 > INT32_MAX)
       return fail(FM_ERR_UNSUPPORTED, "%s sequence stride %lld elements is too large", nm[t], (long long)st[t][1]);
   const int64_t tq = ceil_div(p->seqlen_q, fm::kFwdBlockQ);
   if (tq * p->batch * p->heads > INT32_MAX)
@@ -142,6 +148,7 @@ struct Layout {
   size_t summary = 0, map = 0, summary_q = 0, map_q = 0, lse2 = 0, drow = 0;
   size_t row_cnt = 0, row_off = 0, plan = 0, total = 0, slots = 0, ds = 0;
   size_t counts = 0, order = 0;   // forward launch order
+  size_t vt = 0;                   // FP8 forward: V^T tiles [B][H_kv][Tk][8 KiB]
   size_t order_k = 0, order_qq = 0;   // backward launch orders (counts, then order)
 };
 
@@ -190,6 +197,11 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
     off = align256(off + rows);
     L.order = off;
     off = align256(off + rows);
+    if (p->dtype == FM_FP8_E4M3) {
+      L.vt = off;
+      off = align256(off + (size_t)((int64_t)p->batch * kv_heads(p) * ceil_div(p->seqlen_k, fm::kFwdBlockK) *
+                                    fm::kFwdBlockK * p->head_dim));
+    }
   }
   L.total = off;
   return L;
@@ -221,6 +233,7 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
                     fm::BwdArgs* out, Layout* lay) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
+  if (p->dtype == FM_FP8_E4M3) return fail(FM_ERR_UNSUPPORTED, "the backward takes bf16 or float32 inputs");
   fm::MaskArgs mk;
   st = check_mask(mask, p->batch, p->heads, &mk);
   if (st != FM_OK) return st;
@@ -331,6 +344,8 @@ fm_status fm_workspace_size(const fm_problem* problem, const fm_mask* mask, int3
   st = check_mask(mask, problem->batch, problem->heads, &mk);
   if (st != FM_OK) return st;
   if (!bytes) return fail(FM_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (with_bwd && problem->dtype == FM_FP8_E4M3)
+    return fail(FM_ERR_UNSUPPORTED, "the backward takes bf16 or float32 inputs");
   *bytes = workspace_layout(problem, mask, with_bwd != 0).total;
   return FM_OK;
 }
@@ -355,10 +370,24 @@ fm_status fm_tile_classify(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen
   return classify_into(mk, seqlen_q, seqlen_k, block_q, block_k, transposed ? 1 : 0, summary, classes, stream);
 }
 
-fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v, const fm_mask* mask,
-                      void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Both forwards: validation, classification, launch order, then (FP8) the
+// V^T pre-pass and the FP8 kernel or the bf16/float32 kernel.
+fm_status fwd_common(const fm_problem* p, const void* q, const void* k, const void* v, const float* descale,
+                     const fm_mask* mask, void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
+  const bool fp8 = descale != nullptr;
+  if (fp8 != (p->dtype == FM_FP8_E4M3))
+    return fail(FM_ERR_INVALID_ARGUMENT, fp8 ? "fm_attn_fwd_fp8 needs dtype FM_FP8_E4M3"
+                                             : "FP8 inputs go to fm_attn_fwd_fp8");
+  if (fp8)
+    for (int i = 0; i < 3; ++i)
+      if (!(descale[i] > 0.f) || !std::isfinite(descale[i]))
+        return fail(FM_ERR_INVALID_ARGUMENT, "descale %d must be positive and finite", i);
   fm::MaskArgs mk;
   st = check_mask(mask, p->batch, p->heads, &mk);
   if (st != FM_OK) return st;
@@ -414,11 +443,46 @@ fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const v
   if (e != hipSuccess) return hip_fail(e, "forward order launch");
   a.order = oa.order;
   a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
-  a.group = p->heads / kv_heads(p);
-  e = run_stage(FM_STAGE_FWD, stream,
-                           [&] { return fm::launch_fwd(a, p->head_dim, p->dtype == FM_FP32, stream); });
+  a.heads_kv = kv_heads(p);
+  a.group = p->heads / a.heads_kv;
+  a.o_scale = 1.f;
+  if (fp8) {
+    if ((int64_t)p->batch * a.heads_kv * tk > INT32_MAX) return fail(FM_ERR_INVALID_ARGUMENT, "problem too large");
+    fm::VtArgs va{};
+    va.v = static_cast<const uint8_t*>(v);
+    va.v_sb = p->v_stride[0]; va.v_ss = p->v_stride[1]; va.v_sh = p->v_stride[2];
+    va.batch = p->batch;
+    va.heads_kv = a.heads_kv;
+    va.seq_k = p->seqlen_k;
+    va.tk = tk;
+    va.vt = reinterpret_cast<uint8_t*>(w + L.vt);
+    e = run_stage(FM_STAGE_VT, stream, [&] { return fm::launch_vt(va, stream); });
+    if (e != hipSuccess) return hip_fail(e, "V transpose launch");
+    a.vt = va.vt;
+    a.scale_log2 = p->softmax_scale * descale[0] * descale[1] * 1.4426950408889634f;
+    a.o_scale = descale[2];
+    e = run_stage(FM_STAGE_FWD, stream, [&] { return fm::launch_fwd_fp8(a, stream); });
+  } else {
+    e = run_stage(FM_STAGE_FWD, stream,
+                  [&] { return fm::launch_fwd(a, p->head_dim, p->dtype == FM_FP32, stream); });
+  }
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return FM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v, const fm_mask* mask,
+                      void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return fwd_common(p, q, k, v, nullptr, mask, o, lse, ws, ws_bytes, stream);
+}
+
+fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, const void* v, const float* descale,
+                          const fm_mask* mask, void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!descale) return fail(FM_ERR_INVALID_ARGUMENT, "descale is NULL");
+  return fwd_common(p, q, k, v, descale, mask, o, lse, ws, ws_bytes, stream);
 }
 
 fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const void* v, const void* o,

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "fm_attn.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -154,3 +154,61 @@ def test_classify_rejects_bad_blocks():
 def test_profile_end_without_begin_fails():
     lib = L.load()
     assert lib.fm_profile_end(None, None) == L.FM_ERR_INVALID_ARGUMENT
+
+
+def _fwd_fp8(prob, mask, descale=(1.0, 1.0, 1.0)):
+    lib = L.load()
+    ds = None if descale is None else (C.c_float * 3)(*descale)
+    return lib.fm_attn_fwd_fp8(C.byref(prob), FAKE, FAKE, FAKE, ds, C.byref(mask), FAKE, FAKE, FAKE, 1 << 30, None)
+
+
+def _problem_fp8(D=128, hkv=0):
+    H, Sq, Sk = 2, 100, 120
+    nk = hkv or H
+    arr = lambda s: (C.c_int64 * 3)(*s)
+    return L.fm_problem(1, H, Sq, Sk, D, L.FM_FP8_E4M3, 0.1, arr((Sq * H * D, H * D, D)),
+                        arr((Sk * nk * D, nk * D, D)), arr((Sk * nk * D, nk * D, D)), arr((Sq * H * D, H * D, D)), hkv)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("head_dim_64", L.FM_ERR_UNSUPPORTED),
+    ("bf16_problem", L.FM_ERR_INVALID_ARGUMENT),
+    ("null_descale", L.FM_ERR_INVALID_ARGUMENT),
+    ("zero_descale", L.FM_ERR_INVALID_ARGUMENT),
+    ("nan_descale", L.FM_ERR_INVALID_ARGUMENT),
+])
+def test_fwd_fp8_rejects(case, expect):
+    prob, ds = _problem_fp8(), (1.0, 1.0, 1.0)
+    if case == "head_dim_64":
+        prob = _problem_fp8(D=64)
+    elif case == "bf16_problem":
+        prob = _problem(D=128)
+    elif case == "null_descale":
+        ds = None
+    elif case == "zero_descale":
+        ds = (1.0, 0.0, 1.0)
+    elif case == "nan_descale":
+        ds = (1.0, 1.0, float("nan"))
+    assert _fwd_fp8(prob, _mask(), ds) == expect
+    assert L.load().fm_last_error()
+
+
+def test_fp8_problem_rejected_by_bf16_forward_and_backward():
+    lib = L.load()
+    prob, mask = _problem_fp8(), _mask()
+    assert _fwd(prob, mask) == L.FM_ERR_INVALID_ARGUMENT
+    n = C.c_size_t()
+    assert lib.fm_workspace_size(C.byref(prob), C.byref(mask), 1, C.byref(n)) == L.FM_ERR_UNSUPPORTED
+    assert lib.fm_attn_bwd(C.byref(prob), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, C.byref(mask), FAKE, FAKE, FAKE,
+                           FAKE, 1 << 30, None) == L.FM_ERR_UNSUPPORTED
+
+
+def test_fp8_workspace_holds_the_v_transpose():
+    """The FP8 forward's workspace exceeds the bf16 one by at least the V^T
+    copy: B * H_kv * ceil(Sk / 64) * 64 * 128 bytes."""
+    lib = L.load()
+    mask = _mask()
+    a, b = C.c_size_t(), C.c_size_t()
+    assert lib.fm_workspace_size(C.byref(_problem(D=128)), C.byref(mask), 0, C.byref(a)) == L.FM_OK
+    assert lib.fm_workspace_size(C.byref(_problem_fp8()), C.byref(mask), 0, C.byref(b)) == L.FM_OK
+    assert b.value - a.value >= 1 * 2 * 2 * 64 * 128
