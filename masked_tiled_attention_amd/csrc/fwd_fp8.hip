@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
 // ---------------------------------------------------------------- forward
 struct alignas(16) Fp8Smem {
   uint8_t k[2][TILE_BYTES];    // K tiles: 128-byte rows, 16-byte chunks swizzled by row
-  uint8_t vt[2][TILE_BYTES];   // V^T tiles as the pre-pass wrote them
+  uint8_t vt[3][TILE_BYTES];   // V^T tiles as the pre-pass wrote them (three: a tile's PV runs in the next iteration)
   int32_t bnd[2][4][BK];       // lts, lte, uts, ute of the tile's keys
   uint32_t list[LIST_CAP];     // non-SKIP key tiles (kt | partial bit)
   int32_t scan[NW];
@@ -165,11 +165,11 @@ void fwd_fp8_kernel(FwdArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   int32_t rb[4] = {INT_MIN, INT_MAX, 0, 0};
 
-  auto load_tile = [&](int kt, bool masked, int buf) {
+  auto load_tile = [&](int kt, bool masked, int buf, int vbuf) {
     const int n0 = kt * BK;
     Dma::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff, k_ld, tid, a.seq_k - n0);
     const char* src = vth + (int64_t)kt * TILE_BYTES;
-    const uint32_t dst = Dma::lds_address(reinterpret_cast<const char*>(sm.vt[buf]));
+    const uint32_t dst = Dma::lds_address(reinterpret_cast<const char*>(sm.vt[vbuf]));
 #pragma unroll
     for (int i = 0; i < TILE_BYTES / 1024 / NW; ++i) {
       const int blk = i * NW + wu;
@@ -261,19 +261,46 @@ void fwd_fp8_kernel(FwdArgs a) {
     l_run += rs;
   };
 
+  // O^T += V^T P^T for a tile whose probabilities are in `p`, its V^T in
+  // LDS buffer vbuf.
+  auto pv = [&](const i32x8& p, int vbuf) {
+    const char* vb = reinterpret_cast<const char*>(sm.vt[vbuf]);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int c = 32 * cb + lr;
+      const i32x8 va = cat8(*reinterpret_cast<const u32x4*>(vb + (2 * g) * PLANE + 16 * c),
+                            *reinterpret_cast<const u32x4*>(vb + (2 * g + 1) * PLANE + 16 * c));
+      oacc[cb] = mfma_fp8(va, p, oacc[cb]);
+    }
+  };
+
+  // Software pipeline: iteration t forms S and the probabilities of tile t
+  // while the PV product of tile t-1 runs on the matrix cores. The reference
+  // may move at tile t only after that product has entered O, which the
+  // program order guarantees (the rescale reads O after the MFMAs wrote it).
+  // The first iteration's "previous tile" is V^T buffer 2, zeroed here, with
+  // zero probabilities, so that every iteration runs the same straight-line
+  // code (a branch would split the block and keep the scheduler from
+  // interleaving the product with the softmax). Buffer 2 is first written in
+  // the second iteration, after a barrier.
+  st16(sm.vt[2] + 32 * tid, u32x4{0u, 0u, 0u, 0u});
+  st16(sm.vt[2] + 32 * tid + 16, u32x4{0u, 0u, 0u, 0u});
   int it_global = 0;
+  int vrot = 0;             // V^T buffer of the current tile (it_global mod 3)
+  i32x8 pf_prev = {0, 0, 0, 0, 0, 0, 0, 0};   // probabilities of the previous tile, not yet in O
   auto iteration = [&](auto masked_c, int it, int n_list, uint32_t& ent) {
     constexpr bool MASKED = decltype(masked_c)::value;
     const int buf = it_global & 1;
+    const int vnext = vrot == 2 ? 0 : vrot + 1;
+    const int vprev = vrot == 0 ? 2 : vrot - 1;
     store_bounds(buf, MASKED);
     wait_vmem();
     __syncthreads();
     if (it + 1 < n_list) {
       ent = __builtin_amdgcn_readfirstlane(sm.list[it + 1]);
-      load_tile((int)(ent & ~kPartialBit), (ent & kPartialBit) != 0, buf ^ 1);
+      load_tile((int)(ent & ~kPartialBit), (ent & kPartialBit) != 0, buf ^ 1, vnext);
     }
     const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
-    const char* vb = reinterpret_cast<const char*>(sm.vt[buf]);
     f32x16 sacc[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -286,18 +313,14 @@ void fwd_fp8_kernel(FwdArgs a) {
         sacc[nb] = mfma_fp8(ka, qf[s], sacc[nb]);
       }
     }
+    pv(pf_prev, vprev);
     if constexpr (MASKED) mask_half(sacc[0], 0, buf);
     const float rs0 = soft_half(sacc[0], 0);
     if constexpr (MASKED) mask_half(sacc[1], 1, buf);
     const float rs1 = soft_half(sacc[1], 1);
     settle_tile(sacc, rs0 + rs1);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int c = 32 * cb + lr;
-      const i32x8 va = cat8(*reinterpret_cast<const u32x4*>(vb + (2 * g) * PLANE + 16 * c),
-                            *reinterpret_cast<const u32x4*>(vb + (2 * g + 1) * PLANE + 16 * c));
-      oacc[cb] = mfma_fp8(va, pf, oacc[cb]);
-    }
+    pf_prev = pf;
+    vrot = vnext;
   };
 
   for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
@@ -306,11 +329,17 @@ void fwd_fp8_kernel(FwdArgs a) {
                                                            sm.scan, tid, false, &n_full, ragged_k ? a.tk - 1 : -1);
     if (n_list == 0) continue;
     uint32_t ent = __builtin_amdgcn_readfirstlane(sm.list[0]);
-    load_tile((int)(ent & ~kPartialBit), (ent & kPartialBit) != 0, it_global & 1);
+    load_tile((int)(ent & ~kPartialBit), (ent & kPartialBit) != 0, it_global & 1, vrot);
     int it = 0;
     for (; it < n_full; ++it, ++it_global) iteration(std::false_type{}, it, n_list, ent);
     for (; it < n_list; ++it, ++it_global) iteration(std::true_type{}, it, n_list, ent);
   }
+  pv(pf_prev, vrot == 0 ? 2 : vrot - 1);   // the last tile's product
+  // Hold the product here, with every lane active: left alone, the compiler
+  // sinks these MFMAs into the row_ok branch below, and an MFMA issued with
+  // lanes masked off loses the operand rows those lanes hold.
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) asm volatile("" : "+v"(oacc[cb]));
 
   // ---- epilogue: normalise once (the V descale folded in), write bf16 O and LSE ----
   const float lt = pair_sum(l_run);
