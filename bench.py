@@ -25,6 +25,7 @@ import numpy as np
 
 METRIC = "masked attn fwd/bwd TFLOP/s on unmasked FLOPs, % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2      # MI355X dense fp8 MFMA: twice the bf16 rate
 PEAK_HBM_GBS = 8000.0
 HEADLINE = "c4_doc_causal_128k"
 
@@ -52,7 +53,8 @@ def measured_traffic(kernel: str, workload: str):
     import hashlib
     import re
     root = os.path.dirname(os.path.abspath(__file__))
-    src = {"fwd": "fwd.hip", "bwd": "bwd.hip", "bwd_dq": "bwd.hip", "bwd_dq_ds": "bwd_ds.hip"}.get(kernel)
+    src = {"fwd": "fwd.hip", "bwd": "bwd.hip", "bwd_dq": "bwd.hip", "bwd_dq_ds": "bwd_ds.hip",
+           "fwd_fp8": "fwd_fp8.hip"}.get(kernel)
     if src is None:
         return None
     with open(os.path.join(root, "masked_tiled_attention_amd", "csrc", src), "rb") as f:
@@ -151,6 +153,32 @@ class Runner:
         return 4 * d * self.nnz, (10 * d * self.nnz if self.w.backward else 0)
 
 
+class Fp8Runner:
+    """The FP8 forward (E4M3 codes of the workload's shape, descales 1/64)
+    on device-resident inputs."""
+
+    def __init__(self, fm, w, torch, seed):
+        from synth import tensors as ST
+        dev = "cuda"
+        self.fm, self.w = fm, w
+        shp_q = (w.batch, w.seq_q, w.heads, w.head_dim)
+        shp_k = (w.batch, w.seq_k, w.heads, w.head_dim)
+        self.q = ST.fp8_codes("q", shp_q, seed).to(dev)
+        self.k = ST.fp8_codes("k", shp_k, seed).to(dev)
+        self.v = ST.fp8_codes("v", shp_k, seed).to(dev)
+        self.ds = (1 / 64, 1 / 64, 1 / 64)
+        self.mask = fm.Mask.from_vectors(w.vectors, dev)
+        self.o = torch.empty(shp_q, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.batch, w.heads, w.seq_q), dtype=torch.float32, device=dev)
+        n = fm.fm_workspace_size_fp8(self.q, self.k, self.v, self.mask, w.scale)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.nnz = nnz_of(w.vectors, w.seq_q, w.batch, w.heads)
+
+    def step(self):
+        self.fm.fm_attn_fwd_fp8(self.q, self.k, self.v, self.ds, self.mask, self.w.scale, o=self.o, lse=self.lse,
+                                workspace=self.ws)
+
+
 def time_steps(r, steps, warmup, torch, profile=True):
     fm = r.fm
     for _ in range(warmup):
@@ -214,6 +242,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-store-ds", action="store_true",
                     help="minimum backward workspace: dQ recomputes S and dP instead of reading stored dS")
+    ap.add_argument("--fp8-forward", action="store_true",
+                    help="time only the FP8 forward (E4M3 codes of the workload's shape) and print its line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -244,6 +274,26 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] reference copy: {nbytes} bytes read, {nbytes} bytes written")
         del src, dst
+
+    if args.fp8_forward:
+        w = SC.build(args.workload, args.seed, tensors=False)
+        r = Fp8Runner(fm, w, torch, args.seed)
+        ms, stages = time_steps(r, args.steps, args.warmup, torch)
+        per = lambda s: stages[s][0] / max(1, args.steps)
+        flops = 4 * w.head_dim * r.nnz
+        kms = stages["fwd"][0] / max(1, stages["fwd"][1])
+        achieved = flops / (kms * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": "fp8_forward_throughput", "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "dtype": "fp8_e4m3", "data": "synthetic",
+            "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_q": w.seq_q, "seq_k": w.seq_k,
+                       "head_dim": w.head_dim, "nnz": r.nnz, "passes": "fwd"},
+            "stages_ms_per_step": {s_: round(v[0] / max(1, args.steps), 4) for s_, v in stages.items() if v[1]},
+            "roofline": {"bound": "mfma", "kernel": "fwd_fp8", "kernel_ms": round(kms, 4), "achieved": round(achieved, 2),
+                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                         "traffic": measured_traffic("fwd_fp8", w.name)}}), flush=True)
+        return
 
     log(f"[bench] building {args.workload} seed {args.seed}")
     w = SC.build(args.workload, args.seed)
@@ -341,6 +391,25 @@ def main():
             del rx
             torch.cuda.empty_cache()
         out["workloads"] = sweep
+        # the FP8 forward (E4M3 inputs) on the long workloads, beside the bf16
+        # forward kernel of the same workload
+        fp8 = []
+        bf16_fwd = {it["workload"]: it.get("fwd_kernel_tflops") for it in sweep}
+        bf16_fwd[w.name] = round(f_fwd / (per("fwd") * 1e-3) / 1e12, 2)
+        for name in ("c3b_prefix_lm_32k", "c4_causal_128k", "c4_doc_causal_128k"):
+            log(f"[bench] fp8 forward {name}")
+            wx = SC.build(name, args.seed, tensors=False)
+            rx = Fp8Runner(fm, wx, torch, args.seed)
+            msx, st = time_steps(rx, 5, 2, torch)
+            pf = lambda s: st[s][0] / 5
+            kt = 4 * wx.head_dim * rx.nnz / (pf("fwd") * 1e-3) / 1e12
+            fp8.append({"workload": name, "nnz": rx.nnz, "ms_per_call": round(msx, 4),
+                        "fwd_kernel_ms": round(pf("fwd"), 4), "v_transpose_ms": round(pf("v_transpose"), 4),
+                        "fwd_kernel_tflops": round(kt, 2), "frac_of_fp8_peak": round(kt / PEAK_FP8_TFLOPS, 4),
+                        "bf16_fwd_kernel_tflops": bf16_fwd.get(name)})
+            del rx
+            torch.cuda.empty_cache()
+        out["fp8_forward"] = fp8
     print(json.dumps(out), flush=True)
 
 
