@@ -225,7 +225,10 @@ void fwd_fp8_kernel(FwdArgs a) {
       const float p1 = fast_exp2(fmaf(sc[4 * d + 1], C, nmC));
       const float p2 = fast_exp2(fmaf(sc[4 * d + 2], C, nmC));
       const float p3 = fast_exp2(fmaf(sc[4 * d + 3], C, nmC));
-      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      // The low-half conversion keeps the register's upper bytes, which the
+      // high-half conversion then replaces: passing the dead old contents
+      // (rather than 0) saves zeroing the register first.
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf[4 * nb + d], false);
       pf[4 * nb + d] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, lo, true);
       r0 += p0 + p2;
       r1 += p1 + p3;
