@@ -192,3 +192,36 @@ def test_fp8_prefix_lm_32k_sampled(gpu_lib):
         bound = vmax * (2.0 ** -4 + 2.0 ** -10 * n_small / p.sum(axis=1))
         _check_o(o[0, rows, h], ro, bound, f"prefix-LM 32k h{h}")
         assert_close(lse[0, h, rows], rl, f"prefix-LM 32k h{h} LSE")
+
+
+@pytest.mark.parametrize("name", ["c4_doc_causal_128k", "c4_causal_128k"])
+def test_fp8_128k_sampled(gpu_lib, name):
+    """The FP8 forward in the configuration the benchmark times (the 128K
+    workloads' shape and mask, E4M3 codes with descales 1/64), checked on
+    sampled rows of two heads against the oracle, each within its row's
+    bound, and LSE within the float bar."""
+    from synth import configs as SC
+    w = SC.build(name, seed=0, tensors=False)
+    n, H = w.seq_q, w.heads
+    q8, k8, v8, ds = _codes(w.batch, n, n, H, H, seed=0)
+    log(f"fp8 fwd {name}: running")
+    o, lse = gpu_lib.fm_attn_fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), ds, dev_mask(w.vectors), w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = np.concatenate([rng.choice(n, 24, replace=False), [0, 1, n // 2, n - 1]])
+    qn, kn, vn = q8.numpy(), k8.numpy(), v8.numpy()
+    kd, vd = OF.dequantize(kn, ds[1]), OF.dequantize(vn, ds[2])
+    qd = OF.dequantize(qn[:, rows], ds[0])
+    o = np64(o[:, rows])
+    lse = lse[:, :, rows].double().cpu().numpy()
+    for h in (0, H - 1):
+        ro, rl = OF.forward_rows(qn, kn, vn, ds, w.vectors, w.scale, 0, h, rows)
+        masked = OA.dense_mask(*OA.vectors_for(w.vectors, 0, h), rows, n)
+        s = w.scale * (qd[0, :, h] @ kd[0, :, h].T)
+        s[masked] = -np.inf
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        n_small = ((p < 2.0 ** -6) & ~masked).sum(axis=1)
+        vmax = np.where(~masked, np.abs(vd[0, :, h]).max(axis=1)[None, :], 0.0).max(axis=1)
+        bound = vmax * (2.0 ** -4 + 2.0 ** -10 * n_small / p.sum(axis=1))
+        _check_o(o[0, :, h], ro, bound, f"{name} h{h}")
+        assert_close(lse[0, h], rl, f"{name} h{h} LSE")
