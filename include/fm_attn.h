@@ -181,8 +181,8 @@ fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, c
  * Attention на ROCm", kripta.biz, paragraphs on the attention variants and
  * their ranking: the fastest variant is the FP8 forward; the page names no
  * format or scaling, the readings here are this library's).
- * problem->dtype must be FM_FP8_E4M3 and head_dim 128. q [B,Sq,H,128],
- * k, v [B,Sk,H_kv,128]: device, OCP E4M3 codes (1 sign, 4 exponent bits with
+ * problem->dtype must be FM_FP8_E4M3 (head_dim 64 or 128). q [B,Sq,H,D],
+ * k, v [B,Sk,H_kv,D]: device, OCP E4M3 codes (1 sign, 4 exponent bits with
  * bias 7, 3 mantissa bits; no infinities; the NaN codes 0x7F and 0xFF give
  * NaN results), strides in bytes, rows 16-byte aligned. descale: host array
  * of 3 floats (q, k, v), each positive and finite; the operand is code value
@@ -190,11 +190,10 @@ fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, c
  * fm_attn_fwd does, with both products on the FP8 matrix cores (fp32
  * accumulation) and the probabilities rounded to E4M3 for the second product
  * (they are at most 2^8 there); softmax state, row sums and LSE in fp32.
- * Outputs: o [B,Sq,H,128] bfloat16 (o_stride in elements), lse [B,H,Sq]
+ * Outputs: o [B,Sq,H,D] bfloat16 (o_stride in elements), lse [B,H,Sq]
  * float32. workspace: device, at least fm_workspace_size(.., 0) bytes for
- * this problem (it includes a V^T copy of B * H_kv * ceil(Sk/64) * 8 KiB),
- * 256-byte aligned. Errors as fm_attn_fwd; FM_ERR_UNSUPPORTED for another
- * head_dim. fm_attn_bwd and fm_workspace_size(.., 1) reject FP8 problems
+ * this problem (it includes a V^T copy of B * H_kv * ceil(Sk/64) * 64 * D
+ * bytes), 256-byte aligned. Errors as fm_attn_fwd. fm_attn_bwd and fm_workspace_size(.., 1) reject FP8 problems
  * with FM_ERR_UNSUPPORTED. */
 fm_status fm_attn_fwd_fp8(const fm_problem* problem, const void* q, const void* k, const void* v,
                           const float* descale, const fm_mask* mask, void* o, float* lse,

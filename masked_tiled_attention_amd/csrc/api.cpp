@@ -99,8 +99,6 @@ fm_status check_problem(const fm_problem* p) {
     return fail(FM_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
   if (p->dtype != FM_BF16 && p->dtype != FM_FP32 && p->dtype != FM_FP8_E4M3)
     return fail(FM_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)p->dtype);
-  if (p->dtype == FM_FP8_E4M3 && p->head_dim != 128)
-    return fail(FM_ERR_UNSUPPORTED, "FP8 inputs need head_dim 128 (got %d)", p->head_dim);
   if (!(p->softmax_scale > 0.f) || !std::isfinite(p->softmax_scale))
     return fail(FM_ERR_INVALID_ARGUMENT, "softmax_scale must be positive and finite");
   if (p->heads_kv < 0 || (p->heads_kv > 0 && p->heads % p->heads_kv))
@@ -456,12 +454,12 @@ fm_status fwd_common(const fm_problem* p, const void* q, const void* k, const vo
     va.seq_k = p->seqlen_k;
     va.tk = tk;
     va.vt = reinterpret_cast<uint8_t*>(w + L.vt);
-    e = run_stage(FM_STAGE_VT, stream, [&] { return fm::launch_vt(va, stream); });
+    e = run_stage(FM_STAGE_VT, stream, [&] { return fm::launch_vt(va, p->head_dim, stream); });
     if (e != hipSuccess) return hip_fail(e, "V transpose launch");
     a.vt = va.vt;
     a.scale_log2 = p->softmax_scale * descale[0] * descale[1] * 1.4426950408889634f;
     a.o_scale = descale[2];
-    e = run_stage(FM_STAGE_FWD, stream, [&] { return fm::launch_fwd_fp8(a, stream); });
+    e = run_stage(FM_STAGE_FWD, stream, [&] { return fm::launch_fwd_fp8(a, p->head_dim, stream); });
   } else {
     e = run_stage(FM_STAGE_FWD, stream,
                   [&] { return fm::launch_fwd(a, p->head_dim, p->dtype == FM_FP32, stream); });

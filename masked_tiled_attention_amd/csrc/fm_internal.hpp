@@ -58,14 +58,14 @@ struct FwdArgs {
   const int32_t* order;
   int32_t rep;             // (b, h) pairs per mask row
   int32_t group;           // query heads per K/V head: K/V head = h / group
-  // FP8 forward only: V^T tiles from the pre-pass ([B][H_kv][tk][8 KiB]),
+  // FP8 forward only: V^T tiles from the pre-pass ([B][H_kv][tk][64 * D bytes]),
   // K/V heads, and the factor applied to O at the end (the V descale).
   const uint8_t* vt;
   int32_t heads_kv;
   float o_scale;
 };
 
-// V^T pre-pass of the FP8 forward: V [B][Sk][H_kv][128] E4M3 codes (strides
+// V^T pre-pass of the FP8 forward: V [B][Sk][H_kv][D] E4M3 codes (strides
 // in bytes) to 64-key tiles of four [128 channel][16 key] planes.
 struct VtArgs {
   const uint8_t* v;
@@ -174,8 +174,8 @@ struct ChunkWorkArgs {
 hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream);
 hipError_t launch_classify_map(const ClassifyArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f32, hipStream_t stream);
-hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_vt(const VtArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);

@@ -20,10 +20,14 @@ constexpr uint32_t kPartialBit = 0x80000000u;   // list entry flag: tile needs t
 //     consecutive rows differ in the chunk-group bits [3:2].
 //   D = 64 (128-byte rows, two rows per bank sweep): a bijection of r[3:1]
 //     with r[1] on chunk bit 2.
+//   D = 32 (64-byte rows, four rows per bank sweep; the 64-byte FP8 rows of
+//     head dimension 64): r[3:2] on the two chunk bits.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (D == 128) {
     return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else if constexpr (D == 32) {
+    return (r >> 2) & 3;
   } else {
     return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
   }

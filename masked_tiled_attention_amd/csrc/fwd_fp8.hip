@@ -1,5 +1,5 @@
 // Forward kernel on 8-bit floating-point inputs (OCP E4M3, per-tensor
-// descales), head dimension 128.
+// descales), head dimension 64 or 128.
 //
 // "Современное состояние Flash Attention на ROCm" (kripta.biz), paragraphs on
 // the attention variants and their ranking: the fastest variant runs the
@@ -16,15 +16,16 @@
 // CDNA4 with FP8:
 //   S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (scales fixed at 1):
 //     lane l holds row (l & 31) and 32 consecutive bytes of the contraction
-//     for half l >> 5, so a K row feeds A with two 16-byte LDS reads and the
-//     wavefront's Q rows sit in 16 registers for the whole kernel.
+//     for half l >> 5, so a K row feeds A with two 16-byte LDS reads per 64
+//     channels and the wavefront's Q rows sit in registers (8 per 64
+//     channels) for the whole kernel.
 //   O^T += V^T P^T contracts 64 keys per instruction: P comes straight from
 //     the two S^T accumulators of a tile, register i of 32-key block nb being
 //     byte 16 nb + i of the lane's operand, converted with v_cvt_pk_fp8_f32.
 //     The A operand needs V^T with the same key order; a pre-pass writes,
 //     per 64-key tile, four planes (lane half g, 16-key group kc) of
-//     [128 channels][16 bytes] whose byte t is key 32 kc + 8 (t / 4) + 4 g +
-//     t % 4, zero past the sequence end. The kernel copies these 8 KiB tiles
+//     [D channels][16 bytes] whose byte t is key 32 kc + 8 (t / 4) + 4 g +
+//     t % 4, zero past the sequence end. The kernel copies these D * 64-byte tiles
 //     into LDS unchanged, and each lane reads its channel's two 16-byte
 //     pieces, 16 bytes apart from the neighbouring lane's.
 // Probabilities never exceed 2^8 (the rescale threshold of the max-free
@@ -42,15 +43,14 @@
 namespace fm {
 namespace {
 
-constexpr int D = 128;
 constexpr int BQ = kFwdBlockQ;   // 128 query rows per workgroup
 constexpr int BK = kFwdBlockK;   // 64 keys per K/V tile
 constexpr int NW = BQ / 32;      // 4 wavefronts
 constexpr int NT = NW * 64;      // 256 threads
 constexpr int LIST_CAP = 1024;
-constexpr int TILE_BYTES = BK * D;   // one K tile or one V^T tile: 8 KiB
-constexpr int PLANE = D * 16;        // one (g, kc) plane of a V^T tile: 2 KiB
 constexpr float kRescaleMax = 256.0f;
+template <int D> constexpr int kTileBytes = BK * D;   // one K tile or one V^T tile
+template <int D> constexpr int kPlane = D * 16;       // one (g, kc) plane of a V^T tile
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
@@ -65,9 +65,11 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 
 // ---------------------------------------------------------------- V^T pre-pass
 // One workgroup per (b, K/V head, 64-key tile): the tile's V rows go to LDS
-// as loaded, then each thread assembles two 16-byte plane pieces (plane
-// u / 128, channel u % 128) from bytes of 16 keys of one channel.
+// as loaded, then each thread assembles D / 64 16-byte plane pieces (plane
+// u / D, channel u % D) from bytes of 16 keys of one channel.
+template <int D>
 __global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
+  constexpr int CPT = D / 64;   // 16-byte pieces per thread, in and out
   __shared__ uint8_t s[BK][D];
   const int tid = threadIdx.x;
   const int kt = blockIdx.x % a.tk;
@@ -75,22 +77,18 @@ __global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
   const int hk = bh % a.heads_kv, b = bh / a.heads_kv;
   const int n0 = kt * BK;
   {
-    const int r = tid >> 2, c0 = 32 * (tid & 3);
-    u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-    if (n0 + r < a.seq_k) {
-      const uint8_t* src = a.v + (int64_t)b * a.v_sb + (int64_t)(n0 + r) * a.v_ss + (int64_t)hk * a.v_sh + c0;
-      x0 = ld16(src);
-      x1 = ld16(src + 16);
-    }
-    st16(&s[r][c0], x0);
-    st16(&s[r][c0 + 16], x1);
+    const int r = tid >> 2, c0 = (D / 4) * (tid & 3);
+    const bool ok = n0 + r < a.seq_k;
+    const uint8_t* src = a.v + (int64_t)b * a.v_sb + (int64_t)(n0 + r) * a.v_ss + (int64_t)hk * a.v_sh + c0;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) st16(&s[r][c0 + 16 * i], ok ? ld16(src + 16 * i) : u32x4{0u, 0u, 0u, 0u});
   }
   __syncthreads();
-  uint8_t* dst = a.vt + ((int64_t)bh * a.tk + kt) * TILE_BYTES;
+  uint8_t* dst = a.vt + ((int64_t)bh * a.tk + kt) * kTileBytes<D>;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < CPT; ++i) {
     const int u = tid + 256 * i;
-    const int plane = u >> 7, c = u & 127;
+    const int plane = u / D, c = u % D;
     const int g = plane >> 1, kc = plane & 1;
     u32x4 o;
 #pragma unroll
@@ -104,20 +102,26 @@ __global__ __launch_bounds__(256) void vt_kernel(VtArgs a) {
 }
 
 // ---------------------------------------------------------------- forward
+template <int D>
 struct alignas(16) Fp8Smem {
-  uint8_t k[2][TILE_BYTES];    // K tiles: 128-byte rows, 16-byte chunks swizzled by row
-  uint8_t vt[3][TILE_BYTES];   // V^T tiles as the pre-pass wrote them (three: a tile's PV runs in the next iteration)
+  uint8_t k[2][kTileBytes<D>];    // K tiles: D-byte rows, 16-byte chunks swizzled by row
+  uint8_t vt[3][kTileBytes<D>];   // V^T tiles as the pre-pass wrote them (three: a tile's PV runs in the next iteration)
   int32_t bnd[2][4][BK];       // lts, lte, uts, ute of the tile's keys
   uint32_t list[LIST_CAP];     // non-SKIP key tiles (kt | partial bit)
   int32_t scan[NW];
 };
 
+template <int D>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_fp8_kernel(FwdArgs a) {
-  constexpr int CB = D / 32;   // 32-channel blocks of O^T
-  // A 128-byte K row has the chunk layout of a 64-element bf16 row.
-  using Dma = DmaTile<64, BK, NT>;
-  __shared__ Fp8Smem sm;
+  constexpr int CB = D / 32;       // 32-channel blocks of O^T
+  constexpr int KS = D / 64;       // 64-channel contraction steps of S
+  constexpr int TILE_BYTES = kTileBytes<D>;
+  constexpr int PLANE = kPlane<D>;
+  // A D-byte K row has the chunk layout of a (D / 2)-element bf16 row.
+  constexpr int DB = D / 2;
+  using Dma = DmaTile<DB, BK, NT>;
+  __shared__ Fp8Smem<D> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -140,13 +144,13 @@ void fwd_fp8_kernel(FwdArgs a) {
   const bool row_ok = m < a.seq_q;
 
   // Q rows as B operands: bytes 64 s + 32 g .. + 31 of the lane's row.
-  i32x8 qf[2];
+  i32x8 qf[KS];
   {
     const int mq = min(m, a.seq_q - 1);
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(a.q) + (int64_t)b * a.q_sb + (int64_t)mq * a.q_ss +
                         (int64_t)h * a.q_sh + 32 * g;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) qf[s] = cat8(ld16(qp + 64 * s), ld16(qp + 64 * s + 16));
+    for (int s = 0; s < KS; ++s) qf[s] = cat8(ld16(qp + 64 * s), ld16(qp + 64 * s + 16));
   }
 
   f32x16 oacc[CB];
@@ -286,8 +290,8 @@ void fwd_fp8_kernel(FwdArgs a) {
   // code (a branch would split the block and keep the scheduler from
   // interleaving the product with the softmax). Buffer 2 is first written in
   // the second iteration, after a barrier.
-  st16(sm.vt[2] + 32 * tid, u32x4{0u, 0u, 0u, 0u});
-  st16(sm.vt[2] + 32 * tid + 16, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+  for (int o = 16 * tid; o < TILE_BYTES; o += 16 * NT) st16(sm.vt[2] + o, u32x4{0u, 0u, 0u, 0u});
   int it_global = 0;
   int vrot = 0;             // V^T buffer of the current tile (it_global mod 3)
   i32x8 pf_prev = {0, 0, 0, 0, 0, 0, 0, 0};   // probabilities of the previous tile, not yet in O
@@ -310,9 +314,9 @@ void fwd_fp8_kernel(FwdArgs a) {
       sacc[nb] = f32x16{};
       const int row = 32 * nb + lr;
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const i32x8 ka = cat8(*reinterpret_cast<const u32x4*>(kb + rm_byte<64>(row, 32 * s + 16 * g)),
-                              *reinterpret_cast<const u32x4*>(kb + rm_byte<64>(row, 32 * s + 16 * g + 8)));
+      for (int s = 0; s < KS; ++s) {
+        const i32x8 ka = cat8(*reinterpret_cast<const u32x4*>(kb + rm_byte<DB>(row, 32 * s + 16 * g)),
+                              *reinterpret_cast<const u32x4*>(kb + rm_byte<DB>(row, 32 * s + 16 * g + 8)));
         sacc[nb] = mfma_fp8(ka, qf[s], sacc[nb]);
       }
     }
@@ -368,15 +372,17 @@ void fwd_fp8_kernel(FwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_vt(const VtArgs& a, hipStream_t stream) {
+hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t stream) {
   const int64_t nblk = (int64_t)a.batch * a.heads_kv * a.tk;
-  hipLaunchKernelGGL(vt_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, a);
+  if (head_dim == 128) hipLaunchKernelGGL(vt_kernel<128>, dim3((unsigned)nblk), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(vt_kernel<64>, dim3((unsigned)nblk), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd_fp8(const FwdArgs& a, int head_dim, hipStream_t stream) {
   const int nblk = a.tq * a.batch * a.heads;
-  hipLaunchKernelGGL(fwd_fp8_kernel, dim3(nblk), dim3(NT), 0, stream, a);
+  if (head_dim == 128) hipLaunchKernelGGL(fwd_fp8_kernel<128>, dim3(nblk), dim3(NT), 0, stream, a);
+  else hipLaunchKernelGGL(fwd_fp8_kernel<64>, dim3(nblk), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -171,7 +171,7 @@ def _problem_fp8(D=128, hkv=0):
 
 
 @pytest.mark.parametrize("case,expect", [
-    ("head_dim_64", L.FM_ERR_UNSUPPORTED),
+    ("head_dim_96", L.FM_ERR_UNSUPPORTED),
     ("bf16_problem", L.FM_ERR_INVALID_ARGUMENT),
     ("null_descale", L.FM_ERR_INVALID_ARGUMENT),
     ("zero_descale", L.FM_ERR_INVALID_ARGUMENT),
@@ -179,8 +179,8 @@ def _problem_fp8(D=128, hkv=0):
 ])
 def test_fwd_fp8_rejects(case, expect):
     prob, ds = _problem_fp8(), (1.0, 1.0, 1.0)
-    if case == "head_dim_64":
-        prob = _problem_fp8(D=64)
+    if case == "head_dim_96":
+        prob = _problem_fp8(D=96)
     elif case == "bf16_problem":
         prob = _problem(D=128)
     elif case == "null_descale":

@@ -39,10 +39,10 @@ pytestmark = pytest.mark.gpu
 D = 128
 
 
-def _codes(B, Sq, Sk, H, Hkv, seed, gains=(64.0, 64.0, 64.0)):
-    q8 = ST.fp8_codes("q", (B, Sq, H, D), seed, gains[0])
-    k8 = ST.fp8_codes("k", (B, Sk, Hkv, D), seed, gains[1])
-    v8 = ST.fp8_codes("v", (B, Sk, Hkv, D), seed, gains[2])
+def _codes(B, Sq, Sk, H, Hkv, seed, gains=(64.0, 64.0, 64.0), d=D):
+    q8 = ST.fp8_codes("q", (B, Sq, H, d), seed, gains[0])
+    k8 = ST.fp8_codes("k", (B, Sk, Hkv, d), seed, gains[1])
+    v8 = ST.fp8_codes("v", (B, Sk, Hkv, d), seed, gains[2])
     return q8, k8, v8, tuple(1.0 / g for g in gains)
 
 
@@ -105,15 +105,17 @@ def _families(n, rng):
     }
 
 
-def test_fp8_mask_families(gpu_lib):
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_mask_families(gpu_lib, d):
     rng = np.random.default_rng(8)
     n = 700
     for i, (name, v) in enumerate(_families(n, rng).items()):
-        q8, k8, v8, ds = _codes(2, n, n, 3, 3, seed=40 + i)
-        _compare(gpu_lib, q8, k8, v8, ds, tuple(x[None, None] for x in v), 1 / math.sqrt(D), name)
+        q8, k8, v8, ds = _codes(2, n, n, 3, 3, seed=40 + i, d=d)
+        _compare(gpu_lib, q8, k8, v8, ds, tuple(x[None, None] for x in v), 1 / math.sqrt(d), f"{name} d={d}")
 
 
-def test_fp8_ragged_gqa_per_head_masks(gpu_lib):
+@pytest.mark.parametrize("d", [128, 64])
+def test_fp8_ragged_gqa_per_head_masks(gpu_lib, d):
     """Sq != Sk, both ragged; 4 query heads on 2 K/V heads; a mask per
     (b, h) with fully masked rows."""
     rng = np.random.default_rng(9)
@@ -127,8 +129,8 @@ def test_fp8_ragged_gqa_per_head_masks(gpu_lib):
         fams.append((lts, lte, uts, ute))
     fams[3] = (np.zeros(sk, int), np.full(sk, 100), np.zeros(sk, int), np.zeros(sk, int))   # rows < 100 see nothing
     vec = SM.stack([[fams[b * H + h] for h in range(H)] for b in range(B)])
-    q8, k8, v8, ds = _codes(B, sq, sk, H, Hkv, seed=50)
-    o, lse = _compare(gpu_lib, q8, k8, v8, ds, vec, 0.1, "ragged gqa")
+    q8, k8, v8, ds = _codes(B, sq, sk, H, Hkv, seed=50, d=d)
+    o, lse = _compare(gpu_lib, q8, k8, v8, ds, vec, 0.1, f"ragged gqa d={d}")
     assert (o[0, :100, 3] == 0).all() and np.isneginf(lse[0, 3, :100]).all()
 
 
@@ -143,11 +145,12 @@ def test_fp8_descales_and_wide_scores(gpu_lib, gains, scale):
     _compare(gpu_lib, q8, k8, v8, ds, vec, scale, f"gains {gains} scale {scale}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("sq,sk", [(1, 1), (1, 200), (130, 1), (64, 64), (129, 65)])
-def test_fp8_tiny_and_edge_shapes(gpu_lib, sq, sk):
-    q8, k8, v8, ds = _codes(1, sq, sk, 2, 2, seed=sq * 1000 + sk)
+def test_fp8_tiny_and_edge_shapes(gpu_lib, sq, sk, d):
+    q8, k8, v8, ds = _codes(1, sq, sk, 2, 2, seed=sq * 1000 + sk, d=d)
     vec = tuple(x[None, None] for x in SM.no_mask(sk, sq))
-    _compare(gpu_lib, q8, k8, v8, ds, vec, 1 / math.sqrt(D), f"{sq}x{sk}")
+    _compare(gpu_lib, q8, k8, v8, ds, vec, 1 / math.sqrt(d), f"{sq}x{sk} d={d}")
 
 
 def test_fp8_float8_tensors_and_determinism(gpu_lib):
