@@ -13,9 +13,10 @@
 //
 // Kernels:
 //   bwd_pre   D per query row;
-//   bwd_dkdv  one workgroup per (batch, head, 128-key tile); each wavefront
-//             owns 32 keys whose K and V rows stay in registers and whose dK,
-//             dV accumulate in registers over all non-SKIP 64-row query tiles;
+//   bwd_dkdv  one workgroup per (batch, head, 128-key tile) with K and V in
+//             LDS; each pair of wavefronts owns 32 keys, forms S and dP for
+//             half the rows of every non-SKIP 64-row query tile each, and one
+//             accumulates dV, the other dK, in registers;
 //   bwd_dq    one workgroup per (batch, head, 128-row query tile); each
 //             wavefront owns 32 query rows whose Q, dO, LSE, D stay in
 //             registers and whose dQ accumulates over all non-SKIP 64-key
@@ -23,6 +24,7 @@
 //             that no workgroup ever adds into another one's output: no
 //             atomics, deterministic results.
 #include <climits>
+#include <cstddef>
 #include <type_traits>
 #include <cmath>
 
@@ -95,37 +97,54 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ dK / dV
+// One workgroup per (batch, K/V head, 128-key tile), eight wavefronts, two per
+// SIMD. Wavefronts w and w + 4 (one SIMD) share keys 32 (w % 4) .. + 31 of the
+// tile. For every 64-row query tile each of the two forms S and dP for its own
+// 32 rows (rows 32 (w / 4) ..) and from them P and dS; they hand each other
+// the half the other needs through LDS, and then the first accumulates dV and
+// the second dK over all 64 rows. Splitting the work this way keeps one
+// output (64 registers) per wavefront, which leaves registers for operand
+// reads issued well ahead of their matrix products. The K and V tiles stay in
+// LDS for the whole kernel; every wavefront reads its keys' rows as operands.
 namespace kv {
 constexpr int BQ = kBwdBlockQ;   // 64 query rows per inner tile
-constexpr int BK = kBwdBlockK;   // 128 keys per workgroup (32 per wavefront)
-
-constexpr int NBUF = 3;          // query tiles in flight: the current one and two prefetched
+constexpr int BK = kBwdBlockK;   // 128 keys per workgroup
+constexpr int WAVES = 8;         // 4 key groups x 2 row halves
+constexpr int THREADS = WAVES * 64;
+constexpr int NBUF = 2;          // query tiles in LDS: the current one and the next
 
 template <int D>
 struct alignas(16) Smem {
-  uint16_t q[NBUF][BQ * D];      // query tiles, row-major, swizzled
+  uint16_t k[BK * D];            // the workgroup's key tile, row-major, swizzled
+  uint16_t v[BK * D];            // its value tile
+  uint16_t q[NBUF][BQ * D];      // query tiles
   uint16_t dout[NBUF][BQ * D];   // dO tiles
   float lse2[NBUF][BQ];          // LSE * log2(e); +inf for rows that see nothing / past the end
   float dd[NBUF][BQ];            // D = rowsum(dO * O)
   uint32_t list[LIST_CAP];
   uint16_t rank[LIST_CAP];       // ascending rank of each list entry (stored-dS slot)
-  uint16_t dsx[NW][32 * BQ];     // per wavefront: its 32 keys' dS, [key][column], regrouped for the stores
-  int32_t scan[NW];
+  // per wavefront, 2 KiB: first its dS regrouped for the stores, then the
+  // P (second half) or dS (first half) handed to the other wavefront of its SIMD
+  uint16_t xch[WAVES][32 * 32];
+  int32_t scan[WAVES];
 };
 }  // namespace kv
 
 // GROUPED: more than one query head per K/V head (the head loop runs
 // a.group times); without it the loop has one trip and folds away.
 template <int D, bool F32, bool GROUPED>
-__global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(BwdArgs a) {
   using namespace kv;
   constexpr int KSTEPS = D / 16;
   constexpr int CB = D / 32;
-  constexpr int QR = (BQ * D / 8) / NT;   // 16-byte chunks per thread of a Q (or dO) tile
+  constexpr int QR = (BQ * D / 8) / THREADS;   // 16-byte chunks per thread of a float32 Q (or dO) tile
+  constexpr int KR = (BK * D / 8) / THREADS;   // ... of a float32 K (or V) tile
   __shared__ Smem<D> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
+  const int kg = __builtin_amdgcn_readfirstlane(w & 3);   // key group
+  const int mb = __builtin_amdgcn_readfirstlane(w >> 2);   // row half for S, dP; 0: accumulates dV, 1: dK
   const int l = tid & 63;
   const int lr = l & 31;
   const int g = l >> 5;
@@ -144,24 +163,36 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const int hk = __builtin_amdgcn_readfirstlane(a.mask.hm > 1 ? kr % hkm : jr % a.heads_kv);
   const int bm = __builtin_amdgcn_readfirstlane(kr / hkm);
 
-  const int n = kt * BK + 32 * w + lr;   // this lane's key
+  const int n = kt * BK + 32 * kg + lr;   // this lane's key
   const bool key_ok = n < a.seq_k;
-
-  // K and V rows of this lane's key as MFMA B operands (channels 16s + 8g ..).
-  // (keys past the end re-read the last key; the ragged tile masks them)
-  u32x4 kf[KSTEPS], vf[KSTEPS];
-  {
-    const int nk = min(n, a.seq_k - 1);
-    const int64_t koff = (int64_t)b * a.k_sb + (int64_t)nk * a.k_ss + (int64_t)hk * a.k_sh + 8 * g;
-    const int64_t voff = (int64_t)b * a.v_sb + (int64_t)nk * a.v_ss + (int64_t)hk * a.v_sh + 8 * g;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      kf[s] = load8_as_bf16<F32>(a.k, koff + 16 * s);
-      vf[s] = load8_as_bf16<F32>(a.v, voff + 16 * s);
-    }
-  }
   const bool ragged_k = (a.seq_k % BK) != 0 && kt == a.tk - 1;
   const bool store_ds = a.plan != nullptr && a.plan[1] != 0;
+  constexpr int ES = F32 ? 4 : 2;
+
+  // ---- K and V tiles into LDS once (keys past the end re-read the last key;
+  // the ragged tile masks them) ----
+  {
+    const int64_t k_ld = a.k_ss * ES, v_ld = a.v_ss * ES;
+    const char* kt0 = reinterpret_cast<const char*>(a.k) +
+                      ((int64_t)b * a.k_sb + (int64_t)kt * BK * a.k_ss + (int64_t)hk * a.k_sh) * ES;
+    const char* vt0 = reinterpret_cast<const char*>(a.v) +
+                      ((int64_t)b * a.v_sb + (int64_t)kt * BK * a.v_ss + (int64_t)hk * a.v_sh) * ES;
+    const int nvalid = a.seq_k - kt * BK;
+    if constexpr (F32) {
+      uint32_t off[KR];
+      u32x4 r[KR];
+      tile_offsets<D, F32, KR, THREADS>(off, k_ld, tid);
+      load_tile_rows<D, F32, KR, THREADS>(r, kt0, off, k_ld, tid, nvalid);
+      store_tile_rows<D, KR, THREADS>(reinterpret_cast<char*>(sm.k), r, tid);
+      tile_offsets<D, F32, KR, THREADS>(off, v_ld, tid);
+      load_tile_rows<D, F32, KR, THREADS>(r, vt0, off, v_ld, tid, nvalid);
+      store_tile_rows<D, KR, THREADS>(reinterpret_cast<char*>(sm.v), r, tid);
+    } else {
+      using DmaK = DmaTile<D, BK, THREADS>;
+      DmaK::load(reinterpret_cast<char*>(sm.k), kt0, DmaK::offset(k_ld, tid), k_ld, tid, nvalid);
+      DmaK::load(reinterpret_cast<char*>(sm.v), vt0, DmaK::offset(v_ld, tid), v_ld, tid, nvalid);
+    }
+  }
 
   // Per query head (set at the start of each head): the lane's key bounds
   // and interval widths, the class column, the stored-dS slot base and
@@ -172,45 +203,38 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
   const uint8_t* ccol = nullptr;
   int64_t slot0 = 0, lrow = 0;
   uint16_t* ds_rep = nullptr;
-  f32x16 dvacc[CB], dkacc[CB];
+  f32x16 acc[CB];   // dV^T (first half) or dK^T (second half) of the wavefront's keys
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    dvacc[cb] = f32x16{};
-    dkacc[cb] = f32x16{};
-  }
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
   const float C = a.scale_log2;
 
   // ---- query tile staging ----
   // Q and dO (bf16) and the rows' LSE*log2(e) and D go straight from global
-  // memory into LDS, two tiles ahead of the math; float32 Q and dO pass
-  // through registers (rounded to bf16) when their tile is staged. Rows past
-  // the end re-read the last row; their LSE*log2(e) is +inf, so P = dS = 0.
-  constexpr int ES = F32 ? 4 : 2;
+  // memory into LDS one tile ahead of the math; float32 Q and dO pass through
+  // registers (rounded to bf16) when their tile is staged. Rows past the end
+  // re-read the last row; their LSE*log2(e) is +inf, so P = dS = 0.
   const int64_t q_ld = a.q_ss * ES, o_ld = a.o_ss * ES;
   const char* qbh = nullptr;
   const char* dbh = nullptr;
-  using Dma = DmaTile<D, BQ, NT>;
+  using Dma = DmaTile<D, BQ, THREADS>;
   constexpr int NOFF = F32 ? QR : 1;
   uint32_t qoff[NOFF], doff[NOFF];
   if constexpr (F32) {
-    tile_offsets<D, F32, QR, NT>(qoff, q_ld, tid);
-    tile_offsets<D, F32, QR, NT>(doff, o_ld, tid);
+    tile_offsets<D, F32, QR, THREADS>(qoff, q_ld, tid);
+    tile_offsets<D, F32, QR, THREADS>(doff, o_ld, tid);
   } else {
     qoff[0] = Dma::offset(q_ld, tid);
     doff[0] = Dma::offset(o_ld, tid);
   }
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  // Direct loads per tile and wavefront: Q and dO (bf16), plus one for the
-  // LSE row block (wavefront 0) or the D row block (wavefront 1).
-  constexpr int GROUP = F32 ? 0 : 2 * Dma::PER;
   auto stage_q = [&](int qt, int buf) {
     const int m0 = qt * BQ;
     if constexpr (F32) {
       u32x4 rq[QR], rd[QR];
-      load_tile_rows<D, F32, QR, NT>(rq, qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
-      load_tile_rows<D, F32, QR, NT>(rd, dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
-      store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.q[buf]), rq, tid);
-      store_tile_rows<D, QR, NT>(reinterpret_cast<char*>(sm.dout[buf]), rd, tid);
+      load_tile_rows<D, F32, QR, THREADS>(rq, qbh + m0 * q_ld, qoff, q_ld, tid, a.seq_q - m0);
+      load_tile_rows<D, F32, QR, THREADS>(rd, dbh + m0 * o_ld, doff, o_ld, tid, a.seq_q - m0);
+      store_tile_rows<D, QR, THREADS>(reinterpret_cast<char*>(sm.q[buf]), rq, tid);
+      store_tile_rows<D, QR, THREADS>(reinterpret_cast<char*>(sm.dout[buf]), rd, tid);
     } else {
       Dma::load(reinterpret_cast<char*>(sm.q[buf]), qbh + m0 * q_ld, qoff[0], q_ld, tid, a.seq_q - m0);
       Dma::load(reinterpret_cast<char*>(sm.dout[buf]), dbh + m0 * o_ld, doff[0], o_ld, tid, a.seq_q - m0);
@@ -219,6 +243,60 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     else if (wu == 1) dma4(a.drow + lrow + m0, 4u * (uint32_t)l, lds_address(sm.dd[buf]));
   };
 
+  // Where the two wavefronts of a SIMD both want the matrix unit, the first
+  // goes first: it then runs its exponentials while the other's products run.
+  if (mb == 0) __builtin_amdgcn_s_setprio(1);
+
+  // LDS byte addresses of this lane's operand reads, computed once: tile
+  // buffer, dO-vs-Q, V-vs-K, 16-row steps and the lane-uniform row half go
+  // into the reads' immediate offsets (none of them changes the swizzle).
+  // S / dP step s: Q (and dO) row 32 mb + lr, K (and V) row 32 kg + lr,
+  // channels 16 s + 8 g.
+  uint32_t qo[KSTEPS], ko[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    qo[s] = lds_address(sm.q[0]) + (uint32_t)rm_byte<D>(32 * mb + lr, 16 * s + 8 * g);
+    ko[s] = lds_address(sm.k) + (uint32_t)rm_byte<D>(32 * kg + lr, 16 * s + 8 * g);
+  }
+  // dV / dK products: transposed dO (first half) or Q (second half) rows of
+  // row block hh (0: the own half, 1: the other's), channel block cb, the two
+  // 4-row groups of tr_operand().
+  uint32_t to[2][CB][2];
+  {
+    const int i = l & 15;
+    const uint32_t tbase = mb ? lds_address(sm.q[0]) : lds_address(sm.dout[0]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int half = hh == 0 ? mb : 1 - mb;
+        const int r0 = 32 * half + 4 * g + (i >> 2);
+        const int col = 32 * cb + 16 * ((l >> 4) & 1) + 4 * (i & 3);
+        to[hh][cb][0] = tbase + (uint32_t)rm_byte<D>(r0, col);
+        to[hh][cb][1] = tbase + (uint32_t)rm_byte<D>(r0 + 8, col);
+      }
+  }
+  // (kept whole: otherwise the compiler splits them into shared parts and
+  // adds those again in every tile)
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    asm volatile("" : "+v"(qo[s]));
+    asm volatile("" : "+v"(ko[s]));
+  }
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      asm volatile("" : "+v"(to[hh][cb][0]));
+      asm volatile("" : "+v"(to[hh][cb][1]));
+    }
+  constexpr uint32_t QTILE = BQ * D * 2;             // bytes per Q (or dO) tile
+  constexpr uint32_t DOUT = 2 * QTILE;               // sm.dout[0] - sm.q[0]
+  constexpr uint32_t VOFF = BK * D * 2;              // sm.v - sm.k
+  static_assert(offsetof(Smem<D>, dout) - offsetof(Smem<D>, q) == DOUT, "tile layout");
+  static_assert(offsetof(Smem<D>, v) - offsetof(Smem<D>, k) == VOFF, "tile layout");
+  char* xmine = reinterpret_cast<char*>(sm.xch[w]);
+  const char* xpeer = reinterpret_cast<const char*>(sm.xch[w ^ 4]);
   int it_global = 0;   // iteration count over heads and passes (selects the LDS buffer)
   const int ngroup = GROUPED ? a.group : 1;
   for (int gi = 0; gi < ngroup; ++gi) {
@@ -257,190 +335,194 @@ __global__ __launch_bounds__(NT) void bwd_dkdv_kernel(BwdArgs a) {
     const int head_base = it_global;   // non-SKIP tiles of earlier heads
     for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
       int n_full;
-      const int n_list = compact_classes_split<LIST_CAP, NT>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list, sm.rank,
-                                                             sm.scan, tid, ragged_k, &n_full);
+      const int n_list = compact_classes_split<LIST_CAP, THREADS>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list,
+                                                                  sm.rank, sm.scan, tid, ragged_k, &n_full);
       if (n_list == 0) continue;
       const int pass_base = it_global - head_base;   // this head's non-SKIP tiles in earlier passes
 
       stage_q((int)(sm.list[0] & ~kPartialBit), it_global % NBUF);
-      if (n_list > 1) stage_q((int)(sm.list[1] & ~kPartialBit), (it_global + 1) % NBUF);
 
       // FULL tiles first, then PARTIAL ones, each with its own straight-line
       // body (one branch-free basic block per query tile).
-      auto iteration = [&](auto masked_c, int it) {
+      auto iteration = [&](auto masked_c, auto buf_c, int it) {
         constexpr bool MASKED = decltype(masked_c)::value;
-        const int buf = it_global % NBUF;
+        constexpr int buf = decltype(buf_c)::value;   // it_global % NBUF
         const int qt = (int)(sm.list[it] & ~kPartialBit);
         const int m0 = qt * BQ;
-        // This tile's loads done. Younger vector-memory operations that may stay
-        // in flight: the next tile's loads and the dS stores of the last two
-        // iterations of this pass (vmcnt counts stores too).
-        wait_vmem_upto((it + 1 < n_list ? GROUP + (wu < 2 ? 1 : 0) : 0) + (store_ds ? 4 * min(it, 2) : 0));
+        // This tile's loads done (and, at a pass's first tile, the K / V tiles).
+        // Younger vector-memory operations that may stay in flight: the dS
+        // stores of the previous iteration (vmcnt counts stores too).
+        if (store_ds && it > 0) wait_vmem_le<2>();
+        else wait_vmem();
         __syncthreads();   // tile `buf` visible to all; the buffer read last iteration is free
-        if (it + 2 < n_list) stage_q((int)(sm.list[it + 2] & ~kPartialBit), (it_global + 2) % NBUF);
-        const char* qb = reinterpret_cast<const char*>(sm.q[buf]);
-        const char* db = reinterpret_cast<const char*>(sm.dout[buf]);
+        if (it + 1 < n_list) stage_q((int)(sm.list[it + 1] & ~kPartialBit), buf ^ 1);
 
-        // One 64-row query tile as two 32-row halves (A: rows 0-31, B: 32-63),
-        // ordered so that each half's elementwise work runs beside the other
-        // half's matrix products (the MFMA unit works while the same wavefront
-        // issues independent VALU instructions):
-        //   S,dP(A) | S,dP(B) + P,dS(A) | dV,dK(A) + P,dS(B) | dV,dK(B)
+        // S = Q K^T and dP = dO V^T for the wavefront's 32 rows x 32 keys
+        // (lane = key, registers = query rows). The four operands of step s
+        // are read two steps ahead of its products (three sets in registers).
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
         {
-          f32x16 sacc[2], dpacc[2];
-          u32x4 pp[2][2], dsp[2][2];
-          // S = Q K^T and dP = dO V^T (lane = key, registers = query rows)
-          auto sdp = [&](int mb) {
-            sacc[mb] = f32x16{};
-            dpacc[mb] = f32x16{};
-  #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-              const int off = rm_byte<D>(32 * mb + lr, 16 * s + 8 * g);
-              sacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(qb + off), kf[s], sacc[mb]);
-              dpacc[mb] = mfma32(*reinterpret_cast<const u32x4*>(db + off), vf[s], dpacc[mb]);
-            }
+          u32x4 op[3][4];
+          auto read = [&](int s, u32x4 (&o)[4]) {
+            o[0] = lds16(qo[s], buf * QTILE);
+            o[1] = lds16(ko[s]);
+            o[2] = lds16(qo[s], DOUT + buf * QTILE);
+            o[3] = lds16(ko[s], VOFF);
           };
-          // P = exp2(S * scale * log2(e) - LSE * log2(e)), dS = P (dP - D),
-          // both rounded to bf16 MFMA operands
-          auto softmax = [&](int mb) {
-  #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const int ml = 32 * mb + 8 * q4 + 4 * g;
-              const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
-              const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
-  #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int i = 4 * q4 + r;
-                float p = fast_exp2(fmaf(sacc[mb][i], C, -l2[r]));
-                if constexpr (MASKED) {
-                  const int mm = m0 + ml + r;
-                  const bool mk = ((uint32_t)(mm - b_lts) < b_lw) | ((uint32_t)(mm - b_uts) < b_uw);
-                  p = mk ? 0.f : p;
-                }
-                sacc[mb][i] = p;
-                dpacc[mb][i] = p * (dpacc[mb][i] - dd[r]);
-              }
-            }
-  #pragma unroll
-            for (int t = 0; t < 2; ++t)
-  #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                pp[mb][t][j] = pack_bf16(sacc[mb][8 * t + 2 * j], sacc[mb][8 * t + 2 * j + 1]);
-                dsp[mb][t][j] = pack_bf16(dpacc[mb][8 * t + 2 * j], dpacc[mb][8 * t + 2 * j + 1]);
-              }
-          };
-          // dV^T += dO^T P, dK^T += Q^T dS (contraction over the half's rows)
-          auto dvdk = [&](int mb) {
-  #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int r0 = 32 * mb + 16 * t + 4 * g;
-  #pragma unroll
-              for (int cb = 0; cb < CB; ++cb) {
-                dvacc[cb] = mfma32(tr_operand<D>(db, l, 32 * cb, r0, r0 + 8), pp[mb][t], dvacc[cb]);
-                dkacc[cb] = mfma32(tr_operand<D>(qb, l, 32 * cb, r0, r0 + 8), dsp[mb][t], dkacc[cb]);
-              }
-            }
-          };
-          // Four scheduling regions; in each, operand reads run ahead of their
-          // MFMAs and the other half's elementwise work sits between MFMAs.
-          sdp(0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-  #pragma unroll
-          for (int j = 0; j < 2 * KSTEPS - 4; ++j) {
+          read(0, op[0]);
+          read(1, op[1]);
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) {
+            if (s + 2 < KSTEPS) read(s + 2, op[(s + 2) % 3]);
+            sacc = mfma32(op[s % 3][0], op[s % 3][1], sacc);
+            dpacc = mfma32(op[s % 3][2], op[s % 3][3], dpacc);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int s = 0; s < KSTEPS - 2; ++s) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
           __builtin_amdgcn_sched_barrier(0);
+        }
 
-          sdp(1);
-          softmax(0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-  #pragma unroll
-          for (int j = 0; j < 2 * KSTEPS; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 9 : 6, 0);
+        // P = exp2(S * scale * log2(e) - LSE * log2(e)), dS = P (dP - D),
+        // both rounded to bf16 MFMA operands
+        u32x4 pp[2], dsp[2];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ml = 32 * mb + 8 * q4 + 4 * g;
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
+          const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * q4 + r;
+            float p = fast_exp2(fmaf(sacc[i], C, -l2[r]));
+            if constexpr (MASKED) {
+              const int mm = m0 + ml + r;
+              const bool mk = ((uint32_t)(mm - b_lts) < b_lw) | ((uint32_t)(mm - b_uts) < b_uw);
+              p = mk ? 0.f : p;
+            }
+            sacc[i] = p;
+            dpacc[i] = p * (dpacc[i] - dd[r]);
           }
-          __builtin_amdgcn_sched_barrier(0);
-
-          dvdk(0);
-          softmax(1);
-          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-  #pragma unroll
-          for (int j = 0; j < 4 * CB; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 9 : 6, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pp[t][j] = pack_bf16(sacc[8 * t + 2 * j], sacc[8 * t + 2 * j + 1]);
+            dsp[t][j] = pack_bf16(dpacc[8 * t + 2 * j], dpacc[8 * t + 2 * j + 1]);
           }
-          __builtin_amdgcn_sched_barrier(0);
 
-          dvdk(1);
-          __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-  #pragma unroll
-          for (int j = 0; j < 4 * CB - 3; ++j) {
+        if (store_ds) {   // 2 stores per lane, counted by the wait above
+          // The stored tile is 16 MFMA operand fragments of 1 KiB, fragment
+          // (rb, s) = query rows 32 rb .. 32 rb + 31 x keys 16 s .. 16 s + 15.
+          // Lane L's 16 bytes at L * 16 hold the row of fragment column
+          // c = L % 32 (row 32 rb + 16 c[3] + 8 j[2] + 4 c[4] + j[1:0] for
+          // element j's half, the order in which the accumulator holds rows) and
+          // keys 16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3 (h = L / 32), the
+          // order in which the dQ kernel's transposing K^T reads take the keys.
+          // The wavefront's 32 keys x 32 rows are fragments (mb, 2 kg) and
+          // (mb, 2 kg + 1). They go through its own LDS block as a row-major
+          // [key][column] tile; transposing reads of it yield whole fragment
+          // lanes, so each store writes 1 KiB of consecutive bytes. LDS accesses
+          // of one wavefront execute in order; no barrier is needed.
+#pragma unroll
+          for (int t = 0; t < 2; ++t) *reinterpret_cast<u32x4*>(xmine + rm_byte<32>(lr, 8 * (2 * g + t))) = dsp[t];
+          const int64_t slot = slot0 + pass_base + sm.rank[it];
+          char* tile = reinterpret_cast<char*>(ds_rep + slot * (BK * BQ));
+#pragma unroll
+          for (int sp = 0; sp < 2; ++sp) {
+            const int r0 = 16 * sp + 4 * g;
+            const u32x4 x = tr_operand<32>(xmine, l, 0, r0, r0 + 8);
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(tile + (mb * 8 + 2 * kg + sp) * 1024 + l * 16));
+          }
+        }
+
+        // Hand over the half the other wavefront needs (its P to the dV
+        // wavefront, its dS to the dK wavefront), keep the own one; then
+        // dV^T += dO^T P (first half) or dK^T += Q^T dS (second half), over
+        // all 64 rows: own rows first, then the other half's. The transposed
+        // operand of step j is read three steps ahead.
+        auto products = [&](auto is_k_c) {
+          constexpr bool IS_K = decltype(is_k_c)::value;
+          u32x4 own[2], peer[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            own[t] = IS_K ? dsp[t] : pp[t];
+            *reinterpret_cast<u32x4*>(xmine + (t * 64 + l) * 16) = IS_K ? pp[t] : dsp[t];
+          }
+          __syncthreads();   // the halves handed over are visible
+#pragma unroll
+          for (int t = 0; t < 2; ++t) peer[t] = *reinterpret_cast<const u32x4*>(xpeer + (t * 64 + l) * 16);
+          constexpr int NS = 4 * CB;   // (row step, channel block) products
+          u32x4 ta[NS];
+          auto tread = [&](int j) {
+            const int hh = j / (2 * CB), t = (j / CB) & 1, cb = j % CB;
+            const uint32_t o = buf * QTILE + t * 16 * (2 * D);   // tile buffer, 16-row step
+            const u32x2 x = lds_tr16(to[hh][cb][0], o);
+            const u32x2 y = lds_tr16(to[hh][cb][1], o);
+            ta[j] = u32x4{x[0], x[1], y[0], y[1]};
+          };
+#pragma unroll
+          for (int j = 0; j < 3; ++j) tread(j);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) {
+            if (j + 3 < NS) tread(j + 3);
+            const int hh = j / (2 * CB), t = (j / CB) & 1, cb = j % CB;
+            acc[cb] = mfma32(ta[j], hh == 0 ? own[t] : peer[t], acc[cb]);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 6 + 2, 0);
+#pragma unroll
+          for (int j = 0; j < NS - 3; ++j) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           }
           __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
           __builtin_amdgcn_sched_barrier(0);
-
-          if (store_ds) {   // 4 stores per lane, counted by the wait above
-            // The stored tile is 16 MFMA operand fragments of 1 KiB, fragment
-            // (rb, s) = columns 32 rb .. 32 rb + 31 x keys 16 s .. 16 s + 15,
-            // lane L's 16 bytes at L * 16 holding column 32 rb + L % 32 and keys
-            // 16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3 (h = L / 32), the order
-            // in which the dQ kernel's transposing K^T reads take the keys.
-            // The wavefront's 32 keys go through its own LDS block as a
-            // row-major [key][column] tile; transposing reads of it yield whole
-            // fragment lanes, so each store writes 1 KiB of consecutive bytes.
-            // LDS accesses of one wavefront execute in order; no barrier is needed.
-            char* xb = reinterpret_cast<char*>(sm.dsx[w]);
-  #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-  #pragma unroll
-              for (int t = 0; t < 2; ++t)
-                *reinterpret_cast<u32x4*>(xb + rm_byte<BQ>(lr, 8 * (4 * g + 2 * mb + t))) = dsp[mb][t];
-            const int64_t slot = slot0 + pass_base + sm.rank[it];
-            char* tile = reinterpret_cast<char*>(ds_rep + slot * (BK * BQ));
-  #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-  #pragma unroll
-              for (int sp = 0; sp < 2; ++sp) {
-                const int r0 = 16 * sp + 4 * g;
-                const u32x4 x = tr_operand<BQ>(xb, l, 32 * rb, r0, r0 + 8);
-                __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(tile + (rb * 8 + 2 * w + sp) * 1024 + l * 16));
-              }
-          }
-        }
+        };
+        if (mb) products(std::true_type{});
+        else products(std::false_type{});
       };
+      using B0 = std::integral_constant<int, 0>;
+      using B1 = std::integral_constant<int, 1>;
       int it = 0;
-      for (; it < n_full; ++it, ++it_global) iteration(std::false_type{}, it);
-      for (; it < n_list; ++it, ++it_global) iteration(std::true_type{}, it);
+      for (; it < n_full; ++it, ++it_global) {
+        if (it_global & 1) iteration(std::false_type{}, B1{}, it);
+        else iteration(std::false_type{}, B0{}, it);
+      }
+      for (; it < n_list; ++it, ++it_global) {
+        if (it_global & 1) iteration(std::true_type{}, B1{}, it);
+        else iteration(std::true_type{}, B0{}, it);
+      }
     }
   }
+  if (mb == 0) __builtin_amdgcn_s_setprio(0);
 
-  // ---- epilogue: dK = scale * dK^T, dV = dV^T, transposed back on store ----
+  // ---- epilogue: dV = dV^T (first half), dK = scale * dK^T (second half),
+  // transposed back on store ----
   if (key_ok) {
-    const int64_t koff = (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)hk * a.k_sh;
-    const int64_t voff = (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)hk * a.v_sh;
+    const bool is_k = mb == 1;
+    const int64_t off = is_k ? (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)hk * a.k_sh
+                             : (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)hk * a.v_sh;
+    void* out = is_k ? a.dk : a.dv;
+    const float sc = is_k ? a.scale : 1.f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int c0 = 32 * cb + 8 * q4 + 4 * g;
-        const float k0 = dkacc[cb][4 * q4] * a.scale, k1 = dkacc[cb][4 * q4 + 1] * a.scale;
-        const float k2 = dkacc[cb][4 * q4 + 2] * a.scale, k3 = dkacc[cb][4 * q4 + 3] * a.scale;
-        const float v0 = dvacc[cb][4 * q4], v1 = dvacc[cb][4 * q4 + 1];
-        const float v2 = dvacc[cb][4 * q4 + 2], v3 = dvacc[cb][4 * q4 + 3];
+        const float x0 = acc[cb][4 * q4] * sc, x1 = acc[cb][4 * q4 + 1] * sc;
+        const float x2 = acc[cb][4 * q4 + 2] * sc, x3 = acc[cb][4 * q4 + 3] * sc;
         if constexpr (F32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dk) + koff + c0) = f32x4{k0, k1, k2, k3};
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dv) + voff + c0) = f32x4{v0, v1, v2, v3};
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off + c0) = f32x4{x0, x1, x2, x3};
         } else {
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.dk) + koff + c0) =
-              u32x2{pack_bf16(k0, k1), pack_bf16(k2, k3)};
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.dv) + voff + c0) =
-              u32x2{pack_bf16(v0, v1), pack_bf16(v2, v3)};
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off + c0) =
+              u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
         }
       }
     }
@@ -696,9 +778,9 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
 template <int D, bool F32>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
   if (a.group > 1)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, true>), dim3(a.tk * a.batch * a.heads_kv), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, true>), dim3(a.tk * a.batch * a.heads_kv), dim3(kv::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, false>), dim3(a.tk * a.batch * a.heads_kv), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, false>), dim3(a.tk * a.batch * a.heads_kv), dim3(kv::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -237,14 +237,14 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   }
 
   // ---- epilogue: dQ = scale * (dQ^T)^T; lane = query row, registers = channels ----
-  // Output column c of the stored layout is row 32 mb + 16 t + 4 g + (j < 4 ?
-  // j : j + 4) with g = c / 32, mb, t = bits 4, 3 of c, j = c % 8.
+  // Column c of stored fragment row block rb is row 32 rb + 16 t + 4 g +
+  // (j < 4 ? j : j + 4) with g, t = bits 4, 3 of c, j = c % 8.
 #pragma unroll
   for (int j = 0; j < BLK; ++j) {
     const int rb = CB == 4 ? j : (w >> 1);
-    const int c = 32 * rb + lr;
+    const int c = lr;
     const int jj = c & 7;
-    const int m = qt * BQ + 32 * ((c >> 4) & 1) + 16 * ((c >> 3) & 1) + 4 * (c >> 5) + (jj < 4 ? jj : jj + 4);
+    const int m = qt * BQ + 32 * rb + 16 * ((c >> 3) & 1) + 4 * (c >> 4) + (jj < 4 ? jj : jj + 4);
     if (m < a.seq_q) {
       const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh;
 #pragma unroll

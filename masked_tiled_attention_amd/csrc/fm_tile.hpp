@@ -51,6 +51,20 @@ __device__ __forceinline__ u32x2 tr16(const char* lds_base, int byte) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
 }
 
+// 16-byte LDS read and transposing read (as tr16) at an LDS byte address.
+// Kernels that precompute per-lane addresses use these, so that constant
+// parts of an address end up in the instruction's immediate offset.
+// The constant part `imm` is added as a pointer offset (it cannot wrap), which
+// lets it fold into the instruction.
+typedef __attribute__((address_space(3))) const char lds_char;
+__device__ __forceinline__ u32x4 lds16(uint32_t addr, uint32_t imm = 0) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>((lds_char*)(size_t)addr + imm);
+}
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t addr, uint32_t imm = 0) {
+  return __builtin_bit_cast(u32x2,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((lds_char*)(size_t)addr + imm)));
+}
+
 // MFMA operand (32 output indices x 16 contraction values) read transposed from
 // a row-major tile whose rows are the contraction index: lane l gets output
 // index obase + (l & 31) and contraction rows r0 + 0..3 (elements 0..3) and
