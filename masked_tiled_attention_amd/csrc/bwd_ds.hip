@@ -13,10 +13,10 @@
 //   plan_count  non-SKIP tiles per key-tile row of the dK/dV class map;
 //   plan_scan   one workgroup: exclusive prefix sums (slot offsets), the total
 //               and whether the workspace holds every tile for every (b, h);
-//   dq_ds       one workgroup per (b, h, 64-row query tile): for each non-SKIP
-//               key tile, K and the stored dS tile go straight into LDS (three
-//               buffers, two tiles ahead) and dQ^T += K^T dS^T accumulates in
-//               registers, wavefront w owning 32 of the channels.
+//   dq_ds       one workgroup per (b, h, pair of 64-row query tiles): for each
+//               key tile non-SKIP for either, K and the pair's stored dS tiles
+//               go straight into LDS (two stages, one ahead) and
+//               dQ^T += K^T dS^T accumulates in registers.
 #include <climits>
 #include <cmath>
 
@@ -32,7 +32,6 @@ constexpr int BK = kBwdBlockK;   // keys per dS tile
 constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr int LIST_CAP = 1024;
-constexpr int NBUF = 3;
 constexpr int64_t kTileBytes = (int64_t)BQ * BK * 2;
 
 // ------------------------------------------------------------------ plan
@@ -122,20 +121,76 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(BwdArgs a, int32_t nrow
 }
 
 // ------------------------------------------------------------------ dQ from dS
+// One workgroup per (b, h, pair of adjacent 64-row query tiles). It walks the
+// key tiles that are non-SKIP for either query tile of the pair; each K tile
+// staged in LDS serves the stored dS tiles of both (two thirds of the bytes
+// staged per tile of work, against one K tile per dS tile).
+constexpr int PAIR = 2;   // query tiles per workgroup
+constexpr int NSTAGE = 2; // staged key tiles: the current one and the next
+
 template <int D>
 struct alignas(16) DsSmem {
-  uint16_t k[NBUF][BK * D];    // key tiles, row-major, swizzled
-  uint16_t ds[NBUF][BK * BQ];  // dS tiles as stored: 16 MFMA operand fragments of 1 KiB
-  uint32_t list[LIST_CAP];
-  int32_t slot[LIST_CAP];      // stored-dS slot of each list entry
+  uint16_t k[NSTAGE][BK * D];          // key tiles, row-major, swizzled
+  uint16_t ds[NSTAGE][PAIR][BK * BQ];  // dS tiles as stored: 16 MFMA operand fragments of 1 KiB
+  uint32_t list[LIST_CAP];             // key tiles of the pair's list
+  int32_t slot[LIST_CAP][PAIR];        // stored-dS slot per query tile of the pair; -1: SKIP
   int32_t scan[NW];
 };
+
+// The pair's key-tile list: ascending key tiles that are non-SKIP for query
+// tile qt0 or qt0 + 1 (the latter only when has1), with both slots. Starts and
+// ends with a barrier.
+__device__ __forceinline__ int compact_pair(const uint8_t* ccol, const int32_t* scol, int64_t stride, int first,
+                                            int count, bool has1, uint32_t* sm_list, int32_t (*sm_slot)[PAIR],
+                                            int32_t* sm_scan, int tid) {
+  constexpr int PER = LIST_CAP / NT;
+  const int lane = tid & 63, wave = tid >> 6;
+  bool on[PER][PAIR];
+  int cnt = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int idx = tid * PER + e;
+    const int64_t o = (int64_t)(first + idx) * stride;
+    on[e][0] = idx < count && ccol[o] != FM_TILE_SKIP;
+    on[e][1] = idx < count && has1 && ccol[o + 1] != FM_TILE_SKIP;
+    cnt += on[e][0] || on[e][1];
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) sm_scan[wave] = incl;
+  __syncthreads();
+  int pos = incl - cnt, n_list = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    if (ww < wave) pos += sm_scan[ww];
+    n_list += sm_scan[ww];
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (on[e][0] || on[e][1]) {
+      const int kt = first + tid * PER + e;
+      const int64_t o = (int64_t)kt * stride;
+      sm_list[pos] = (uint32_t)kt;
+      sm_slot[pos][0] = on[e][0] ? scol[o] : -1;
+      sm_slot[pos][1] = on[e][1] ? scol[o + 1] : -1;
+      ++pos;
+    }
+  }
+  __syncthreads();
+  return n_list;
+}
 
 template <int D, bool F32>
 __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   if (a.plan == nullptr || a.plan[1] == 0) return;   // dQ comes from the recompute kernel
   constexpr int CB = D / 32;              // 32-channel blocks of dQ^T
-  constexpr int BLK = 2 * CB / NW;        // (channel block, row block) pairs per wavefront
+  constexpr int RB = 2 * PAIR;            // 32-row blocks of the pair
+  constexpr int BLK = CB * RB / NW;       // (channel block, row block) pairs per wavefront
   constexpr int KR = (BK * D / 8) / NT;   // 16-byte chunks per thread of a float32 key tile
   constexpr int ES = F32 ? 4 : 2;
   __shared__ DsSmem<D> sm;
@@ -150,7 +205,9 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   // on nearby rows and share K tiles in L2 (this kernel is bound by memory
   // traffic, so that beats ordering by length).
   const int nbh = a.batch * a.heads;
-  const int qt = a.tq - 1 - (int)(blockIdx.x / nbh);
+  const int npair = (a.tq + PAIR - 1) / PAIR;
+  const int qt0 = PAIR * (npair - 1 - (int)(blockIdx.x / nbh));
+  const bool has1 = qt0 + 1 < a.tq;
   const int bh = blockIdx.x % nbh;
   const int b = bh / a.heads;
   const int h = bh % a.heads;
@@ -158,16 +215,21 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   const int rep_i = (a.mask.bm > 1 ? 0 : b) * (a.mask.hm > 1 ? 1 : a.heads) + (a.mask.hm > 1 ? 0 : h);
   const int64_t total = __builtin_amdgcn_readfirstlane(a.plan[0]);   // uniform
   const uint16_t* ds_rep = a.ds + (int64_t)rep_i * total * (BK * BQ);
-  const uint8_t* ccol = a.classes_t + (int64_t)mrow * a.tk * a.tq + qt;   // stride tq over kt
-  const int32_t* scol = a.slots + (int64_t)mrow * a.tk * a.tq + qt;
+  const uint8_t* ccol = a.classes_t + (int64_t)mrow * a.tk * a.tq + qt0;   // stride tq over kt
+  const int32_t* scol = a.slots + (int64_t)mrow * a.tk * a.tq + qt0;
 
-  // this wavefront's channel block and row blocks
+  // This wavefront's channel block and row blocks (row block rb: query tile
+  // rb / 2 of the pair, rows 32 (rb % 2) ..). For d = 128 a wavefront owns one
+  // channel block and all four row blocks; for d = 64 one channel block and
+  // one row block of each query tile.
   const int cbw = CB == 4 ? w : (w & 1);
+  auto rb_of = [&](int j) { return CB == 4 ? j : (w >> 1) + 2 * j; };
   f32x16 acc[BLK];
 #pragma unroll
   for (int j = 0; j < BLK; ++j) acc[j] = f32x16{};
 
-  // ---- staging: K (bf16: direct loads; float32: through registers) and dS ----
+  // ---- staging: K (bf16: direct loads; float32: through registers) and the
+  // present dS tiles ----
   const int64_t k_ld = a.k_ss * ES;
   const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)__builtin_amdgcn_readfirstlane(h / a.group) * a.k_sh) * ES;
   using DmaK = DmaTile<D, BK, NT>;
@@ -178,11 +240,10 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   } else {
     koff[0] = DmaK::offset(k_ld, tid);
   }
-  constexpr int SPER = BK * BQ * 2 / 1024 / NW;                 // dS fragments per wavefront
-  constexpr int GROUP = (F32 ? 0 : DmaK::PER) + SPER;         // direct loads per tile and wavefront
+  constexpr int SPER = BK * BQ * 2 / 1024 / NW;   // dS fragments per wavefront and tile
   const uint32_t sdst = lds_address(sm.ds) + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
-  auto stage = [&](int idx, int buf) {   // list entry idx -> buffer buf
-    const int kt = __builtin_amdgcn_readfirstlane((int)(sm.list[idx] & ~kPartialBit));   // uniform
+  auto stage = [&](int idx, int buf) {   // list entry idx -> stage buf
+    const int kt = __builtin_amdgcn_readfirstlane((int)sm.list[idx]);   // uniform
     const int n0 = kt * BK;
     if constexpr (F32) {
       u32x4 rk[KR];
@@ -191,48 +252,60 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
     } else {
       DmaK::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff[0], k_ld, tid, a.seq_k - n0);
     }
-    const int64_t slot = __builtin_amdgcn_readfirstlane(sm.slot[idx]);   // uniform
-    // the tile is copied as stored, fragment i * NW + w by this wavefront
-    const char* src = reinterpret_cast<const char*>(ds_rep + slot * (BK * BQ)) + w * 1024;
-    const uint32_t dst = sdst + (uint32_t)buf * (BK * BQ * 2);
 #pragma unroll
-    for (int i = 0; i < SPER; ++i)
-      DmaK::dma16_nt(src + i * NW * 1024, 16u * (uint32_t)l, dst + (uint32_t)(i * NW) * 1024u);
+    for (int q = 0; q < PAIR; ++q) {
+      const int64_t slot = __builtin_amdgcn_readfirstlane(sm.slot[idx][q]);   // uniform
+      if (slot < 0) continue;
+      // the tile is copied as stored, fragment i * NW + w by this wavefront
+      const char* src = reinterpret_cast<const char*>(ds_rep + slot * (BK * BQ)) + w * 1024;
+      const uint32_t dst = sdst + (uint32_t)(buf * PAIR + q) * (BK * BQ * 2);
+#pragma unroll
+      for (int i = 0; i < SPER; ++i)
+        DmaK::dma16_nt(src + i * NW * 1024, 16u * (uint32_t)l, dst + (uint32_t)(i * NW) * 1024u);
+    }
+  };
+
+  // dQ^T (channels x rows) += K^T (channels x keys) dS^T (keys x rows), 16
+  // keys per step: K^T read transposed, dS^T as the stored fragment lane, both
+  // with the same key order per lane half. Only the present query tiles' row
+  // blocks take part (P0, P1: query tile 0, 1 present).
+  auto products = [&](const char* kb, const char* sb, auto p0_c, auto p1_c) {
+    constexpr bool P0 = decltype(p0_c)::value, P1 = decltype(p1_c)::value;
+    constexpr int NJ = (P0 ? BLK / 2 : 0) + (P1 ? BLK / 2 : 0);
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int r0 = 16 * s + 4 * g;
+      const u32x4 ka = tr_operand<D>(kb, l, 32 * cbw, r0, r0 + 8);
+#pragma unroll
+      for (int j = 0; j < BLK; ++j) {
+        const int rb = rb_of(j);
+        const int q = rb >> 1;
+        if ((q == 0 && !P0) || (q == 1 && !P1)) continue;
+        acc[j] = mfma32(ka, *reinterpret_cast<const u32x4*>(sb + q * (BK * BQ * 2) + ((rb & 1) * 8 + s) * 1024 + l * 16),
+                        acc[j]);
+      }
+    }
+    sched_lds_mfma<(BK / 16) * NJ, (1 + 2 * NJ) / NJ, 2>();
   };
 
   int it_global = 0;
   for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
-    const int n_list = compact_classes<LIST_CAP, NT>(ccol, kt0, min(LIST_CAP, a.tk - kt0), sm.list, sm.scan, tid,
-                                                     (int64_t)a.tq);
+    const int n_list = compact_pair(ccol, scol, (int64_t)a.tq, kt0, min(LIST_CAP, a.tk - kt0), has1, sm.list,
+                                    sm.slot, sm.scan, tid);
     if (n_list == 0) continue;
-    for (int i = tid; i < n_list; i += NT) sm.slot[i] = scol[(int64_t)(sm.list[i] & ~kPartialBit) * a.tq];
-    __syncthreads();
-    stage(0, it_global % NBUF);
-    if (n_list > 1) stage(1, (it_global + 1) % NBUF);
+    stage(0, it_global % NSTAGE);
 
     for (int it = 0; it < n_list; ++it, ++it_global) {
-      const int buf = it_global % NBUF;
-      if (it + 1 < n_list) wait_vmem_le<GROUP>();   // this tile landed; the next may be in flight
-      else wait_vmem();
-      __syncthreads();   // tile `buf` visible to all; the buffer read last iteration is free
-      if (it + 2 < n_list) stage(it + 2, (it_global + 2) % NBUF);
+      const int buf = it_global % NSTAGE;
+      wait_vmem();       // this stage landed (nothing younger is in flight)
+      __syncthreads();   // stage `buf` visible to all; the stage read last iteration is free
+      if (it + 1 < n_list) stage(it + 1, (it_global + 1) % NSTAGE);
       const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
       const char* sb = reinterpret_cast<const char*>(sm.ds[buf]);
-
-      // dQ^T (channels x rows) += K^T (channels x keys) dS^T (keys x rows),
-      // 16 keys per step: K^T read transposed, dS^T as the stored fragment
-      // lane, both with the same key order per lane half.
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        const int r0 = 16 * s + 4 * g;
-        const u32x4 ka = tr_operand<D>(kb, l, 32 * cbw, r0, r0 + 8);
-#pragma unroll
-        for (int j = 0; j < BLK; ++j) {
-          const int rb = CB == 4 ? j : (w >> 1);
-          acc[j] = mfma32(ka, *reinterpret_cast<const u32x4*>(sb + (rb * 8 + s) * 1024 + l * 16), acc[j]);
-        }
-      }
-      sched_lds_mfma<(BK / 16) * BLK, (2 + BLK) / BLK, 2>();
+      const bool p0 = sm.slot[it][0] >= 0, p1 = sm.slot[it][1] >= 0;
+      if (p0 && p1) products(kb, sb, std::true_type{}, std::true_type{});
+      else if (p0) products(kb, sb, std::true_type{}, std::false_type{});
+      else products(kb, sb, std::false_type{}, std::true_type{});
     }
   }
 
@@ -241,10 +314,10 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   // (j < 4 ? j : j + 4) with g, t = bits 4, 3 of c, j = c % 8.
 #pragma unroll
   for (int j = 0; j < BLK; ++j) {
-    const int rb = CB == 4 ? j : (w >> 1);
+    const int rb = rb_of(j);
     const int c = lr;
     const int jj = c & 7;
-    const int m = qt * BQ + 32 * rb + 16 * ((c >> 3) & 1) + 4 * (c >> 4) + (jj < 4 ? jj : jj + 4);
+    const int m = (qt0 + (rb >> 1)) * BQ + 32 * (rb & 1) + 16 * ((c >> 3) & 1) + 4 * (c >> 4) + (jj < 4 ? jj : jj + 4);
     if (m < a.seq_q) {
       const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh;
 #pragma unroll
@@ -265,7 +338,8 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
 
 template <int D, bool F32>
 hipError_t launch_dq_ds_t(const BwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F32>), dim3(a.tq * a.batch * a.heads), dim3(NT), 0, s, a);
+  const int npair = (a.tq + PAIR - 1) / PAIR;
+  hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F32>), dim3(npair * a.batch * a.heads), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
