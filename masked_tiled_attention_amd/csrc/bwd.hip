@@ -502,6 +502,10 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     }
   }
   if (mb == 0) __builtin_amdgcn_s_setprio(0);
+  // A key tile that no query tile sees skips the loop above with its K / V
+  // direct loads possibly still in flight: they must land before the
+  // workgroup ends and its LDS goes to another one.
+  wait_vmem();
 
   // ---- epilogue: dV = dV^T (first half), dK = scale * dK^T (second half),
   // transposed back on store ----

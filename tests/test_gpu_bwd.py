@@ -160,6 +160,21 @@ def test_bwd_stored_ds_random_vectors_rectangular(gpu_lib):
         _compare_ds(gpu_lib, q, k, v, do, vec, 0.1, f"random {sq}x{sk}")
 
 
+def test_bwd_key_tiles_masked_for_every_row(gpu_lib):
+    """Keys [128, 384) are masked for every row, so two whole 128-key tiles
+    have no non-SKIP query tile: their dK / dV are exactly 0 and the key tiles
+    around them match the oracle, with the minimum and the stored-dS
+    workspace."""
+    n, d = 700, 128
+    lts, lte, uts, ute = (np.array(x) for x in SM.causal(n))
+    lts[128:384], lte[128:384] = 0, n
+    vec = tuple(x[None, None] for x in (lts, lte, uts, ute))
+    q, k, v, do = ST.qkv(1, n, n, 2, d, seed=41, with_do=True)
+    _, dk, dv = _compare(gpu_lib, q, k, v, do, vec, 1 / math.sqrt(d), "dead key tiles")
+    assert torch.all(dk[:, 128:384] == 0) and torch.all(dv[:, 128:384] == 0)
+    _compare_ds(gpu_lib, q, k, v, do, vec, 1 / math.sqrt(d), "dead key tiles, stored dS")
+
+
 def test_bwd_stored_ds_float32_inputs(gpu_lib):
     n = 300
     vec = tuple(x[None, None] for x in SM.causal(n))
