@@ -391,6 +391,22 @@ def main():
             del rx
             torch.cuda.empty_cache()
         out["workloads"] = sweep
+        # the headline workload's spread over mask seeds: the document lengths
+        # (and with them the density) change with the seed
+        spread = [{"seed": args.seed, "nnz": out["config"]["nnz"], "density": out["config"]["density"],
+                   "ms_per_step": out["ms_per_step"], "tflops": out["value"]}]
+        for sd in (x for x in range(4) if x != args.seed):
+            log(f"[bench] seed spread {w.name} seed {sd}")
+            wx = SC.build(w.name, sd)
+            rx = Runner(fm, wx, torch, store_ds)
+            msx, _ = time_steps(rx, 5, 2, torch)
+            a, b = rx.flops()
+            spread.append({"seed": sd, "nnz": rx.nnz,
+                           "density": round(rx.nnz / (wx.batch * wx.heads * wx.seq_q * wx.seq_k), 5),
+                           "ms_per_step": round(msx, 4), "tflops": round((a + b) / (msx * 1e-3) / 1e12, 2)})
+            del rx
+            torch.cuda.empty_cache()
+        out["seed_spread"] = spread
         # the FP8 forward (E4M3 inputs) on the long workloads, beside the bf16
         # forward kernel of the same workload
         fp8 = []
