@@ -175,6 +175,15 @@ def test_bwd_key_tiles_masked_for_every_row(gpu_lib):
     _compare_ds(gpu_lib, q, k, v, do, vec, 1 / math.sqrt(d), "dead key tiles, stored dS")
 
 
+def test_bwd_stored_ds_more_key_tiles_than_one_list(gpu_lib):
+    """140,000 keys: 1094 key tiles, more than one compacted list of the dQ
+    kernel, which then walks its key tiles in two passes."""
+    sq, sk = 200, 140000
+    vec = tuple(x[None, None] for x in SM.no_mask(sk, sq))
+    q, k, v, do = ST.qkv(1, sq, sk, 1, 128, seed=43, with_do=True)
+    _compare_ds(gpu_lib, q, k, v, do, vec, 0.088, "140k keys")
+
+
 def test_bwd_stored_ds_float32_inputs(gpu_lib):
     n = 300
     vec = tuple(x[None, None] for x in SM.causal(n))

@@ -60,15 +60,25 @@ def _sample_cols(vec, sq, rng, budget=3000, k=12):
 
 
 def _run(fm, w, vec_dev):
+    """Forward, and the backward twice: with the minimum workspace (dQ
+    recomputed) and with the stored-dS workspace the benchmark times (dQ from
+    the stored dS tiles). Returns (o, lse), grads, dq from stored dS."""
     q, k, v = (t.cuda() for t in (w.q, w.k, w.v))
     o, lse = fm.fm_attn_fwd(q, k, v, vec_dev, w.scale)
-    grads = None
+    grads = dq_ds = None
     if w.backward:
         do = w.do.cuda()
-        grads = fm.fm_attn_bwd(q, k, v, o, lse, do, vec_dev, w.scale)
+        grads = tuple(g.cpu() for g in fm.fm_attn_bwd(q, k, v, o, lse, do, vec_dev, w.scale))
+        ws = torch.empty(fm.fm_bwd_workspace_size_ds(q, k, v, vec_dev, w.scale), dtype=torch.uint8, device="cuda")
+        dq2, dk2, dv2 = fm.fm_attn_bwd(q, k, v, o, lse, do, vec_dev, w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        del ws
+        # dK and dV do not depend on the dQ path
+        assert torch.equal(dk2.cpu(), grads[1]) and torch.equal(dv2.cpu(), grads[2])
+        dq_ds = dq2.cpu()
     torch.cuda.synchronize()
     out = (o.cpu(), lse.cpu())
-    return out, None if grads is None else tuple(g.cpu() for g in grads)
+    return out, grads, dq_ds
 
 
 @pytest.mark.parametrize("name", [n for n in SC.NAMES if n != "c5_cp_rank3_of_8"])
@@ -76,7 +86,7 @@ def test_workload_full_size(gpu_lib, name):
     fm = gpu_lib
     log(f"workload {name}: building inputs")
     w = SC.build(name, seed=0)
-    (o, lse), grads = _run(fm, w, dev_mask(w.vectors))
+    (o, lse), grads, dq_ds = _run(fm, w, dev_mask(w.vectors))
     rng = np.random.default_rng(1)
     q, k, v = np64(w.q), np64(w.k), np64(w.v)
     do = np64(w.do) if w.backward else None
@@ -97,6 +107,7 @@ def test_workload_full_size(gpu_lib, name):
         dq, dk, dv = grads
         rq = OA.backward_rows(q, k, v, do, w.vectors, w.scale, b, h, rows)
         _check_rows(np64(dq)[b, rows, h], rq, len(uni), f"{name} b{b}h{h} dQ")
+        _check_rows(np64(dq_ds)[b, rows, h], rq, len(uni), f"{name} b{b}h{h} dQ from stored dS")
         vb = tuple(None if x is None else x[[b if x.shape[0] > 1 else 0]][:, [h if x.shape[1] > 1 else 0]]
                    for x in w.vectors)
         cols = _sample_cols(vb, w.seq_q, rng)
@@ -121,7 +132,7 @@ def test_workload_cp_rank_share(gpu_lib):
     loc_ref = OM.localize(w.global_vectors, w.chunk_start, w.chunk_len)
     for g, r in zip((loc.lts, loc.lte, loc.uts, loc.ute), loc_ref):
         assert np.array_equal(g.cpu().numpy(), r)
-    (o, lse), (dq, dk, dv) = _run(fm, w, loc)
+    (o, lse), (dq, dk, dv), dq_ds = _run(fm, w, loc)
     rng = np.random.default_rng(2)
     qg = np64(ST.randn("q", (w.batch, w.seq_q_global, w.heads, w.head_dim), w.seed, w.dtype))
     k, v, do_l = np64(w.k), np64(w.v), np64(w.do)
@@ -136,6 +147,7 @@ def test_workload_cp_rank_share(gpu_lib):
         _check_rows(lse[0, h, rows].double().numpy(), rl, len(uni), f"cp h{h} LSE (global reference)")
         rq = OA.backward_rows(qg, k, v, do_g, w.global_vectors, w.scale, 0, h, grows)
         _check_rows(np64(dq)[0, rows, h], rq, len(uni), f"cp h{h} dQ (global reference)")
+        _check_rows(np64(dq_ds)[0, rows, h], rq, len(uni), f"cp h{h} dQ from stored dS (global reference)")
         cols = _sample_cols(loc_ref, w.seq_q, rng)
         rk, rv = OA.backward_cols(np64(w.q), k, v, do_l, loc_ref, w.scale, 0, h, cols)
         assert_close(np64(dk)[0, cols, h], rk, f"cp h{h} dK cols")
