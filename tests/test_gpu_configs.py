@@ -81,11 +81,14 @@ def _run(fm, w, vec_dev):
     return out, grads, dq_ds
 
 
-@pytest.mark.parametrize("name", [n for n in SC.NAMES if n != "c5_cp_rank3_of_8"])
-def test_workload_full_size(gpu_lib, name):
+# every workload at seed 0, and the headline workload also at the densest and
+# sparsest mask seeds of the benchmark's seed spread
+@pytest.mark.parametrize("name,seed", [(n, 0) for n in SC.NAMES if n != "c5_cp_rank3_of_8"] +
+                         [("c4_doc_causal_128k", 1), ("c4_doc_causal_128k", 2)])
+def test_workload_full_size(gpu_lib, name, seed):
     fm = gpu_lib
-    log(f"workload {name}: building inputs")
-    w = SC.build(name, seed=0)
+    log(f"workload {name} seed {seed}: building inputs")
+    w = SC.build(name, seed=seed)
     (o, lse), grads, dq_ds = _run(fm, w, dev_mask(w.vectors))
     rng = np.random.default_rng(1)
     q, k, v = np64(w.q), np64(w.k), np64(w.v)
