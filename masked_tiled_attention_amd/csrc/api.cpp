@@ -148,11 +148,17 @@ struct Layout {
   size_t counts = 0, order = 0;   // forward launch order
   size_t vt = 0;                   // FP8 forward: V^T tiles [B][H_kv][Tk][8 KiB]
   size_t order_k = 0, order_qq = 0;   // backward launch orders (counts, then order)
+  size_t part = 0;                     // split-head dK/dV partials (0: not used)
 };
 
 int64_t padded_rows(int64_t sq) { return ceil_div(sq, 128) * 128; }
 
 int32_t kv_heads(const fm_problem* p) { return p->heads_kv > 0 ? p->heads_kv : p->heads; }
+
+// Grouped-query attention whose mask is shared by all heads runs one dK/dV
+// workgroup per query head (float32 partials summed afterwards): a workgroup
+// that ran a whole group of heads over one key tile would be the longest one.
+bool split_heads(const fm_problem* p, const fm_mask* m) { return kv_heads(p) < p->heads && m->heads == 1; }
 
 Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
   Layout L;
@@ -186,6 +192,10 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
     off = align256(off + (size_t)(mrows * tk * 8));
     L.order_qq = off;
     off = align256(off + (size_t)(mrows * tq_q * 8));
+    if (split_heads(p, m)) {   // float32 dK, dV partials per query head
+      L.part = off;
+      off = align256(off + (size_t)p->batch * p->heads * p->seqlen_k * p->head_dim * 4 * 2);
+    }
     L.slots = off;
     L.ds = align256(off + (size_t)(mrows * tk * tq * 4));
   } else {
@@ -283,6 +293,7 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   a.plan = reinterpret_cast<int32_t*>(w + L.plan);
   a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
   a.rep_kv = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : a.heads_kv);
+  a.part = L.part ? reinterpret_cast<float*>(w + L.part) : nullptr;
   // launch orders: key-tile rows of the transposed dK/dV map (one line per
   // K/V mask row and key tile, counting the class rows of the K/V head's
   // query heads when the mask has a row per head) and the query-tile rows of

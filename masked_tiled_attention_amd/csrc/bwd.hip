@@ -152,13 +152,19 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   // Key tiles longest first, then the (b, K/V head) pairs sharing the K/V
   // mask row; the workgroup runs the `group` query heads of its K/V head one
   // after the other, with dK, dV accumulating over all of them.
-  const int line = __builtin_amdgcn_readfirstlane(a.order_k[blockIdx.x / a.rep_kv]);   // K/V mask row * tk + key tile
+  // With split heads (a.part set; a mask shared by all heads), each of the
+  // `group` query heads of a K/V head has a workgroup of its own, which writes
+  // float32 partial dK, dV that a second kernel sums.
+  const int split = GROUPED && a.part != nullptr;
+  const int rep = split ? a.rep_kv * a.group : a.rep_kv;
+  const int line = __builtin_amdgcn_readfirstlane(a.order_k[blockIdx.x / rep]);   // K/V mask row * tk + key tile
   // (integer divisions by launch constants expand to vector code: the results
   // are taken back to scalar registers so that the addresses stay scalar)
   const int kt = __builtin_amdgcn_readfirstlane(line % a.tk);
   const int kr = __builtin_amdgcn_readfirstlane(line / a.tk);
   const int hkm = a.mask.hm > 1 ? a.heads_kv : 1;   // K/V mask rows per batch row
-  const int jr = __builtin_amdgcn_readfirstlane(blockIdx.x % a.rep_kv);
+  const int jr = __builtin_amdgcn_readfirstlane((blockIdx.x % rep) / (split ? a.group : 1));
+  const int gsel = __builtin_amdgcn_readfirstlane(split ? blockIdx.x % a.group : 0);   // the head (split heads)
   const int b = __builtin_amdgcn_readfirstlane(a.mask.bm > 1 ? kr / hkm : jr / (a.mask.hm > 1 ? 1 : a.heads_kv));
   const int hk = __builtin_amdgcn_readfirstlane(a.mask.hm > 1 ? kr % hkm : jr % a.heads_kv);
   const int bm = __builtin_amdgcn_readfirstlane(kr / hkm);
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   const char* xpeer = reinterpret_cast<const char*>(sm.xch[w ^ 4]);
   int it_global = 0;   // iteration count over heads and passes (selects the LDS buffer)
   const int ngroup = GROUPED ? a.group : 1;
-  for (int gi = 0; gi < ngroup; ++gi) {
+  for (int gi = gsel; gi < (split ? gsel + 1 : ngroup); ++gi) {
     h = hk * ngroup + gi;
     {
       const int hm = a.mask.hm > 1 ? h : 0;
@@ -509,7 +515,18 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
 
   // ---- epilogue: dV = dV^T (first half), dK = scale * dK^T (second half),
   // transposed back on store ----
-  if (key_ok) {
+  if (key_ok && split) {   // float32 partials [2][B][H][Sk][D]: dK, then dV
+    const bool is_k = mb == 1;
+    float* out = a.part + (is_k ? 0 : (int64_t)a.batch * a.heads * a.seq_k * D) +
+                 (((int64_t)b * a.heads + hk * a.group + gsel) * a.seq_k + n) * D;
+    const float sc = is_k ? a.scale : 1.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * q4 + 4 * g) =
+            f32x4{acc[cb][4 * q4] * sc, acc[cb][4 * q4 + 1] * sc, acc[cb][4 * q4 + 2] * sc, acc[cb][4 * q4 + 3] * sc};
+  } else if (key_ok) {
     const bool is_k = mb == 1;
     const int64_t off = is_k ? (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)hk * a.k_sh
                              : (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)hk * a.v_sh;
@@ -779,12 +796,48 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Split heads: dK, dV of K/V head hk = the sum of the float32 partials of its
+// `group` query heads; one thread per 4 channels of one key.
+template <int D, bool F32>
+__global__ __launch_bounds__(256) void kv_reduce_kernel(BwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (b, hk, n, c4)
+  const int64_t total = (int64_t)a.batch * a.heads_kv * a.seq_k * (D / 4);
+  if (i >= total) return;
+  const int c0 = (int)(i % (D / 4)) * 4;
+  const int n = (int)((i / (D / 4)) % a.seq_k);
+  const int hk = (int)((i / ((int64_t)(D / 4) * a.seq_k)) % a.heads_kv);
+  const int b = (int)(i / ((int64_t)(D / 4) * a.seq_k * a.heads_kv));
+  const int64_t half = (int64_t)a.batch * a.heads * a.seq_k * D;
+#pragma unroll
+  for (int kind = 0; kind < 2; ++kind) {   // 0: dK, 1: dV
+    f32x4 x = f32x4{};
+    for (int gi = 0; gi < a.group; ++gi)
+      x += *reinterpret_cast<const f32x4*>(a.part + kind * half +
+                                           (((int64_t)b * a.heads + hk * a.group + gi) * a.seq_k + n) * D + c0);
+    const int64_t off = kind == 0 ? (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)hk * a.k_sh + c0
+                                  : (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)hk * a.v_sh + c0;
+    void* out = kind == 0 ? a.dk : a.dv;
+    if constexpr (F32) {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = x;
+    } else {
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + off) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+    }
+  }
+}
+
 template <int D, bool F32>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t s) {
-  if (a.group > 1)
+  if (a.group > 1 && a.part != nullptr) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, true>), dim3(a.tk * a.batch * a.heads), dim3(kv::THREADS), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)a.batch * a.heads_kv * a.seq_k * (D / 4);
+    hipLaunchKernelGGL((kv_reduce_kernel<D, F32>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  } else if (a.group > 1) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, true>), dim3(a.tk * a.batch * a.heads_kv), dim3(kv::THREADS), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, F32, false>), dim3(a.tk * a.batch * a.heads_kv), dim3(kv::THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -133,6 +133,11 @@ struct BwdArgs {
   // tiling and the recompute dQ kernel's query tiles (may be nullptr).
   const int32_t* order_k;
   const int32_t* order_qq;
+  // Grouped-query attention with a mask shared by all heads: one dK/dV
+  // workgroup per query head, float32 partials [2][B][H][Sk][D] (dK, then dV)
+  // summed per K/V head afterwards; nullptr: a workgroup runs all the query
+  // heads of its K/V head.
+  float* part;
 };
 
 // (b, h) of workgroup p given the mask row it serves (see FwdArgs::order).
