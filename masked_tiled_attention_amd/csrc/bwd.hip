@@ -130,8 +130,9 @@ struct alignas(16) Smem {
 };
 }  // namespace kv
 
-// GROUPED: more than one query head per K/V head (the head loop runs
-// a.group times); without it the loop has one trip and folds away.
+// GROUPED: more than one query head per K/V head. The head loop runs the
+// group's a.group heads, or only the workgroup's own head with split heads
+// (a.part set); without GROUPED it has one trip and folds away.
 template <int D, bool F32, bool GROUPED>
 __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(BwdArgs a) {
   using namespace kv;
