@@ -149,6 +149,8 @@ struct Layout {
   size_t vt = 0;                   // FP8 forward: V^T tiles [B][H_kv][Tk][8 KiB]
   size_t order_k = 0, order_qq = 0;   // backward launch orders (counts, then order)
   size_t part = 0;                     // split-head dK/dV partials (0: not used)
+  size_t opart = 0, lpart = 0;         // split-list forward partials (0: not used)
+  int32_t ksplit = 1;
 };
 
 int64_t padded_rows(int64_t sq) { return ceil_div(sq, 128) * 128; }
@@ -159,6 +161,21 @@ int32_t kv_heads(const fm_problem* p) { return p->heads_kv > 0 ? p->heads_kv : p
 // workgroup per query head (float32 partials summed afterwards): a workgroup
 // that ran a whole group of heads over one key tile would be the longest one.
 bool split_heads(const fm_problem* p, const fm_mask* m) { return kv_heads(p) < p->heads && m->heads == 1; }
+
+// Parts per query tile's key-tile list in the bf16 / float32 forward. With
+// fewer workgroups than fill the chip about four times over (2048 for 256 CUs
+// at two per CU), the longest lists would bound the kernel, so lists are cut
+// into up to 8 parts, merged by a second kernel. Only long key ranges are
+// split (128 key tiles, 8192 keys, per part): the host cannot see how long
+// the lists are, and cutting short ones costs more than it saves.
+int32_t fwd_split(const fm_problem* p) {
+  if (p->dtype == FM_FP8_E4M3) return 1;
+  const int64_t nwg = ceil_div(p->seqlen_q, fm::kFwdBlockQ) * p->batch * p->heads;
+  const int64_t tk = ceil_div(p->seqlen_k, fm::kFwdBlockK);
+  int32_t ks = 1;
+  while (ks < 8 && nwg * 2 * ks <= 2048 && tk >= 128 * ks) ks *= 2;
+  return ks;
+}
 
 Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
   Layout L;
@@ -205,6 +222,14 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
     off = align256(off + rows);
     L.order = off;
     off = align256(off + rows);
+    L.ksplit = fwd_split(p);
+    if (L.ksplit > 1) {
+      const size_t rows_all = (size_t)L.ksplit * p->batch * p->heads * p->seqlen_q;
+      L.opart = off;
+      off = align256(off + rows_all * p->head_dim * 4);
+      L.lpart = off;
+      off = align256(off + rows_all * 4);
+    }
     if (p->dtype == FM_FP8_E4M3) {
       L.vt = off;
       off = align256(off + (size_t)((int64_t)p->batch * kv_heads(p) * ceil_div(p->seqlen_k, fm::kFwdBlockK) *
@@ -455,6 +480,11 @@ fm_status fwd_common(const fm_problem* p, const void* q, const void* k, const vo
   a.heads_kv = kv_heads(p);
   a.group = p->heads / a.heads_kv;
   a.o_scale = 1.f;
+  a.ksplit = L.ksplit;
+  if (L.ksplit > 1) {
+    a.opart = reinterpret_cast<float*>(w + L.opart);
+    a.lpart = reinterpret_cast<float*>(w + L.lpart);
+  }
   if (fp8) {
     if ((int64_t)p->batch * a.heads_kv * tk > INT32_MAX) return fail(FM_ERR_INVALID_ARGUMENT, "problem too large");
     fm::VtArgs va{};

@@ -63,6 +63,14 @@ struct FwdArgs {
   const uint8_t* vt;
   int32_t heads_kv;
   float o_scale;
+  // Split lists (bf16 / float32 forward): with ksplit > 1 each query tile's
+  // compacted key-tile list is cut into ksplit contiguous parts, one workgroup
+  // each, which write float32 partial O (normalised over their part) to
+  // opart [ksplit][B][H][Sq][D] and their LSE to lpart [ksplit][B][H][Sq];
+  // a second kernel merges them into O and LSE.
+  int32_t ksplit;
+  float* opart;
+  float* lpart;
 };
 
 // V^T pre-pass of the FP8 forward: V [B][Sk][H_kv][D] E4M3 codes (strides

@@ -78,9 +78,13 @@ void fwd_kernel(FwdArgs a) {
   const int g = l >> 5;
 
   // Query tiles longest first (order from the class map), then the (b, h)
-  // pairs that share the tile's mask row.
-  const int line = __builtin_amdgcn_readfirstlane(a.order[blockIdx.x / a.rep]);   // mask row * tq + query tile
-  const int j = blockIdx.x % a.rep;
+  // pairs that share the tile's mask row, then (split lists) the parts of the
+  // tile's key-tile list.
+  const int ks = a.ksplit > 1 ? a.ksplit : 1;
+  const int sp = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % ks));   // this workgroup's part
+  const int wg = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / ks));
+  const int line = __builtin_amdgcn_readfirstlane(a.order[wg / a.rep]);   // mask row * tq + query tile
+  const int j = wg % a.rep;
   const int qt = line % a.tq;
   const int mr = line / a.tq;
   const int bm = mr / a.mask.hm;
@@ -292,19 +296,34 @@ void fwd_kernel(FwdArgs a) {
     int n_full;
     const int n_list = compact_classes_split<LIST_CAP, NT>(crow, kt0, min(LIST_CAP, a.tk - kt0), sm.list, nullptr,
                                                            sm.scan, tid, false, &n_full, ragged_k ? a.tk - 1 : -1);
-    if (n_list == 0) continue;
+    // this workgroup's part of the list (all of it unless lists are split)
+    const int lo = (int)((int64_t)n_list * sp / ks), hi = (int)((int64_t)n_list * (sp + 1) / ks);
+    if (lo == hi) continue;
 
-    uint32_t ent = __builtin_amdgcn_readfirstlane(sm.list[0]);
+    uint32_t ent = __builtin_amdgcn_readfirstlane(sm.list[lo]);
     load_tile((int)(ent & ~kPartialBit), (ent & kPartialBit) != 0, it_global & 1);
-    int it = 0;
-    for (; it < n_full; ++it, ++it_global) iteration(std::false_type{}, it, n_list, ent);
-    for (; it < n_list; ++it, ++it_global) iteration(std::true_type{}, it, n_list, ent);
+    int it = lo;
+    for (; it < min(n_full, hi); ++it, ++it_global) iteration(std::false_type{}, it, hi, ent);
+    for (; it < hi; ++it, ++it_global) iteration(std::true_type{}, it, hi, ent);
   }
 
   // ---- epilogue: normalise once, write O and LSE ----
   const float lt = pair_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (row_ok) {
+  if (ks > 1) {   // split lists: float32 partial O and LSE of this part
+    if (row_ok) {
+      const int64_t r = (((int64_t)sp * a.batch + b) * a.heads + h) * a.seq_q + m;
+      float* op = a.opart + r * D;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(op + cb * 32 + 8 * q4 + 4 * g) =
+              f32x4{oacc[cb][4 * q4] * inv, oacc[cb][4 * q4 + 1] * inv, oacc[cb][4 * q4 + 2] * inv,
+                    oacc[cb][4 * q4 + 3] * inv};
+      if (g == 0) a.lpart[r] = lt > 0.f ? (m_run * C + __log2f(lt)) * kLn2 : -INFINITY;
+    }
+  } else if (row_ok) {
     const int64_t ooff = (int64_t)b * a.o_sb + (int64_t)m * a.o_ss + (int64_t)h * a.o_sh;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
@@ -327,10 +346,51 @@ void fwd_kernel(FwdArgs a) {
   }
 }
 
+// Split lists: O and LSE of each row from the parts' normalised partial O_s
+// and LSE_s: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the
+// parts' softmax weights). A row no part sees keeps O = 0, LSE = -inf. One
+// thread per 4 channels of one row.
+template <int D, bool F32>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // ((b * H + h) * Sq + m) * D / 4 + c4
+  const int64_t rows = (int64_t)a.batch * a.heads * a.seq_q;
+  if (i >= rows * (D / 4)) return;
+  const int64_t r = i / (D / 4);
+  const int c0 = (int)(i % (D / 4)) * 4;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.ksplit; ++s) mx = fmaxf(mx, a.lpart[s * rows + r]);
+  f32x4 o = f32x4{};
+  float lse = -INFINITY;
+  if (mx > -INFINITY) {
+    float sum = 0.f;
+    for (int s = 0; s < a.ksplit; ++s) sum += __expf(a.lpart[s * rows + r] - mx);
+    lse = mx + __logf(sum);
+    for (int s = 0; s < a.ksplit; ++s) {
+      const float ws = __expf(a.lpart[s * rows + r] - lse);
+      o += ws * *reinterpret_cast<const f32x4*>(a.opart + (s * rows + r) * D + c0);
+    }
+  }
+  const int m = (int)(r % a.seq_q);
+  const int h = (int)((r / a.seq_q) % a.heads);
+  const int b = (int)(r / ((int64_t)a.seq_q * a.heads));
+  const int64_t ooff = (int64_t)b * a.o_sb + (int64_t)m * a.o_ss + (int64_t)h * a.o_sh + c0;
+  if constexpr (F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.o) + ooff) = o;
+  } else {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + ooff) = u32x2{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+  }
+  if (c0 == 0) a.lse[r] = lse;
+}
+
 template <int D, bool F32>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  const int nblk = a.tq * a.batch * a.heads;
+  const int ks = a.ksplit > 1 ? a.ksplit : 1;
+  const int nblk = a.tq * a.batch * a.heads * ks;
   hipLaunchKernelGGL((fwd_kernel<D, F32>), dim3(nblk), dim3(NT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  const int64_t n = (int64_t)a.batch * a.heads * a.seq_q * (D / 4);
+  hipLaunchKernelGGL((fwd_merge_kernel<D, F32>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -75,6 +75,30 @@ def test_fwd_random_vectors_rectangular(gpu_lib):
             assert torch.all(lse[:, :, torch.from_numpy(empty)] == -math.inf)
 
 
+def test_fwd_split_lists(gpu_lib):
+    """Few workgroups and long key lists (256 rows x 65536 keys, 2 heads):
+    each query tile's key-tile list is cut into parts merged afterwards (8
+    here). Masks: none; random bounds; rows 100..159 masked for every key
+    (O = 0, LSE = -inf); only keys 0..319 open (five key tiles, so some parts
+    are empty); head_dim 64 and float32 as well."""
+    rng = np.random.default_rng(5)
+    sq, sk = 256, 65536
+    j = np.arange(sk)
+    i32 = lambda *xs: tuple(np.asarray(x, dtype=np.int32)[None, None] for x in xs)
+    masks = {
+        "none": i32(np.full(sk, sq), np.full(sk, sq), np.zeros(sk), np.zeros(sk)),
+        "random": i32(*(rng.integers(-20, sq + 20, sk) for _ in range(4))),
+        "dead rows": i32(np.full(sk, 100), np.full(sk, 160), rng.integers(0, sq, sk), rng.integers(0, sq, sk)),
+        "few keys": i32(np.where(j >= 320, 0, sq), np.full(sk, sq), np.zeros(sk), np.zeros(sk)),
+    }
+    for d, dtype in ((128, torch.bfloat16), (64, torch.bfloat16), (64, torch.float32)):
+        for t, (name, vec) in enumerate(masks.items()):
+            q, k, v = ST.qkv(1, sq, sk, 2, d, seed=80 + t, dtype=dtype)
+            o, lse = _compare_fwd(gpu_lib, q, k, v, vec, 1 / math.sqrt(d), f"split {name} d={d} {dtype}")
+            if name == "dead rows":
+                assert torch.all(o[:, 100:160] == 0) and torch.all(lse[:, :, 100:160] == -math.inf)
+
+
 def test_fwd_fully_masked_rows_and_tiles(gpu_lib):
     """Rows 100..299 see no key at all: whole query tiles are SKIP everywhere."""
     n = 600
