@@ -126,10 +126,13 @@ typedef struct {
 void fm_kernel_tile(int32_t head_dim, int32_t bwd, int32_t* block_q, int32_t* block_k);
 
 /* Bytes of device workspace fm_attn_fwd (with_bwd = 0) or fm_attn_bwd
- * (with_bwd = 1) needs at least: tile summaries and class maps, plus for the
- * backward the per-row terms LSE * log2(e) and D = rowsum(dO * O) and the
- * stored-dS plan counters. With this much, fm_attn_bwd recomputes S and dP a
- * second time for dQ. */
+ * (with_bwd = 1) needs at least: tile summaries and class maps; for a forward
+ * launch with few query tiles and long key ranges, float32 partial O and LSE
+ * of the parts its key-tile lists are cut into; for the backward the per-row
+ * terms LSE * log2(e) and D = rowsum(dO * O), the stored-dS plan counters
+ * and, for grouped-query attention with a mask shared by all heads, float32
+ * dK / dV partials per query head (8 * B * H * Sk * D bytes). With this much,
+ * fm_attn_bwd recomputes S and dP a second time for dQ. */
 fm_status fm_workspace_size(const fm_problem* problem, const fm_mask* mask,
                             int32_t with_bwd, size_t* bytes);
 
@@ -172,7 +175,10 @@ fm_status fm_tile_classify(const fm_mask* mask, int32_t seqlen_q, int32_t seqlen
  * evaluated only on PARTIAL tiles. workspace: device, at least
  * fm_workspace_size(.., 0) bytes, 256-byte aligned. Tiles are launched
  * longest first (by their number of non-SKIP partner tiles), here and in the
- * backward; the order does not change any result. */
+ * backward; the order does not change any result. When the launch has few
+ * query tiles and long key ranges, each query tile's list is cut into parts
+ * whose normalised partial results a second kernel merges (exact up to
+ * rounding order; deterministic). */
 fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, const void* v,
                       const fm_mask* mask, void* o, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
