@@ -151,6 +151,8 @@ struct Layout {
   size_t part = 0;                     // split-head dK/dV partials (0: not used)
   size_t opart = 0, lpart = 0;         // split-list forward partials (0: not used)
   int32_t ksplit = 1;
+  size_t dqpart = 0;                   // split-list stored-dS dQ partials (0: not used)
+  int32_t dq_split = 1;
 };
 
 int64_t padded_rows(int64_t sq) { return ceil_div(sq, 128) * 128; }
@@ -168,6 +170,16 @@ bool split_heads(const fm_problem* p, const fm_mask* m) { return kv_heads(p) < p
 // into up to 8 parts, merged by a second kernel. Only long key ranges are
 // split (128 key tiles, 8192 keys, per part): the host cannot see how long
 // the lists are, and cutting short ones costs more than it saves.
+// The same for the stored-dS dQ kernel's query-tile pairs (one workgroup per
+// CU: about four times over is 1024 workgroups; 64 key tiles of 128 per part).
+int32_t dq_split(const fm_problem* p) {
+  const int64_t nwg = ceil_div(ceil_div(p->seqlen_q, fm::kBwdBlockQ), 2) * p->batch * p->heads;
+  const int64_t tk = ceil_div(p->seqlen_k, fm::kBwdBlockK);
+  int32_t ks = 1;
+  while (ks < 8 && nwg * 2 * ks <= 1024 && tk >= 64 * ks) ks *= 2;
+  return ks;
+}
+
 int32_t fwd_split(const fm_problem* p) {
   if (p->dtype == FM_FP8_E4M3) return 1;
   const int64_t nwg = ceil_div(p->seqlen_q, fm::kFwdBlockQ) * p->batch * p->heads;
@@ -209,6 +221,11 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
     off = align256(off + (size_t)(mrows * tk * 8));
     L.order_qq = off;
     off = align256(off + (size_t)(mrows * tq_q * 8));
+    L.dq_split = dq_split(p);
+    if (L.dq_split > 1) {   // float32 dQ partials of the split lists
+      L.dqpart = off;
+      off = align256(off + (size_t)L.dq_split * p->batch * p->heads * p->seqlen_q * p->head_dim * 4);
+    }
     if (split_heads(p, m)) {   // float32 dK, dV partials per query head
       L.part = off;
       off = align256(off + (size_t)p->batch * p->heads * p->seqlen_k * p->head_dim * 4 * 2);
@@ -319,6 +336,8 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
   a.rep_kv = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : a.heads_kv);
   a.part = L.part ? reinterpret_cast<float*>(w + L.part) : nullptr;
+  a.dq_split = L.dq_split;
+  a.dqpart = L.dqpart ? reinterpret_cast<float*>(w + L.dqpart) : nullptr;
   // launch orders: key-tile rows of the transposed dK/dV map (one line per
   // K/V mask row and key tile, counting the class rows of the K/V head's
   // query heads when the mask has a row per head) and the query-tile rows of

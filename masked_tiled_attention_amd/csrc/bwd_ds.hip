@@ -13,10 +13,12 @@
 //   plan_count  non-SKIP tiles per key-tile row of the dK/dV class map;
 //   plan_scan   one workgroup: exclusive prefix sums (slot offsets), the total
 //               and whether the workspace holds every tile for every (b, h);
-//   dq_ds       one workgroup per (b, h, pair of 64-row query tiles): for each
-//               key tile non-SKIP for either, K and the pair's stored dS tiles
-//               go straight into LDS (two stages, one ahead) and
-//               dQ^T += K^T dS^T accumulates in registers.
+//   dq_ds       one workgroup per (b, h, pair of 64-row query tiles), or per
+//               part of the pair's list when few pairs have long key ranges:
+//               for each key tile non-SKIP for either, K and the pair's stored
+//               dS tiles go straight into LDS (two stages, one ahead) and
+//               dQ^T += K^T dS^T accumulates in registers;
+//   dq_merge    split lists: dQ = the sum of the parts' float32 partials.
 #include <climits>
 #include <cmath>
 
@@ -204,11 +206,16 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   // Later query tiles first, heads interleaved: neighbouring workgroups work
   // on nearby rows and share K tiles in L2 (this kernel is bound by memory
   // traffic, so that beats ordering by length).
+  // With split lists (a.dq_split > 1), consecutive workgroups take the
+  // parts of one pair's key-tile list and write float32 partial dQ.
+  const int ks = a.dq_split > 1 ? a.dq_split : 1;
+  const int sp = (int)(blockIdx.x % ks);   // this workgroup's part
+  const int wg = (int)(blockIdx.x / ks);
   const int nbh = a.batch * a.heads;
   const int npair = (a.tq + PAIR - 1) / PAIR;
-  const int qt0 = PAIR * (npair - 1 - (int)(blockIdx.x / nbh));
+  const int qt0 = PAIR * (npair - 1 - wg / nbh);
   const bool has1 = qt0 + 1 < a.tq;
-  const int bh = blockIdx.x % nbh;
+  const int bh = wg % nbh;
   const int b = bh / a.heads;
   const int h = bh % a.heads;
   const int mrow = (a.mask.bm > 1 ? b : 0) * a.mask.hm + (a.mask.hm > 1 ? h : 0);
@@ -292,14 +299,16 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
     const int n_list = compact_pair(ccol, scol, (int64_t)a.tq, kt0, min(LIST_CAP, a.tk - kt0), has1, sm.list,
                                     sm.slot, sm.scan, tid);
-    if (n_list == 0) continue;
-    stage(0, it_global % NSTAGE);
+    // this workgroup's part of the list (all of it unless lists are split)
+    const int lo = (int)((int64_t)n_list * sp / ks), hi = (int)((int64_t)n_list * (sp + 1) / ks);
+    if (lo == hi) continue;
+    stage(lo, it_global % NSTAGE);
 
-    for (int it = 0; it < n_list; ++it, ++it_global) {
+    for (int it = lo; it < hi; ++it, ++it_global) {
       const int buf = it_global % NSTAGE;
       wait_vmem();       // this stage landed (nothing younger is in flight)
       __syncthreads();   // stage `buf` visible to all; the stage read last iteration is free
-      if (it + 1 < n_list) stage(it + 1, (it_global + 1) % NSTAGE);
+      if (it + 1 < hi) stage(it + 1, (it_global + 1) % NSTAGE);
       const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
       const char* sb = reinterpret_cast<const char*>(sm.ds[buf]);
       const bool p0 = sm.slot[it][0] >= 0, p1 = sm.slot[it][1] >= 0;
@@ -318,7 +327,14 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
     const int c = lr;
     const int jj = c & 7;
     const int m = (qt0 + (rb >> 1)) * BQ + 32 * (rb & 1) + 16 * ((c >> 3) & 1) + 4 * (c >> 4) + (jj < 4 ? jj : jj + 4);
-    if (m < a.seq_q) {
+    if (m < a.seq_q && ks > 1) {   // float32 partial [ks][B][H][Sq][D]
+      float* out = a.dqpart + ((((int64_t)sp * a.batch + b) * a.heads + h) * a.seq_q + m) * D;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(out + 32 * cbw + 8 * q4 + 4 * g) =
+            f32x4{acc[j][4 * q4] * a.scale, acc[j][4 * q4 + 1] * a.scale, acc[j][4 * q4 + 2] * a.scale,
+                  acc[j][4 * q4 + 3] * a.scale};
+    } else if (m < a.seq_q) {
       const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
@@ -336,10 +352,39 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   }
 }
 
+// Split lists: dQ = the sum of the parts' float32 partials (fixed order), one
+// thread per 4 channels of one row. Exits when the plan chose the recompute
+// path.
+template <int D, bool F32>
+__global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a) {
+  if (a.plan == nullptr || a.plan[1] == 0) return;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // ((b * H + h) * Sq + m) * D / 4 + c4
+  const int64_t rows = (int64_t)a.batch * a.heads * a.seq_q;
+  if (i >= rows * (D / 4)) return;
+  const int64_t r = i / (D / 4);
+  const int c0 = (int)(i % (D / 4)) * 4;
+  f32x4 x = f32x4{};
+  for (int s = 0; s < a.dq_split; ++s) x += *reinterpret_cast<const f32x4*>(a.dqpart + (s * rows + r) * D + c0);
+  const int m = (int)(r % a.seq_q);
+  const int h = (int)((r / a.seq_q) % a.heads);
+  const int b = (int)(r / ((int64_t)a.seq_q * a.heads));
+  const int64_t off = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh + c0;
+  if constexpr (F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dq) + off) = x;
+  } else {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.dq) + off) = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+  }
+}
+
 template <int D, bool F32>
 hipError_t launch_dq_ds_t(const BwdArgs& a, hipStream_t s) {
+  const int ks = a.dq_split > 1 ? a.dq_split : 1;
   const int npair = (a.tq + PAIR - 1) / PAIR;
-  hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F32>), dim3(npair * a.batch * a.heads), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F32>), dim3(npair * a.batch * a.heads * ks), dim3(NT), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  const int64_t n = (int64_t)a.batch * a.heads * a.seq_q * (D / 4);
+  hipLaunchKernelGGL((dq_merge_kernel<D, F32>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

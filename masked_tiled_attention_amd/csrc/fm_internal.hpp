@@ -146,6 +146,11 @@ struct BwdArgs {
   // summed per K/V head afterwards; nullptr: a workgroup runs all the query
   // heads of its K/V head.
   float* part;
+  // Stored-dS dQ with split lists: with dq_split > 1 each query-tile pair's
+  // key-tile list is cut into dq_split parts, one workgroup each, writing
+  // float32 partial dQ [dq_split][B][H][Sq][D] that a second kernel sums.
+  int32_t dq_split;
+  float* dqpart;
 };
 
 // (b, h) of workgroup p given the mask row it serves (see FwdArgs::order).

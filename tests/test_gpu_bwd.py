@@ -177,11 +177,18 @@ def test_bwd_key_tiles_masked_for_every_row(gpu_lib):
 
 def test_bwd_stored_ds_more_key_tiles_than_one_list(gpu_lib):
     """140,000 keys: 1094 key tiles, more than one compacted list of the dQ
-    kernel, which then walks its key tiles in two passes."""
+    kernel, which then walks its key tiles in two passes. With so few query
+    tiles the lists are also split into parts (8 here, 4 for the random mask
+    over 16,384 keys) whose partial dQ a second kernel sums."""
     sq, sk = 200, 140000
     vec = tuple(x[None, None] for x in SM.no_mask(sk, sq))
     q, k, v, do = ST.qkv(1, sq, sk, 1, 128, seed=43, with_do=True)
     _compare_ds(gpu_lib, q, k, v, do, vec, 0.088, "140k keys")
+    rng = np.random.default_rng(44)
+    sq, sk = 300, 16384
+    vec = tuple(rng.integers(-20, sq + 20, (1, 1, sk)).astype(np.int32) for _ in range(4))
+    q, k, v, do = ST.qkv(1, sq, sk, 2, 128, seed=45, with_do=True)
+    _compare_ds(gpu_lib, q, k, v, do, vec, 0.088, "random 300x16384")
 
 
 def test_bwd_stored_ds_float32_inputs(gpu_lib):
@@ -207,10 +214,13 @@ def test_bwd_stored_ds_path_is_taken(gpu_lib):
         ws = torch.empty(full - short, dtype=torch.uint8, device="cuda")
         gpu_lib.fm_attn_bwd(q, k, v, o, lse, do, m, 0.088, workspace=ws)
         torch.cuda.synchronize()
-        gpu_lib.fm_profile_begin(64)
-        gpu_lib.fm_attn_bwd(q, k, v, o, lse, do, m, 0.088, workspace=ws)
-        st = gpu_lib.fm_profile_end()
-        times[short] = (st["bwd_dq"][0], st["bwd_dq_ds"][0])
+        runs = []
+        for _ in range(3):   # the fastest of three calls: one slow outlier does not decide
+            gpu_lib.fm_profile_begin(64)
+            gpu_lib.fm_attn_bwd(q, k, v, o, lse, do, m, 0.088, workspace=ws)
+            st = gpu_lib.fm_profile_end()
+            runs.append((st["bwd_dq"][0], st["bwd_dq_ds"][0]))
+        times[short] = (min(r[0] for r in runs), min(r[1] for r in runs))
     log(f"dQ kernel ms (recompute, stored dS): full workspace {times[0]}, one byte short {times[1]}")
     # each dQ kernel takes several times longer when its path is the one taken
     # (an exiting launch still costs a few microseconds)
