@@ -164,14 +164,12 @@ int32_t kv_heads(const fm_problem* p) { return p->heads_kv > 0 ? p->heads_kv : p
 // that ran a whole group of heads over one key tile would be the longest one.
 bool split_heads(const fm_problem* p, const fm_mask* m) { return kv_heads(p) < p->heads && m->heads == 1; }
 
-// Parts per query tile's key-tile list in the bf16 / float32 forward. With
-// fewer workgroups than fill the chip about four times over (2048 for 256 CUs
-// at two per CU), the longest lists would bound the kernel, so lists are cut
-// into up to 8 parts, merged by a second kernel. Only long key ranges are
-// split (128 key tiles, 8192 keys, per part): the host cannot see how long
-// the lists are, and cutting short ones costs more than it saves.
-// The same for the stored-dS dQ kernel's query-tile pairs (one workgroup per
-// CU: about four times over is 1024 workgroups; 64 key tiles of 128 per part).
+// Parts per query-tile pair's key-tile list in the stored-dS dQ kernel (one
+// workgroup per CU). A launch with few pairs and long lists is bound by its
+// longest lists, so the count doubles (up to 8) while the split launch stays
+// within 1024 workgroups and each part keeps at least 32 key tiles of 128
+// keys. The host cannot see the list lengths; cutting short ones costs more
+// than it saves.
 int32_t dq_split(const fm_problem* p) {
   const int64_t nwg = ceil_div(ceil_div(p->seqlen_q, fm::kBwdBlockQ), 2) * p->batch * p->heads;
   const int64_t tk = ceil_div(p->seqlen_k, fm::kBwdBlockK);
@@ -180,6 +178,9 @@ int32_t dq_split(const fm_problem* p) {
   return ks;
 }
 
+// The same for the query tiles of the bf16 / float32 forward (two workgroups
+// per CU): the count doubles (up to 8) while the split launch stays within
+// 2048 workgroups and each part keeps at least 64 key tiles of 64 keys.
 int32_t fwd_split(const fm_problem* p) {
   if (p->dtype == FM_FP8_E4M3) return 1;
   const int64_t nwg = ceil_div(p->seqlen_q, fm::kFwdBlockQ) * p->batch * p->heads;
