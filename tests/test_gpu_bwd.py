@@ -189,6 +189,10 @@ def test_bwd_stored_ds_more_key_tiles_than_one_list(gpu_lib):
     vec = tuple(rng.integers(-20, sq + 20, (1, 1, sk)).astype(np.int32) for _ in range(4))
     q, k, v, do = ST.qkv(1, sq, sk, 2, 128, seed=45, with_do=True)
     _compare_ds(gpu_lib, q, k, v, do, vec, 0.088, "random 300x16384")
+    # float32 inputs, head_dim 64: the same split with float32 partials and output
+    q, k, v, do = ST.qkv(1, 200, 16384, 1, 64, seed=46, dtype=torch.float32, with_do=True)
+    _compare_ds(gpu_lib, q, k, v, do, tuple(x[None, None] for x in SM.no_mask(16384, 200)), 0.125,
+                "float32 200x16384", out_round=0.0)
 
 
 def test_bwd_stored_ds_float32_inputs(gpu_lib):

@@ -80,7 +80,7 @@ def test_fwd_split_lists(gpu_lib):
     each query tile's key-tile list is cut into parts merged afterwards (8
     here). Masks: none; random bounds; rows 100..159 masked for every key
     (O = 0, LSE = -inf); only keys 0..319 open (five key tiles, so some parts
-    are empty); head_dim 64 and float32 as well."""
+    are empty); head_dim 64 and 128, bf16 and float32."""
     rng = np.random.default_rng(5)
     sq, sk = 256, 65536
     j = np.arange(sk)
@@ -91,7 +91,7 @@ def test_fwd_split_lists(gpu_lib):
         "dead rows": i32(np.full(sk, 100), np.full(sk, 160), rng.integers(0, sq, sk), rng.integers(0, sq, sk)),
         "few keys": i32(np.where(j >= 320, 0, sq), np.full(sk, sq), np.zeros(sk), np.zeros(sk)),
     }
-    for d, dtype in ((128, torch.bfloat16), (64, torch.bfloat16), (64, torch.float32)):
+    for d, dtype in ((128, torch.bfloat16), (64, torch.bfloat16), (64, torch.float32), (128, torch.float32)):
         for t, (name, vec) in enumerate(masks.items()):
             q, k, v = ST.qkv(1, sq, sk, 2, d, seed=80 + t, dtype=dtype)
             o, lse = _compare_fwd(gpu_lib, q, k, v, vec, 1 / math.sqrt(d), f"split {name} d={d} {dtype}")
