@@ -162,7 +162,12 @@ int32_t kv_heads(const fm_problem* p) { return p->heads_kv > 0 ? p->heads_kv : p
 // Grouped-query attention whose mask is shared by all heads runs one dK/dV
 // workgroup per query head (float32 partials summed afterwards): a workgroup
 // that ran a whole group of heads over one key tile would be the longest one.
-bool split_heads(const fm_problem* p, const fm_mask* m) { return kv_heads(p) < p->heads && m->heads == 1; }
+// Its partials take 8 * B * H * Sk * D bytes of workspace; beyond 4 GiB the
+// workgroups run their K/V head's query heads in turn instead.
+bool split_heads(const fm_problem* p, const fm_mask* m) {
+  const uint64_t bytes = (uint64_t)p->batch * p->heads * p->seqlen_k * p->head_dim * 8;
+  return kv_heads(p) < p->heads && m->heads == 1 && bytes <= (uint64_t(4) << 30);
+}
 
 // Parts per query-tile pair's key-tile list in the stored-dS dQ kernel (one
 // workgroup per CU). A launch with few pairs and long lists is bound by its
