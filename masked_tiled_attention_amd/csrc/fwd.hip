@@ -236,6 +236,26 @@ void fwd_kernel(FwdArgs a) {
     l_run += rs;
   };
 
+  // Offsets of the transposed V reads, computed once. The swizzle depends on
+  // the row modulo 16 only, so the 16-key steps of a tile (+16 rows) are
+  // immediate offsets on the same address, and per tile only the buffer is
+  // added. The offsets are made opaque so that the compiler keeps them whole
+  // rather than rebuilding them per read.
+  uint32_t vo[CB][2];
+  {
+    const uint32_t vbase = lds_address(sm.v[0]);
+    const int i = l & 15;
+    const int r = 4 * g + (i >> 2);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = 32 * cb + 16 * ((l >> 4) & 1) + 4 * (i & 3);
+      vo[cb][0] = vbase + (uint32_t)rm_byte<D>(r, col);
+      vo[cb][1] = vbase + (uint32_t)rm_byte<D>(r + 8, col);
+      asm volatile("" : "+v"(vo[cb][0]));
+      asm volatile("" : "+v"(vo[cb][1]));
+    }
+  }
+
   int it_global = 0;   // iteration count across passes (selects the LDS buffer)
   auto iteration = [&](auto masked_c, int it, int n_list, uint32_t& ent) {
     constexpr bool MASKED = decltype(masked_c)::value;
@@ -248,7 +268,19 @@ void fwd_kernel(FwdArgs a) {
       load_tile((int)(ent & ~kPartialBit), (ent & kPartialBit) != 0, buf ^ 1);
     }
     const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
-    const char* vb = reinterpret_cast<const char*>(sm.v[buf]);
+    const uint32_t bo = (uint32_t)buf * (BK * D * 2);
+    uint32_t vt_addr[CB][2];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      vt_addr[cb][0] = vo[cb][0] + bo;
+      vt_addr[cb][1] = vo[cb][1] + bo;
+    }
+    // V^T operand of the 16 keys from row 16 rr of the tile (rr = 0..3)
+    auto vt = [&](int cb, int rr) {
+      const u32x2 x = lds_tr16(vt_addr[cb][0], (uint32_t)rr * (16 * 2 * D));
+      const u32x2 y = lds_tr16(vt_addr[cb][1], (uint32_t)rr * (16 * 2 * D));
+      return u32x4{x[0], x[1], y[0], y[1]};
+    };
     f32x16 sacc[NB];
 
     // S^T = K Q^T, first 32 keys
@@ -270,24 +302,18 @@ void fwd_kernel(FwdArgs a) {
 
     // O^T += V^T P^T over the first 32 keys, under the second half's softmax
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r0 = 16 * t + 4 * g;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        oacc[cb] = mfma32(tr_operand<D>(vb, l, cb * 32, r0, r0 + 8), pf[0][t], oacc[cb]);
-    }
+      for (int cb = 0; cb < CB; ++cb) oacc[cb] = mfma32(vt(cb, t), pf[0][t], oacc[cb]);
     if constexpr (MASKED) mask_half(sacc[1], 1, buf);
     const float rs1 = soft_half(sacc[1], 1);
     settle_half(sacc[1], 1, rs1);
 
     // O^T += V^T P^T over the second 32 keys
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r0 = 32 + 16 * t + 4 * g;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-        oacc[cb] = mfma32(tr_operand<D>(vb, l, cb * 32, r0, r0 + 8), pf[1][t], oacc[cb]);
-    }
+      for (int cb = 0; cb < CB; ++cb) oacc[cb] = mfma32(vt(cb, 2 + t), pf[1][t], oacc[cb]);
     sched_lds_mfma<2 * CB, 2, 3>();
   };
 
