@@ -89,8 +89,6 @@ __device__ __forceinline__ void sched_lds_mfma() {
 // Lane id within the wavefront.
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
-
 // max / sum of x over the lane pair (l, l ^ 32), one v_permlane32_swap (no
 // LDS round trip). Both lanes of a pair get bit-identical results.
 __device__ __forceinline__ float pair_max(float x) {
@@ -100,15 +98,6 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Map a linear workgroup index so that consecutive logical indices land on
-// the same XCD (workgroups are dispatched round-robin over the 8 XCDs).
-// Logical tiles that share K/V then share an L2.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int per = n / 8;
-  if (bid >= per * 8) return bid;
-  return (bid % 8) * per + bid / 8;
 }
 
 }  // namespace fm

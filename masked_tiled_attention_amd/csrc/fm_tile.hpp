@@ -354,24 +354,4 @@ __device__ __forceinline__ void wait_vmem_le() {
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
-// wait_vmem_le<n>() for a wavefront-uniform n in [0, 31] (larger n: n = 31,
-// which waits for more than asked, never less).
-__device__ __forceinline__ void wait_vmem_upto(int n) {
-  switch (n) {
-#define FM_WAIT_CASE(k) \
-  case k:               \
-    wait_vmem_le<k>();  \
-    break;
-    FM_WAIT_CASE(0) FM_WAIT_CASE(1) FM_WAIT_CASE(2) FM_WAIT_CASE(3) FM_WAIT_CASE(4) FM_WAIT_CASE(5)
-    FM_WAIT_CASE(6) FM_WAIT_CASE(7) FM_WAIT_CASE(8) FM_WAIT_CASE(9) FM_WAIT_CASE(10) FM_WAIT_CASE(11)
-    FM_WAIT_CASE(12) FM_WAIT_CASE(13) FM_WAIT_CASE(14) FM_WAIT_CASE(15) FM_WAIT_CASE(16) FM_WAIT_CASE(17)
-    FM_WAIT_CASE(18) FM_WAIT_CASE(19) FM_WAIT_CASE(20) FM_WAIT_CASE(21) FM_WAIT_CASE(22) FM_WAIT_CASE(23)
-    FM_WAIT_CASE(24) FM_WAIT_CASE(25) FM_WAIT_CASE(26) FM_WAIT_CASE(27) FM_WAIT_CASE(28) FM_WAIT_CASE(29)
-    FM_WAIT_CASE(30)
-#undef FM_WAIT_CASE
-    default:
-      wait_vmem_le<31>();
-  }
-}
-
 }  // namespace fm
