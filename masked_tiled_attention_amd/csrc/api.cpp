@@ -169,8 +169,8 @@ bool split_heads(const fm_problem* p, const fm_mask* m) {
   return kv_heads(p) < p->heads && m->heads == 1 && bytes <= (uint64_t(4) << 30);
 }
 
-// Parts per query-tile pair's key-tile list in the stored-dS dQ kernel (one
-// workgroup per CU). A launch with few pairs and long lists is bound by its
+// Parts per query-tile pair's key-tile list in the stored-dS dQ kernel (two
+// workgroups per CU). A launch with few pairs and long lists is bound by its
 // longest lists, so the count doubles (up to 8) while the split launch stays
 // within 1024 workgroups and each part keeps at least 32 key tiles of 128
 // keys. The host cannot see the list lengths; cutting short ones costs more
