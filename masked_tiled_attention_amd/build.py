@@ -37,9 +37,16 @@ COMMON = [
 ]
 
 
+# Per-source additions. The dK/dV kernel's loop is scheduled for instruction-
+# level parallelism rather than the default occupancy-first strategy: its
+# occupancy is fixed at two wavefronts per SIMD anyway, and the ILP schedule
+# measured 3.56 against 3.62 ms at 128K document-causal.
+EXTRA = {"bwd.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
