@@ -17,7 +17,9 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
+import statistics
 import sys
 import time
 
@@ -45,28 +47,47 @@ def nnz_of(vectors, seq_q, batch, heads):
     return total
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3
-    FETCH_SIZE / WRITE_SIZE summaries under profiles/, or None when none was
-    taken on the kernel's current source (sha256 prefix recorded with it)."""
+SOURCES = {"fwd": "fwd.hip", "bwd": "bwd.hip", "bwd_dq": "bwd.hip", "bwd_dq_ds": "bwd_ds.hip",
+           "fwd_fp8": "fwd_fp8.hip"}
+
+
+def _profile_record(tag: str, kernel: str, workload: str):
+    """Value of a machine-readable line `<tag>: kernel=K workload=W
+    source=F sha256=H <key>=V` in the summaries under profiles/, kept only
+    while F's sha256 prefix still equals H (the kernel has not changed since
+    the profile was taken); else None."""
     import glob
     import hashlib
     import re
     root = os.path.dirname(os.path.abspath(__file__))
-    src = {"fwd": "fwd.hip", "bwd": "bwd.hip", "bwd_dq": "bwd.hip", "bwd_dq_ds": "bwd_ds.hip",
-           "fwd_fp8": "fwd_fp8.hip"}.get(kernel)
+    src = SOURCES.get(kernel)
     if src is None:
         return None
     with open(os.path.join(root, "masked_tiled_attention_amd", "csrc", src), "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()[:16]
-    pat = re.compile(r"traffic: kernel=(\S+) workload=(\S+) source=(\S+) sha256=(\S+) bytes=(\d+)")
+    pat = re.compile(tag + r": kernel=(\S+) workload=(\S+) source=(\S+) sha256=(\S+) \w+=([0-9.]+)")
     for path in sorted(glob.glob(os.path.join(root, "profiles", "*.md"))):
         with open(path) as f:
             for line in f:
                 m = pat.match(line.strip())
                 if m and m[1] == kernel and m[2] == workload and m[3] == src and m[4] == digest:
-                    return int(m[5])
+                    return float(m[5])
     return None
+
+
+def profiled_kernel_us(kernel: str, workload: str):
+    """rocprofv3 average duration (us) of `kernel` over the timed steps of a
+    bench.py run on `workload`, from the kernel-stats summaries under
+    profiles/ (None when none matches the kernel's current source)."""
+    return _profile_record("kernel_avg", kernel, workload)
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE summaries under profiles/, or None when none was
+    taken on the kernel's current source."""
+    v = _profile_record("traffic", kernel, workload)
+    return None if v is None else int(v)
 
 
 class Runner:
@@ -148,6 +169,10 @@ class Runner:
             fm.fm_attn_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.mask, w.scale,
                            dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_b)
 
+    def dq_path(self):
+        """True when the last backward formed dQ from stored dS tiles."""
+        return self.fm.fm_bwd_dq_path(self.q, self.k, self.v, self.mask, self.ws_b, self.w.scale)
+
     def flops(self):
         d = self.w.head_dim
         return 4 * d * self.nnz, (10 * d * self.nnz if self.w.backward else 0)
@@ -179,22 +204,46 @@ class Fp8Runner:
                                 workspace=self.ws)
 
 
-def time_steps(r, steps, warmup, torch, profile=True):
-    fm = r.fm
+def time_steps(r, steps, warmup, torch, min_ms=0.0):
+    """Wall time of whole steps on the launch stream, with nothing recorded
+    inside a step: `warmup` untimed steps, then `steps` timed ones (more, when
+    min_ms is set, until the timed region lasts about min_ms), one HIP event
+    at each step boundary. Returns {"steps", "mean", "median", "min"} in ms
+    per step."""
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if profile:
-        fm.fm_profile_begin(64 * steps + 64)
-    start.record()
+    n = steps
+    if min_ms > 0:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(2):
+            r.step()
+        e1.record()
+        torch.cuda.synchronize()
+        est = max(e0.elapsed_time(e1) / 2, 1e-3)
+        n = max(steps, int(math.ceil(min_ms / est)))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for i in range(n):
+        r.step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    return {"steps": n, "mean": ev[0].elapsed_time(ev[n]) / n, "median": statistics.median(per), "min": min(per)}
+
+
+def stage_times(r, steps, torch):
+    """Per-stage kernel times from a separate, instrumented pass: the library
+    records a HIP event pair around each of its launches, on the launch
+    stream. Returns {stage: (ms per step, ms per launch, launches per step)}."""
+    fm = r.fm
+    torch.cuda.synchronize()
+    fm.fm_profile_begin(64 * steps + 64)
     for _ in range(steps):
         r.step()
-    stop.record()
-    torch.cuda.synchronize()
-    stages = fm.fm_profile_end() if profile else {}
-    ms = start.elapsed_time(stop) / steps
-    return ms, stages
+    raw = fm.fm_profile_end()
+    return {s: (v[0] / steps, v[0] / v[1] if v[1] else 0.0, v[1] / steps) for s, v in raw.items()}
 
 
 def cpu_baseline(w, vectors, budget_rows=None):
@@ -231,11 +280,39 @@ def cpu_baseline(w, vectors, budget_rows=None):
                       f"{dt:.1f} s, float64 numpy"}
 
 
+def _tflops(flops, ms):
+    return round(flops / (ms * 1e-3) / 1e12, 2) if ms > 0 else None
+
+
+def _timing(t):
+    return {"steps": t["steps"], "mean_ms": round(t["mean"], 4), "median_ms": round(t["median"], 4),
+            "min_ms": round(t["min"], 4)}
+
+
+# Executed matrix flops per open pair of each attention kernel: forward 4d
+# (QK^T, PV), dK/dV kernel 8d (QK^T, dO V^T, P^T dO, dS^T Q), recompute dQ
+# kernel 6d (QK^T, dO V^T, dS K), dQ from stored dS 2d (dS K).
+KERNEL_FLOPS_PER_PAIR = {"fwd": 4, "bwd": 8, "bwd_dq": 6, "bwd_dq_ds": 2}
+BWD_STAGES = ("bwd_pre", "bwd_plan", "bwd", "bwd_dq", "bwd_dq_ds")
+
+
+def split_ms(st, backward):
+    """(forward ms, backward ms) per step from stage times. Classification
+    runs once in the forward and twice in the backward (one per backward
+    tiling); its small cost is split in that ratio, as is the launch-order
+    pass."""
+    per = lambda s: st[s][0]
+    shared = per("classify_summary") + per("classify_map") + per("order")
+    fwd_ms = per("fwd") + (shared / 3 if backward else shared)
+    bwd_ms = sum(per(s) for s in BWD_STAGES) + 2 * shared / 3 if backward else 0.0
+    return fwd_ms, bwd_ms
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -275,21 +352,25 @@ def main():
         log(f"[bench] reference copy: {nbytes} bytes read, {nbytes} bytes written")
         del src, dst
 
+    # sweep lines: at least 5 warm-up steps, then at least 20 timed steps or
+    # 200 ms, whichever is longer; stage times from a separate 5-step pass
+    SW_WARM, SW_STEPS, SW_MIN_MS, ST_STEPS = 5, 20, 200.0, 5
+
     if args.fp8_forward:
         w = SC.build(args.workload, args.seed, tensors=False)
         r = Fp8Runner(fm, w, torch, args.seed)
-        ms, stages = time_steps(r, args.steps, args.warmup, torch)
-        per = lambda s: stages[s][0] / max(1, args.steps)
+        t = time_steps(r, args.steps, args.warmup, torch)
+        st = stage_times(r, ST_STEPS, torch)
         flops = 4 * w.head_dim * r.nnz
-        kms = stages["fwd"][0] / max(1, stages["fwd"][1])
+        kms = st["fwd"][1]
         achieved = flops / (kms * 1e-3) / 1e12
         print(json.dumps({
-            "metric": "fp8_forward_throughput", "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-            "higher_is_better": True, "dtype": "fp8_e4m3", "data": "synthetic",
+            "metric": "fp8_forward_throughput", "value": _tflops(flops, t["mean"]), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t["mean"], 4),
+            "timing": _timing(t), "higher_is_better": True, "dtype": "fp8_e4m3", "data": "synthetic",
             "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_q": w.seq_q, "seq_k": w.seq_k,
                        "head_dim": w.head_dim, "nnz": r.nnz, "passes": "fwd"},
-            "stages_ms_per_step": {s_: round(v[0] / max(1, args.steps), 4) for s_, v in stages.items() if v[1]},
+            "stages_ms_per_step": {s_: round(v[0], 4) for s_, v in st.items() if v[2]},
             "roofline": {"bound": "mfma", "kernel": "fwd_fp8", "kernel_ms": round(kms, 4), "achieved": round(achieved, 2),
                          "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                          "traffic": measured_traffic("fwd_fp8", w.name)}}), flush=True)
@@ -299,34 +380,34 @@ def main():
     w = SC.build(args.workload, args.seed)
     store_ds = not args.no_store_ds
     r = Runner(fm, w, torch, store_ds)
-    ms, stages = time_steps(r, args.steps, args.warmup, torch)
+    t = time_steps(r, args.steps, args.warmup, torch)
+    ms = t["mean"]
+    st = stage_times(r, max(5, min(args.steps, 20)), torch)
     f_fwd, f_bwd = r.flops()
-    per = lambda s: stages[s][0] / max(1, args.steps)
-    # classification runs once in the forward and twice in the backward (one
-    # per backward kernel tiling); its small cost is split in that ratio
-    cls_ms = per("classify_summary") + per("classify_map")
-    fwd_ms = per("fwd") + (cls_ms / 3 if w.backward else cls_ms)
-    bwd_ms = (per("bwd_pre") + per("bwd_plan") + per("bwd") + per("bwd_dq") + per("bwd_dq_ds") + 2 * cls_ms / 3
-              if w.backward else 0.0)
+    fwd_ms, bwd_ms = split_ms(st, w.backward)
     total_tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
-    log(f"[bench] {w.name}: {ms:.3f} ms/step, {total_tflops:.1f} TFLOP/s")
+    log(f"[bench] {w.name}: {ms:.3f} ms/step (median {t['median']:.3f}, min {t['min']:.3f}), "
+        f"{total_tflops:.1f} TFLOP/s")
 
-    # dominant kernel: the one with the largest time per step. Executed matrix
-    # flops per open pair: forward 4d (QK^T, PV), dK/dV kernel 8d (QK^T, dO V^T,
-    # P^T dO, dS^T Q), dQ kernel 6d (QK^T, dO V^T, dS K) or, from stored dS, 2d.
+    # dominant kernel: the one with the largest time per step
     d = w.head_dim
-    kernel_flops = {"fwd": 4 * d * r.nnz, "bwd": 8 * d * r.nnz, "bwd_dq": 6 * d * r.nnz,
-                    "bwd_dq_ds": 2 * d * r.nnz}
-    kern = max((k for k in kernel_flops if stages[k][1]), key=lambda s: stages[s][0])
-    kflops = kernel_flops[kern]
-    kms = stages[kern][0] / max(1, stages[kern][1])
+    kern = max((k for k in KERNEL_FLOPS_PER_PAIR if st[k][2]), key=lambda s_: st[s_][0])
+    kflops = KERNEL_FLOPS_PER_PAIR[kern] * d * r.nnz
+    kms = st[kern][1]
     achieved = kflops / (kms * 1e-3) / 1e12
+    prof_us = profiled_kernel_us(kern, w.name)
+    roof = {"bound": "mfma", "kernel": kern, "kernel_ms": round(kms, 4), "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(kern, w.name),
+            "flop_per_launch": kflops,
+            "kernel_ms_rocprof": None if prof_us is None else round(prof_us / 1e3, 4),
+            "frac_rocprof": None if prof_us is None else round(kflops / (prof_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     out = {
         "metric": METRIC,
         "value": round(total_tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": t["steps"],
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
@@ -339,23 +420,40 @@ def main():
                    "passes": "fwd+bwd" if w.backward else "fwd", "nnz": r.nnz,
                    "dq_from": ("stored dS" if store_ds else "recompute") if w.backward else None,
                    "density": round(r.nnz / (w.batch * w.heads * w.seq_q * w.seq_k), 5)},
+        "timing": _timing(t),
         "pct_of_bf16_peak": round(100 * total_tflops / PEAK_BF16_TFLOPS, 2),
-        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None},
-        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None},
-        "stages_ms_per_step": {s: round(v[0] / max(1, args.steps), 4) for s, v in stages.items() if v[1]},
-        "roofline": {"bound": "mfma", "kernel": kern, "kernel_ms": round(kms, 4),
-                     "achieved": round(achieved, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(kern, w.name)},
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": _tflops(f_fwd, fwd_ms)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": _tflops(f_bwd, bwd_ms),
+                "workspace_bytes": r.ws_b_bytes if w.backward else None},
+        "stages_ms_per_step": {s_: round(v[0], 4) for s_, v in st.items() if v[2]},
+        "roofline": roof,
     }
+    if w.backward:
+        log(f"[bench] dQ path of the timed backward: {'stored dS' if r.dq_path() else 'recompute'}")
+        out["config"]["dq_from"] = "stored dS" if r.dq_path() else "recompute"
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, r.vectors)
+    del r
+    torch.cuda.empty_cache()
+    if w.backward and store_ds:
+        # the same step with the minimum workspace: dQ recomputes S and dP, and
+        # no intermediate matrix is kept in HBM
+        log(f"[bench] {w.name} with the minimum backward workspace (recompute dQ)")
+        rr = Runner(fm, w, torch, store_ds=False)
+        tr = time_steps(rr, args.steps, args.warmup, torch)
+        sr = stage_times(rr, 5, torch)
+        _, bwd_r = split_ms(sr, True)
+        out["bwd_recompute"] = {
+            "ms": round(bwd_r, 4), "tflops": _tflops(f_bwd, bwd_r), "workspace_bytes": rr.ws_b_bytes,
+            "dq_kernel_ms": round(sr["bwd_dq"][1], 4),
+            "dq_kernel_tflops": _tflops(6 * d * rr.nnz, sr["bwd_dq"][1]),
+            "step": {"tflops": _tflops(f_fwd + f_bwd, tr["mean"]), **_timing(tr)},
+            "dq_from": "stored dS" if rr.dq_path() else "recompute"}
+        del rr
+        torch.cuda.empty_cache()
     if not args.no_sweep:
         sweep = []
-        del r
-        torch.cuda.empty_cache()
         # the other workloads, then grouped-query attention on the prefix-LM
         # workload (8 query heads on 2 K/V heads)
         jobs = [(name, None) for name in SC.NAMES if name != args.workload] + [("c3b_prefix_lm_32k", 2)]
@@ -366,25 +464,25 @@ def main():
                 wx.k = wx.k[:, :, :kv_heads].contiguous()
                 wx.v = wx.v[:, :, :kv_heads].contiguous()
             rx = Runner(fm, wx, torch, store_ds)
-            msx, st = time_steps(rx, 5, 2, torch)
+            tx = time_steps(rx, SW_STEPS, SW_WARM, torch, SW_MIN_MS)
+            sx = stage_times(rx, ST_STEPS, torch)
             a, b = rx.flops()
-            pf = lambda s: st[s][0] / 5
             item = {"workload": name + (f" ({wx.heads} query heads on {kv_heads} K/V heads)" if kv_heads else ""),
-                    "nnz": rx.nnz, "ms_per_step": round(msx, 4),
-                    "tflops": round((a + b) / (msx * 1e-3) / 1e12, 2),
-                    "fwd_kernel_tflops": round(a / (pf("fwd") * 1e-3) / 1e12, 2)}
+                    "nnz": rx.nnz, "ms_per_step": round(tx["mean"], 4), "timing": _timing(tx),
+                    "tflops": _tflops(a + b, tx["mean"]),
+                    "fwd_kernel_tflops": _tflops(a, sx["fwd"][0])}
             if wx.backward:
-                item["dkdv_kernel_tflops"] = round(8 * wx.head_dim * rx.nnz / (pf("bwd") * 1e-3) / 1e12, 2)
-                if st["bwd_dq_ds"][1] and pf("bwd_dq_ds") > pf("bwd_dq"):
-                    item["dq_ds_kernel_tflops"] = round(2 * wx.head_dim * rx.nnz / (pf("bwd_dq_ds") * 1e-3) / 1e12, 2)
-                    item["dq_ds_gbs"] = round(2 * rx.nnz / (pf("bwd_dq_ds") * 1e-3) / 1e9, 1)
+                item["dkdv_kernel_tflops"] = _tflops(8 * wx.head_dim * rx.nnz, sx["bwd"][0])
+                if rx.dq_path():
+                    item["dq_ds_kernel_tflops"] = _tflops(2 * wx.head_dim * rx.nnz, sx["bwd_dq_ds"][0])
+                    item["dq_ds_gbs"] = round(2 * rx.nnz / (sx["bwd_dq_ds"][0] * 1e-3) / 1e9, 1)
                 else:
-                    item["dq_kernel_tflops"] = round(6 * wx.head_dim * rx.nnz / (pf("bwd_dq") * 1e-3) / 1e12, 2)
-                bwd_x = sum(pf(s_) for s_ in ("bwd_pre", "bwd_plan", "bwd", "bwd_dq", "bwd_dq_ds"))
-                item["bwd_tflops"] = round(b / (bwd_x * 1e-3) / 1e12, 2)
+                    item["dq_kernel_tflops"] = _tflops(6 * wx.head_dim * rx.nnz, sx["bwd_dq"][0])
+                _, bwd_x = split_ms(sx, True)
+                item["bwd_tflops"] = _tflops(b, bwd_x)
             if wx.global_vectors is not None:
-                item["localize_ms"] = round(pf("localize"), 4)
-                item["transfer_set_ms"] = round(pf("transfer"), 4)
+                item["localize_ms"] = round(sx["localize"][0], 4)
+                item["transfer_set_ms"] = round(sx["transfer"][0], 4)
                 item["kv_tiles_needed"] = f"{rx.kv_tiles[0]} of {rx.kv_tiles[1]} ({rx.transfer_bk}-key tiles)"
                 item["cp_plan"] = rx.cp_plan
             sweep.append(item)
@@ -399,11 +497,12 @@ def main():
             log(f"[bench] seed spread {w.name} seed {sd}")
             wx = SC.build(w.name, sd)
             rx = Runner(fm, wx, torch, store_ds)
-            msx, _ = time_steps(rx, 5, 2, torch)
+            tx = time_steps(rx, SW_STEPS, SW_WARM, torch, SW_MIN_MS)
             a, b = rx.flops()
             spread.append({"seed": sd, "nnz": rx.nnz,
                            "density": round(rx.nnz / (wx.batch * wx.heads * wx.seq_q * wx.seq_k), 5),
-                           "ms_per_step": round(msx, 4), "tflops": round((a + b) / (msx * 1e-3) / 1e12, 2)})
+                           "ms_per_step": round(tx["mean"], 4), "timing": _timing(tx),
+                           "tflops": _tflops(a + b, tx["mean"])})
             del rx
             torch.cuda.empty_cache()
         out["seed_spread"] = spread
@@ -411,16 +510,16 @@ def main():
         # forward kernel of the same workload
         fp8 = []
         bf16_fwd = {it["workload"]: it.get("fwd_kernel_tflops") for it in sweep}
-        bf16_fwd[w.name] = round(f_fwd / (per("fwd") * 1e-3) / 1e12, 2)
+        bf16_fwd[w.name] = _tflops(f_fwd, st["fwd"][0])
         for name in ("c3b_prefix_lm_32k", "c4_causal_128k", "c4_doc_causal_128k"):
             log(f"[bench] fp8 forward {name}")
             wx = SC.build(name, args.seed, tensors=False)
             rx = Fp8Runner(fm, wx, torch, args.seed)
-            msx, st = time_steps(rx, 5, 2, torch)
-            pf = lambda s: st[s][0] / 5
-            kt = 4 * wx.head_dim * rx.nnz / (pf("fwd") * 1e-3) / 1e12
-            fp8.append({"workload": name, "nnz": rx.nnz, "ms_per_call": round(msx, 4),
-                        "fwd_kernel_ms": round(pf("fwd"), 4), "v_transpose_ms": round(pf("v_transpose"), 4),
+            tx = time_steps(rx, SW_STEPS, SW_WARM, torch, SW_MIN_MS)
+            sx = stage_times(rx, ST_STEPS, torch)
+            kt = 4 * wx.head_dim * rx.nnz / (sx["fwd"][0] * 1e-3) / 1e12
+            fp8.append({"workload": name, "nnz": rx.nnz, "ms_per_call": round(tx["mean"], 4), "timing": _timing(tx),
+                        "fwd_kernel_ms": round(sx["fwd"][0], 4), "v_transpose_ms": round(sx["v_transpose"][0], 4),
                         "fwd_kernel_tflops": round(kt, 2), "frac_of_fp8_peak": round(kt / PEAK_FP8_TFLOPS, 4),
                         "bf16_fwd_kernel_tflops": bf16_fwd.get(name)})
             del rx

@@ -34,7 +34,8 @@
  *     "host" pointers are read before the call returns. The caller owns every
  *     buffer. The library never allocates device memory.
  *   - Every kernel is launched asynchronously on `stream` (NULL = the null
- *     stream); no call synchronises the host.
+ *     stream); no call synchronises the host, except the three that say so
+ *     (fm_bwd_workspace_size_ds, fm_bwd_dq_path, fm_profile_end).
  *   - A status other than FM_OK means nothing was launched, except
  *     FM_ERR_HIP, which reports a HIP error raised by a launch. The message
  *     of the last failure on the calling thread is fm_last_error().
@@ -218,6 +219,17 @@ fm_status fm_attn_bwd(const fm_problem* problem, const void* q, const void* k, c
                       const void* o, const float* lse, const void* dout, const fm_mask* mask,
                       void* dq, void* dk, void* dv,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Which dQ path the last fm_attn_bwd call with this problem, mask and
+ * workspace took (pages silent; a query of this library's own choice
+ * between the two exact dQ kernels above). *stored_ds receives 1 when dQ
+ * came from the stored dS tiles and 0 when it was recomputed. A workspace
+ * smaller than the slot map always gives 0 without touching the device;
+ * otherwise the flag the plan kernel wrote into the workspace is copied to
+ * the host after waiting for `stream`. Call it after fm_attn_bwd on the same
+ * stream, before the workspace is reused. */
+fm_status fm_bwd_dq_path(const fm_problem* problem, const fm_mask* mask, const void* workspace,
+                         size_t workspace_bytes, hipStream_t stream, int32_t* stored_ds);
 
 /* Mask localization for one context-parallel rank (FlashMask-3 page,
  * contributions paragraph: clip, shift, max on the bound vectors, no

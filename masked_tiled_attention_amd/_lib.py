@@ -21,7 +21,7 @@ STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_INVALID_ARGUMENT", 2: "FM_ERR_UNSUPPORTED
                 3: "FM_ERR_WORKSPACE", 4: "FM_ERR_HIP"}
 
 # Every symbol the header declares (checked by the CPU test-suite).
-EXPORTS = ("fm_kernel_tile", "fm_workspace_size", "fm_bwd_workspace_size_ds", "fm_tile_classify",
+EXPORTS = ("fm_kernel_tile", "fm_workspace_size", "fm_bwd_workspace_size_ds", "fm_bwd_dq_path", "fm_tile_classify",
            "fm_attn_fwd", "fm_attn_fwd_fp8", "fm_attn_bwd", "fm_mask_localize", "fm_kv_transfer_set", "fm_chunk_work", "fm_cp_plan",
            "fm_profile_begin",
            "fm_profile_end", "fm_last_error")
@@ -68,6 +68,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.fm_workspace_size.argtypes = [P(fm_problem), P(fm_mask), i32, P(sz)]
     lib.fm_bwd_workspace_size_ds.restype = C.c_int
     lib.fm_bwd_workspace_size_ds.argtypes = [P(fm_problem), P(fm_mask), vp, sz, vp, P(sz)]
+    lib.fm_bwd_dq_path.restype = C.c_int
+    lib.fm_bwd_dq_path.argtypes = [P(fm_problem), P(fm_mask), vp, sz, vp, P(i32)]
     lib.fm_tile_classify.restype = C.c_int
     lib.fm_tile_classify.argtypes = [P(fm_mask), i32, i32, i32, i32, i32, vp, vp, vp]
     lib.fm_attn_fwd.restype = C.c_int

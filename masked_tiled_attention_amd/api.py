@@ -73,10 +73,15 @@ class Mask:
                          ref.shape[0], ref.shape[1], ref.stride(0), ref.stride(1))
 
 
-def _stream(stream) -> int:
+def _stream_obj(stream, device=None):
+    """The torch stream the kernels go on: the current stream of `device` when
+    `stream` is None, a torch stream as given, or a raw hipStream_t handle
+    wrapped as an external stream."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
 
 
 def _check_bshd(t: torch.Tensor, name: str):
@@ -88,9 +93,16 @@ def _check_bshd(t: torch.Tensor, name: str):
         raise ValueError(f"{name}: head dimension must be contiguous")
 
 
+def _same_device(ref: torch.Tensor, *named):
+    for t, n in named:
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{n} is on {t.device}, q on {ref.device}")
+
+
 def _problem(q, k, v, o, scale) -> L.fm_problem:
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _check_bshd(t, n)
+    _same_device(q, (k, "k"), (v, "v"), (o, "o"))
     if q.dtype not in _DTYPES or any(t.dtype != q.dtype for t in (k, v, o)):
         raise ValueError("q, k, v, o must share dtype bfloat16 or float32")
     B, Sq, H, D = q.shape
@@ -118,6 +130,7 @@ def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
 def _problem_fp8(q, k, v, o, scale) -> L.fm_problem:
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
         _check_bshd(t, n)
+    _same_device(q, (k, "k"), (v, "v"), (o, "o"))
     if o.dtype != torch.bfloat16:
         raise ValueError("o must be bfloat16")
     B, Sq, H, D = q.shape
@@ -138,24 +151,27 @@ def fm_attn_fwd_fp8(q, k, v, descale, mask: "Mask", scale=None, o=None, lse=None
     o in bfloat16."""
     q, k, v = _codes(q, "q"), _codes(k, "k"), _codes(v, "v")
     B, Sq, H, D = q.shape
-    if o is None:
-        o = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q.device)
-    if lse is None:
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq):
-        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
-    ds = [float(x) for x in descale]
-    if len(ds) != 3:
-        raise ValueError("descale must hold 3 factors (q, k, v)")
-    prob = _problem_fp8(q, k, v, o, scale)
-    m = mask._c()
-    lib = L.load()
-    n = C.c_size_t()
-    L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 0, C.byref(n)))
-    ws = _workspace(n.value, q.device, workspace)
-    dsc = (C.c_float * 3)(*ds)
-    L.check(lib.fm_attn_fwd_fp8(C.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), dsc, C.byref(m),
-                                o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    s = _stream_obj(stream, q.device)
+    with torch.cuda.stream(s):
+        if o is None:
+            o = torch.empty((B, Sq, H, D), dtype=torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq):
+            raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+        _same_device(q, (lse, "lse"))
+        ds = [float(x) for x in descale]
+        if len(ds) != 3:
+            raise ValueError("descale must hold 3 factors (q, k, v)")
+        prob = _problem_fp8(q, k, v, o, scale)
+        m = mask._c()
+        lib = L.load()
+        n = C.c_size_t()
+        L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 0, C.byref(n)))
+        ws, nws = _workspace(n.value, q.device, workspace)
+        dsc = (C.c_float * 3)(*ds)
+        L.check(lib.fm_attn_fwd_fp8(C.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), dsc, C.byref(m),
+                                    o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nws, s.cuda_stream))
     return o, lse
 
 
@@ -196,17 +212,41 @@ def fm_bwd_workspace_size_ds(q, k, v, mask: Mask, scale=None, stream=None) -> in
     lib = L.load()
     n = C.c_size_t()
     L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 1, C.byref(n)))
-    tmp = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q.device)
-    out = C.c_size_t()
-    L.check(lib.fm_bwd_workspace_size_ds(C.byref(prob), C.byref(m), tmp.data_ptr(), tmp.numel(),
-                                         _stream(stream), C.byref(out)))
+    s = _stream_obj(stream, q.device)
+    with torch.cuda.stream(s):
+        tmp = torch.empty(max(n.value, 256), dtype=torch.uint8, device=q.device)
+        out = C.c_size_t()
+        L.check(lib.fm_bwd_workspace_size_ds(C.byref(prob), C.byref(m), tmp.data_ptr(), tmp.numel(),
+                                             s.cuda_stream, C.byref(out)))
     return out.value
 
 
+def fm_bwd_dq_path(q, k, v, mask: Mask, workspace, scale=None, stream=None) -> bool:
+    """True when the last fm_attn_bwd with these shapes, mask and workspace
+    formed dQ from stored dS tiles, False when it recomputed S and dP (waits
+    for the stream)."""
+    prob = _problem(q, k, v, q, scale)
+    m = mask._c()
+    ws, nws = _workspace(0, q.device, workspace)
+    flag = C.c_int32()
+    L.check(L.load().fm_bwd_dq_path(C.byref(prob), C.byref(m), ws.data_ptr(), nws,
+                                    _stream_obj(stream, q.device).cuda_stream, C.byref(flag)))
+    return bool(flag.value)
+
+
 def _workspace(nbytes: int, device, workspace):
-    if workspace is not None:
-        return workspace
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    """(tensor, byte count) of the workspace: the caller's (a contiguous
+    device tensor on `device`, any dtype; its whole storage counts) or a new
+    uint8 one. Call it with the launch stream current, so that a temporary
+    workspace is recycled only by work ordered after the launch."""
+    if workspace is None:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return ws, ws.numel()
+    if not workspace.is_cuda or workspace.device != torch.device(device):
+        raise ValueError(f"workspace must be a device tensor on {device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace, workspace.numel() * workspace.element_size()
 
 
 def fm_tile_classify(mask: Mask, seq_q: int, seq_k: int, block_q: int, block_k: int,
@@ -217,32 +257,37 @@ def fm_tile_classify(mask: Mask, seq_q: int, seq_k: int, block_q: int, block_k: 
     bm, hm = m.batch, m.heads
     tq, tk = -(-seq_q // block_q), -(-seq_k // block_k)
     dev = mask.first().device
-    summary = torch.empty((bm, hm, tk, 8), dtype=torch.int32, device=dev)
-    shape = (bm, hm, tk, tq) if transposed else (bm, hm, tq, tk)
-    classes = torch.empty(shape, dtype=torch.uint8, device=dev)
-    L.check(L.load().fm_tile_classify(C.byref(m), int(seq_q), int(seq_k), int(block_q), int(block_k),
-                                      int(bool(transposed)), summary.data_ptr(), classes.data_ptr(),
-                                      _stream(stream)))
+    s = _stream_obj(stream, dev)
+    with torch.cuda.stream(s):
+        summary = torch.empty((bm, hm, tk, 8), dtype=torch.int32, device=dev)
+        shape = (bm, hm, tk, tq) if transposed else (bm, hm, tq, tk)
+        classes = torch.empty(shape, dtype=torch.uint8, device=dev)
+        L.check(L.load().fm_tile_classify(C.byref(m), int(seq_q), int(seq_k), int(block_q), int(block_k),
+                                          int(bool(transposed)), summary.data_ptr(), classes.data_ptr(),
+                                          s.cuda_stream))
     return summary, classes
 
 
 def fm_attn_fwd(q, k, v, mask: Mask, scale=None, o=None, lse=None, workspace=None, stream=None):
     """Masked attention forward. Returns (o, lse)."""
-    if o is None:
-        o = torch.empty_like(q)
-    B, Sq, H, _ = q.shape
-    if lse is None:
-        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq):
-        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
-    prob = _problem(q, k, v, o, scale)
-    m = mask._c()
-    lib = L.load()
-    n = C.c_size_t()
-    L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 0, C.byref(n)))
-    ws = _workspace(n.value, q.device, workspace)
-    L.check(lib.fm_attn_fwd(C.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), C.byref(m),
-                            o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    s = _stream_obj(stream, q.device)
+    with torch.cuda.stream(s):
+        if o is None:
+            o = torch.empty_like(q)
+        B, Sq, H, _ = q.shape
+        if lse is None:
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq):
+            raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+        _same_device(q, (lse, "lse"))
+        prob = _problem(q, k, v, o, scale)
+        m = mask._c()
+        lib = L.load()
+        n = C.c_size_t()
+        L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 0, C.byref(n)))
+        ws, nws = _workspace(n.value, q.device, workspace)
+        L.check(lib.fm_attn_fwd(C.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), C.byref(m),
+                                o.data_ptr(), lse.data_ptr(), ws.data_ptr(), nws, s.cuda_stream))
     return o, lse
 
 
@@ -256,20 +301,23 @@ def fm_attn_bwd(q, k, v, o, lse, do, mask: Mask, scale=None, dq=None, dk=None, d
     B, Sq, H, _ = q.shape
     if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq):
         raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    for g, ref, nm in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
-        if g.shape != ref.shape or g.stride() != ref.stride() or g.dtype != ref.dtype:
-            raise ValueError(f"{nm} must match its primal in shape, strides and dtype")
-    m = mask._c()
-    lib = L.load()
-    n = C.c_size_t()
-    L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 1, C.byref(n)))
-    ws = _workspace(n.value, q.device, workspace)
-    L.check(lib.fm_attn_bwd(C.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            lse.data_ptr(), do.data_ptr(), C.byref(m), dq.data_ptr(), dk.data_ptr(),
-                            dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    s = _stream_obj(stream, q.device)
+    with torch.cuda.stream(s):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        for g, ref, nm in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+            if g.shape != ref.shape or g.stride() != ref.stride() or g.dtype != ref.dtype:
+                raise ValueError(f"{nm} must match its primal in shape, strides and dtype")
+        _same_device(q, (do, "do"), (lse, "lse"), (dq, "dq"), (dk, "dk"), (dv, "dv"))
+        m = mask._c()
+        lib = L.load()
+        n = C.c_size_t()
+        L.check(lib.fm_workspace_size(C.byref(prob), C.byref(m), 1, C.byref(n)))
+        ws, nws = _workspace(n.value, q.device, workspace)
+        L.check(lib.fm_attn_bwd(C.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), do.data_ptr(), C.byref(m), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), ws.data_ptr(), nws, s.cuda_stream))
     return dq, dk, dv
 
 
@@ -287,11 +335,13 @@ def fm_mask_localize(mask: Mask, seq_q_global: int, chunk_start, chunk_len, stre
     nck = len(starts)
     cs = (C.c_int32 * max(nck, 1))(*starts)
     cl = (C.c_int32 * max(nck, 1))(*lens)
-    out = [None if (i < 2 and mask.lts is None) or (i >= 2 and mask.uts is None)
-           else torch.empty((bm, hm, sk), dtype=torch.int32, device=ref.device) for i in range(4)]
-    ptrs = (C.c_void_p * 4)(*[None if t is None else t.data_ptr() for t in out])
-    L.check(L.load().fm_mask_localize(C.byref(m), int(sk), int(seq_q_global), cs, cl, nck, ptrs,
-                                      _stream(stream)))
+    s = _stream_obj(stream, ref.device)
+    with torch.cuda.stream(s):
+        out = [None if (i < 2 and mask.lts is None) or (i >= 2 and mask.uts is None)
+               else torch.empty((bm, hm, sk), dtype=torch.int32, device=ref.device) for i in range(4)]
+        ptrs = (C.c_void_p * 4)(*[None if t is None else t.data_ptr() for t in out])
+        L.check(L.load().fm_mask_localize(C.byref(m), int(sk), int(seq_q_global), cs, cl, nck, ptrs,
+                                          s.cuda_stream))
     return Mask(*out)
 
 
@@ -308,9 +358,11 @@ def fm_chunk_work(mask: Mask, seq_q_global: int, chunk_start, chunk_len, stream=
     nck = len(starts)
     cs = (C.c_int32 * max(nck, 1))(*starts)
     cl = (C.c_int32 * max(nck, 1))(*lens)
-    work = torch.empty((bm * hm, nck), dtype=torch.int64, device=ref.device)
-    L.check(L.load().fm_chunk_work(C.byref(m), int(sk), int(seq_q_global), cs, cl, nck, work.data_ptr(),
-                                   _stream(stream)))
+    s = _stream_obj(stream, ref.device)
+    with torch.cuda.stream(s):
+        work = torch.empty((bm * hm, nck), dtype=torch.int64, device=ref.device)
+        L.check(L.load().fm_chunk_work(C.byref(m), int(sk), int(seq_q_global), cs, cl, nck, work.data_ptr(),
+                                       s.cuda_stream))
     return work
 
 
@@ -333,10 +385,12 @@ def fm_kv_transfer_set(mask: Mask, seq_q: int, block_k: int, with_count: bool = 
     ref = mask.first()
     bm, hm, sk = ref.shape
     tk = -(-int(sk) // int(block_k))
-    need = torch.empty((bm, hm, tk), dtype=torch.uint8, device=ref.device)
-    count = torch.empty((bm, hm), dtype=torch.int32, device=ref.device) if with_count else None
-    L.check(L.load().fm_kv_transfer_set(C.byref(m), int(seq_q), int(sk), int(block_k), need.data_ptr(),
-                                        None if count is None else count.data_ptr(), _stream(stream)))
+    s = _stream_obj(stream, ref.device)
+    with torch.cuda.stream(s):
+        need = torch.empty((bm, hm, tk), dtype=torch.uint8, device=ref.device)
+        count = torch.empty((bm, hm), dtype=torch.int32, device=ref.device) if with_count else None
+        L.check(L.load().fm_kv_transfer_set(C.byref(m), int(seq_q), int(sk), int(block_k), need.data_ptr(),
+                                            None if count is None else count.data_ptr(), s.cuda_stream))
     return need, count
 
 

@@ -1,8 +1,8 @@
 // C ABI of libfmattn (declared in include/fm_attn.h): argument validation,
 // workspace layout, launch sequencing and per-launch event timing.
 // Nothing here allocates device memory; every launch goes on the caller's
-// stream and no call synchronises the host (fm_profile_end and
-// fm_bwd_workspace_size_ds excepted).
+// stream and no call synchronises the host (fm_profile_end,
+// fm_bwd_workspace_size_ds and fm_bwd_dq_path excepted).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -596,6 +596,31 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
     e = run_stage(FM_STAGE_BWD_DQ_DS, stream, [&] { return fm::launch_bwd_dq_ds(a, p->head_dim, f32, stream); });
     if (e != hipSuccess) return hip_fail(e, "dQ (stored dS) launch");
   }
+  return FM_OK;
+}
+
+fm_status fm_bwd_dq_path(const fm_problem* p, const fm_mask* mask, const void* ws, size_t ws_bytes,
+                         hipStream_t stream, int32_t* stored_ds) {
+  if (!stored_ds) return fail(FM_ERR_INVALID_ARGUMENT, "stored_ds is NULL");
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  if (p->dtype == FM_FP8_E4M3) return fail(FM_ERR_UNSUPPORTED, "the backward takes bf16 or float32 inputs");
+  fm::MaskArgs mk;
+  if ((st = check_mask(mask, p->batch, p->heads, &mk)) != FM_OK) return st;
+  const Layout L = workspace_layout(p, mask, true);
+  if (!ws || reinterpret_cast<uintptr_t>(ws) % 256)
+    return fail(FM_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
+  if (ws_bytes < L.total)
+    return fail(FM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  *stored_ds = 0;
+  if (ws_bytes < L.ds) return FM_OK;   // no room for the slot map: recompute is certain
+  int32_t flag = 0;
+  const int32_t* plan = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + L.plan);
+  hipError_t e;
+  if ((e = hipMemcpyAsync(&flag, plan + 1, sizeof(flag), hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+      (e = hipStreamSynchronize(stream)) != hipSuccess)
+    return hip_fail(e, "reading the dQ path flag");
+  *stored_ds = flag != 0;
   return FM_OK;
 }
 

@@ -315,7 +315,8 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
       ccol = a.classes_t + ((int64_t)mrow * a.tk + kt) * a.tq;
       // The lane's key bounds (keys past the end are masked for every row) and
       // interval widths (0 for empty intervals): row mm is masked by [s, e) iff
-      // (uint)(mm - s) < width, exact for every int32 s, e.
+      // (uint)mm - (uint)s < width (modulo 2^32, so no signed overflow), exact
+      // for every int32 s, e.
       int32_t lte = INT_MAX, ute = 0;
       b_lts = INT_MIN;
       b_uts = 0;
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
             float p = fast_exp2(fmaf(sacc[i], C, -l2[r]));
             if constexpr (MASKED) {
               const int mm = m0 + ml + r;
-              const bool mk = ((uint32_t)(mm - b_lts) < b_lw) | ((uint32_t)(mm - b_uts) < b_uw);
+              const bool mk = ((uint32_t)mm - (uint32_t)b_lts < b_lw) | ((uint32_t)mm - (uint32_t)b_uts < b_uw);
               p = mk ? 0.f : p;
             }
             sacc[i] = p;

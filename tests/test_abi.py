@@ -126,6 +126,23 @@ def test_workspace_size_grows_with_backward():
     assert 0 < a.value < b.value
 
 
+def test_bwd_dq_path_without_room_for_stored_ds():
+    """A backward workspace of the minimum size has no room for the stored-dS
+    slot map: the query answers "recompute" from the sizes alone, without
+    touching the device; too small a workspace and a NULL result are
+    rejected."""
+    lib = L.load()
+    prob, mask = _problem(B=1, H=2, Sq=1000, Sk=1000), _mask()
+    n = C.c_size_t()
+    assert lib.fm_workspace_size(C.byref(prob), C.byref(mask), 1, C.byref(n)) == L.FM_OK
+    flag = C.c_int32(7)
+    assert lib.fm_bwd_dq_path(C.byref(prob), C.byref(mask), FAKE, n.value, None, C.byref(flag)) == L.FM_OK
+    assert flag.value == 0
+    assert lib.fm_bwd_dq_path(C.byref(prob), C.byref(mask), FAKE, n.value - 1, None,
+                              C.byref(flag)) == L.FM_ERR_WORKSPACE
+    assert lib.fm_bwd_dq_path(C.byref(prob), C.byref(mask), FAKE, n.value, None, None) == L.FM_ERR_INVALID_ARGUMENT
+
+
 @pytest.mark.parametrize("starts,lens,sq,expect", [
     ([0, 100], [200, 50], 1000, L.FM_ERR_INVALID_ARGUMENT),    # overlap
     ([500, 100], [10, 10], 1000, L.FM_ERR_INVALID_ARGUMENT),   # descending
