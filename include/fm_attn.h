@@ -184,6 +184,22 @@ fm_status fm_attn_fwd(const fm_problem* problem, const void* q, const void* k, c
                       const fm_mask* mask, void* o, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The forward (fm_attn_fwd), allocating nothing and taking no workspace:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). Inputs,
+ * outputs, layout, results and errors are those of fm_attn_fwd (bf16 or
+ * float32 problems). Its tile classes, launch order and split partials go to
+ * a scratch array of 64 MiB that the library holds on each GPU it runs on
+ * until the process ends; a problem whose forward workspace cannot fit there
+ * (even with its key-tile lists left whole) fails with FM_ERR_WORKSPACE.
+ * Every byte of scratch a kernel reads was written earlier in the same call,
+ * so nothing has to start at zero. All calls on one GPU share its scratch:
+ * calls that may overlap on one GPU (other streams, other threads) race and
+ * must be serialised by the caller. `stream` must belong to the current
+ * device. */
+fm_status fm_attn_fwd_noalloc(const fm_problem* problem, const void* q, const void* k, const void* v,
+                              const fm_mask* mask, void* o, float* lse, hipStream_t stream);
+
 /* Forward on 8-bit floating-point inputs ("Современное состояние Flash
  * Attention на ROCm", kripta.biz, paragraphs on the attention variants and
  * their ranking: the fastest variant is the FP8 forward; the page names no

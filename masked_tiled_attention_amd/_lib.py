@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "FM_OK", 1: "FM_ERR_INVALID_ARGUMENT", 2: "FM_ERR_UNSUPPORTED
 
 # Every symbol the header declares (checked by the CPU test-suite).
 EXPORTS = ("fm_kernel_tile", "fm_workspace_size", "fm_bwd_workspace_size_ds", "fm_bwd_dq_path", "fm_tile_classify",
-           "fm_attn_fwd", "fm_attn_fwd_fp8", "fm_attn_bwd", "fm_mask_localize", "fm_kv_transfer_set", "fm_chunk_work", "fm_cp_plan",
+           "fm_attn_fwd", "fm_attn_fwd_noalloc", "fm_attn_fwd_fp8", "fm_attn_bwd", "fm_mask_localize", "fm_kv_transfer_set", "fm_chunk_work", "fm_cp_plan",
            "fm_profile_begin",
            "fm_profile_end", "fm_last_error")
 
@@ -74,6 +74,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     lib.fm_tile_classify.argtypes = [P(fm_mask), i32, i32, i32, i32, i32, vp, vp, vp]
     lib.fm_attn_fwd.restype = C.c_int
     lib.fm_attn_fwd.argtypes = [P(fm_problem), vp, vp, vp, P(fm_mask), vp, vp, vp, sz, vp]
+    lib.fm_attn_fwd_noalloc.restype = C.c_int
+    lib.fm_attn_fwd_noalloc.argtypes = [P(fm_problem), vp, vp, vp, P(fm_mask), vp, vp, vp]
     lib.fm_attn_fwd_fp8.restype = C.c_int
     lib.fm_attn_fwd_fp8.argtypes = [P(fm_problem), vp, vp, vp, P(C.c_float), P(fm_mask), vp, vp, vp, sz, vp]
     lib.fm_attn_bwd.restype = C.c_int

@@ -291,6 +291,21 @@ def fm_attn_fwd(q, k, v, mask: Mask, scale=None, o=None, lse=None, workspace=Non
     return o, lse
 
 
+def fm_attn_fwd_noalloc(q, k, v, mask: Mask, o, lse, scale=None, stream=None):
+    """The forward through the entry point that allocates nothing and takes
+    no workspace (its scratch is a fixed device array of the library, shared
+    by every call on the GPU). o and lse are the caller's; returns them."""
+    B, Sq, H, _ = q.shape
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Sq):
+        raise ValueError("lse must be a contiguous float32 [B, H, Sq] tensor")
+    _same_device(q, (lse, "lse"))
+    prob = _problem(q, k, v, o, scale)
+    m = mask._c()
+    L.check(L.load().fm_attn_fwd_noalloc(C.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(), C.byref(m),
+                                         o.data_ptr(), lse.data_ptr(), _stream_obj(stream, q.device).cuda_stream))
+    return o, lse
+
+
 def fm_attn_bwd(q, k, v, o, lse, do, mask: Mask, scale=None, dq=None, dk=None, dv=None,
                 workspace=None, stream=None):
     """Masked attention backward. Returns (dq, dk, dv)."""

@@ -8,7 +8,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -58,6 +60,45 @@ hipError_t run_stage(fm_stage st, hipStream_t s, F&& launch) {
 
 fm_status hip_fail(hipError_t e, const char* what) {
   return fail(FM_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- scratch
+// Device memory of the allocation-free forward (fm_attn_fwd_noalloc): a
+// file-scope device array, one copy per GPU the library runs on, held until
+// the process ends. In host code `scratch` names a host-side stand-in, never
+// the device memory: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is used.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, which must be
+// the device of `stream` (a NULL stream is the current device's).
+fm_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FM_ERR_UNSUPPORTED, "device %d out of range", dev);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if ((e = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(FM_ERR_INVALID_ARGUMENT, "stream belongs to device %d, the current device is %d", (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % 256)
+      return fail(FM_ERR_HIP, "scratch address %p is NULL or not 256-byte aligned", ptr);
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return FM_OK;
 }
 
 // ---------------------------------------------------------------- validation
@@ -195,7 +236,8 @@ int32_t fwd_split(const fm_problem* p) {
   return ks;
 }
 
-Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
+// max_split caps the forward's list parts (1: no split partials).
+Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t max_split = 8) {
   Layout L;
   const int64_t bh = (int64_t)m->batch * m->heads;
   size_t off = 0;
@@ -245,7 +287,7 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd) {
     off = align256(off + rows);
     L.order = off;
     off = align256(off + rows);
-    L.ksplit = fwd_split(p);
+    L.ksplit = std::min(fwd_split(p), std::max(max_split, 1));
     if (L.ksplit > 1) {
       const size_t rows_all = (size_t)L.ksplit * p->batch * p->heads * p->seqlen_q;
       L.opart = off;
@@ -436,7 +478,8 @@ namespace {
 // Both forwards: validation, classification, launch order, then (FP8) the
 // V^T pre-pass and the FP8 kernel or the bf16/float32 kernel.
 fm_status fwd_common(const fm_problem* p, const void* q, const void* k, const void* v, const float* descale,
-                     const fm_mask* mask, void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+                     const fm_mask* mask, void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                     int32_t max_split = 8) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   const bool fp8 = descale != nullptr;
@@ -453,7 +496,7 @@ fm_status fwd_common(const fm_problem* p, const void* q, const void* k, const vo
   if ((st = check_ptr(q, "q")) || (st = check_ptr(k, "k")) || (st = check_ptr(v, "v")) ||
       (st = check_ptr(o, "o")) || (st = check_ptr(lse, "lse")))
     return st;
-  const Layout L = workspace_layout(p, mask, false);
+  const Layout L = workspace_layout(p, mask, false, max_split);
   if (!ws || reinterpret_cast<uintptr_t>(ws) % 256)
     return fail(FM_ERR_WORKSPACE, "workspace is NULL or not 256-byte aligned");
   if (ws_bytes < L.total)
@@ -541,6 +584,25 @@ extern "C" {
 fm_status fm_attn_fwd(const fm_problem* p, const void* q, const void* k, const void* v, const fm_mask* mask,
                       void* o, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
   return fwd_common(p, q, k, v, nullptr, mask, o, lse, ws, ws_bytes, stream);
+}
+
+fm_status fm_attn_fwd_noalloc(const fm_problem* p, const void* q, const void* k, const void* v, const fm_mask* mask,
+                              void* o, float* lse, hipStream_t stream) {
+  fm_status st = check_problem(p);
+  if (st != FM_OK) return st;
+  fm::MaskArgs mk;
+  if ((st = check_mask(mask, p->batch, p->heads, &mk)) != FM_OK) return st;
+  // as many list parts as the scratch holds (fewer parts change only the
+  // rounding order of the merge)
+  int32_t split = 8;
+  while (split > 1 && workspace_layout(p, mask, false, split).total > kScratchBytes) split /= 2;
+  const size_t need = workspace_layout(p, mask, false, split).total;
+  if (need > kScratchBytes)
+    return fail(FM_ERR_WORKSPACE, "the allocation-free forward needs %zu bytes of scratch; it holds at most %zu",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(stream, &ws)) != FM_OK) return st;
+  return fwd_common(p, q, k, v, nullptr, mask, o, lse, ws, kScratchBytes, stream, split);
 }
 
 fm_status fm_attn_fwd_fp8(const fm_problem* p, const void* q, const void* k, const void* v, const float* descale,

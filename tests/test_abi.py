@@ -126,6 +126,20 @@ def test_workspace_size_grows_with_backward():
     assert 0 < a.value < b.value
 
 
+def test_fwd_noalloc_rejects_problems_beyond_its_scratch():
+    """The allocation-free forward holds 64 MiB of scratch: 128 per-head
+    masks over 65,536 x 65,536 need a 64 MiB class map alone, so the call
+    fails with FM_ERR_WORKSPACE before touching the device."""
+    lib = L.load()
+    prob = _problem(B=1, H=128, Sq=65536, Sk=65536)
+    mask = _mask(hm=128)
+    rc = lib.fm_attn_fwd_noalloc(C.byref(prob), FAKE, FAKE, FAKE, C.byref(mask), FAKE, FAKE, None)
+    assert rc == L.FM_ERR_WORKSPACE
+    assert b"scratch" in lib.fm_last_error()
+    assert lib.fm_attn_fwd_noalloc(None, FAKE, FAKE, FAKE, C.byref(mask), FAKE, FAKE, None) == \
+        L.FM_ERR_INVALID_ARGUMENT
+
+
 def test_bwd_dq_path_without_room_for_stored_ds():
     """A backward workspace of the minimum size has no room for the stored-dS
     slot map: the query answers "recompute" from the sizes alone, without
