@@ -98,34 +98,39 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ dK / dV
 // One workgroup per (batch, K/V head, 128-key tile), eight wavefronts, two per
-// SIMD. Wavefronts w and w + 4 (one SIMD) share keys 32 (w % 4) .. + 31 of the
-// tile. For every 64-row query tile each of the two forms S and dP for its own
-// 32 rows (rows 32 (w / 4) ..) and from them P and dS; they hand each other
-// the half the other needs through LDS, and then the first accumulates dV and
-// the second dK over all 64 rows. Splitting the work this way keeps one
-// output (64 registers) per wavefront, which leaves registers for operand
-// reads issued well ahead of their matrix products. The K and V tiles stay in
-// LDS for the whole kernel; every wavefront reads its keys' rows as operands.
+// SIMD. Wavefronts w and w + 4 (one SIMD) own keys 32 (w % 4) .. + 31 of the
+// tile and split the products of every non-SKIP 64-row query tile by kind:
+//   the P wavefront (w < 4) holds its keys' K rows in registers, forms
+//     S = Q K^T and P for all 64 rows, hands the bf16 P to its partner through
+//     LDS and accumulates dV^T += dO^T P;
+//   the dS wavefront (w >= 4) holds its keys' V rows in registers and works
+//     one query tile behind: dP = dO V^T of the previous tile, dS = P (dP - D)
+//     with the P handed over one iteration earlier, dK^T += Q^T dS (and the
+//     dS tile to HBM when dQ is formed from it).
+// With K and V in registers only Q and dO are read from LDS (each once as
+// rows and once transposed per wavefront pair), and working one tile behind
+// frees the dS wavefront from waiting for its partner's exponentials, so the
+// two wavefronts of a SIMD overlap their matrix products with each other's
+// vector work. Three query tiles live in LDS: the P wavefronts' current one,
+// the dS wavefronts' previous one, and the next one loading.
 namespace kv {
 constexpr int BQ = kBwdBlockQ;   // 64 query rows per inner tile
 constexpr int BK = kBwdBlockK;   // 128 keys per workgroup
-constexpr int WAVES = 8;         // 4 key groups x 2 row halves
+constexpr int WAVES = 8;         // 4 key groups x (P, dS)
 constexpr int THREADS = WAVES * 64;
-constexpr int NBUF = 2;          // query tiles in LDS: the current one and the next
+constexpr int NBUF = 3;          // query tiles in LDS
 
 template <int D>
 struct alignas(16) Smem {
-  uint16_t k[BK * D];            // the workgroup's key tile, row-major, swizzled
-  uint16_t v[BK * D];            // its value tile
-  uint16_t q[NBUF][BQ * D];      // query tiles
+  uint16_t q[NBUF][BQ * D];      // query tiles, row-major, swizzled
   uint16_t dout[NBUF][BQ * D];   // dO tiles
   float lse2[NBUF][BQ];          // LSE * log2(e); +inf for rows that see nothing / past the end
   float dd[NBUF][BQ];            // D = rowsum(dO * O)
   uint32_t list[LIST_CAP];
   uint16_t rank[LIST_CAP];       // ascending rank of each list entry (stored-dS slot)
-  // per wavefront, 2 KiB: first its dS regrouped for the stores, then the
-  // P (second half) or dS (first half) handed to the other wavefront of its SIMD
-  uint16_t xch[WAVES][32 * 32];
+  // per key group, two buffers of 4 KiB: the bf16 P of one query tile (64 rows
+  // x 32 keys in MFMA operand order), then the dS wavefront's store staging
+  uint16_t xch[4][2][BQ * 32];
   int32_t scan[WAVES];
 };
 }  // namespace kv
@@ -139,13 +144,12 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   constexpr int KSTEPS = D / 16;
   constexpr int CB = D / 32;
   constexpr int QR = (BQ * D / 8) / THREADS;   // 16-byte chunks per thread of a float32 Q (or dO) tile
-  constexpr int KR = (BK * D / 8) / THREADS;   // ... of a float32 K (or V) tile
   __shared__ Smem<D> sm;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
-  const int kg = __builtin_amdgcn_readfirstlane(w & 3);   // key group
-  const int mb = __builtin_amdgcn_readfirstlane(w >> 2);   // row half for S, dP; 0: accumulates dV, 1: dK
+  const int kg = __builtin_amdgcn_readfirstlane(w & 3);          // key group
+  const bool is_p = __builtin_amdgcn_readfirstlane(w >> 2) == 0;  // P wavefront (else dS wavefront)
   const int l = tid & 63;
   const int lr = l & 31;
   const int g = l >> 5;
@@ -176,29 +180,17 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   const bool store_ds = a.plan != nullptr && a.plan[1] != 0;
   constexpr int ES = F32 ? 4 : 2;
 
-  // ---- K and V tiles into LDS once (keys past the end re-read the last key;
-  // the ragged tile masks them) ----
+  // ---- the lane's key row as MFMA B operands, once: K for the P wavefront,
+  // V for the dS wavefront, channels 16 s + 8 g .. + 7 in step s (keys past
+  // the end re-read the last key; their pairs are masked) ----
+  u32x4 kvf[KSTEPS];
   {
-    const int64_t k_ld = a.k_ss * ES, v_ld = a.v_ss * ES;
-    const char* kt0 = reinterpret_cast<const char*>(a.k) +
-                      ((int64_t)b * a.k_sb + (int64_t)kt * BK * a.k_ss + (int64_t)hk * a.k_sh) * ES;
-    const char* vt0 = reinterpret_cast<const char*>(a.v) +
-                      ((int64_t)b * a.v_sb + (int64_t)kt * BK * a.v_ss + (int64_t)hk * a.v_sh) * ES;
-    const int nvalid = a.seq_k - kt * BK;
-    if constexpr (F32) {
-      uint32_t off[KR];
-      u32x4 r[KR];
-      tile_offsets<D, F32, KR, THREADS>(off, k_ld, tid);
-      load_tile_rows<D, F32, KR, THREADS>(r, kt0, off, k_ld, tid, nvalid);
-      store_tile_rows<D, KR, THREADS>(reinterpret_cast<char*>(sm.k), r, tid);
-      tile_offsets<D, F32, KR, THREADS>(off, v_ld, tid);
-      load_tile_rows<D, F32, KR, THREADS>(r, vt0, off, v_ld, tid, nvalid);
-      store_tile_rows<D, KR, THREADS>(reinterpret_cast<char*>(sm.v), r, tid);
-    } else {
-      using DmaK = DmaTile<D, BK, THREADS>;
-      DmaK::load(reinterpret_cast<char*>(sm.k), kt0, DmaK::offset(k_ld, tid), k_ld, tid, nvalid);
-      DmaK::load(reinterpret_cast<char*>(sm.v), vt0, DmaK::offset(v_ld, tid), v_ld, tid, nvalid);
-    }
+    const int nn = min(n, a.seq_k - 1);
+    const int64_t off = is_p ? (int64_t)b * a.k_sb + (int64_t)nn * a.k_ss + (int64_t)hk * a.k_sh + 8 * g
+                             : (int64_t)b * a.v_sb + (int64_t)nn * a.v_ss + (int64_t)hk * a.v_sh + 8 * g;
+    const void* src = is_p ? a.k : a.v;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) kvf[s] = load8_as_bf16<F32>(src, off + 16 * s);
   }
 
   // Per query head (set at the start of each head): the lane's key bounds
@@ -210,7 +202,7 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   const uint8_t* ccol = nullptr;
   int64_t slot0 = 0, lrow = 0;
   uint16_t* ds_rep = nullptr;
-  f32x16 acc[CB];   // dV^T (first half) or dK^T (second half) of the wavefront's keys
+  f32x16 acc[CB];   // dV^T (P wavefront) or dK^T (dS wavefront) of the wavefront's keys
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
   const float C = a.scale_log2;
@@ -250,61 +242,198 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     else if (wu == 1) dma4(a.drow + lrow + m0, 4u * (uint32_t)l, lds_address(sm.dd[buf]));
   };
 
-  // Where the two wavefronts of a SIMD both want the matrix unit, the first
-  // goes first: it then runs its exponentials while the other's products run.
-  if (mb == 0) __builtin_amdgcn_s_setprio(1);
+  // Where the two wavefronts of a SIMD both want the matrix unit, the P
+  // wavefront goes first: its exponentials then overlap the other's products.
+  if (is_p) __builtin_amdgcn_s_setprio(1);
 
-  // LDS byte addresses of this lane's operand reads, computed once: tile
-  // buffer, dO-vs-Q, V-vs-K, 16-row steps and the lane-uniform row half go
+  // LDS byte offsets of this lane's operand reads within a tile, computed
+  // once; the tile's base is added per iteration, row blocks and row steps go
   // into the reads' immediate offsets (none of them changes the swizzle).
-  // S / dP step s: Q (and dO) row 32 mb + lr, K (and V) row 32 kg + lr,
-  // channels 16 s + 8 g.
-  uint32_t qo[KSTEPS], ko[KSTEPS];
+  // Row operands (Q for the P wavefront, dO for the dS wavefront) of step s:
+  // row lr (+ 32 per row block), channels 16 s + 8 g.
+  uint32_t fo[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    qo[s] = lds_address(sm.q[0]) + (uint32_t)rm_byte<D>(32 * mb + lr, 16 * s + 8 * g);
-    ko[s] = lds_address(sm.k) + (uint32_t)rm_byte<D>(32 * kg + lr, 16 * s + 8 * g);
-  }
-  // dV / dK products: transposed dO (first half) or Q (second half) rows of
-  // row block hh (0: the own half, 1: the other's), channel block cb, the two
-  // 4-row groups of tr_operand().
-  uint32_t to[2][CB][2];
+  for (int s = 0; s < KSTEPS; ++s) fo[s] = (uint32_t)rm_byte<D>(lr, 16 * s + 8 * g);
+  // Transposed operands (dO^T for the P wavefront, Q^T for the dS wavefront)
+  // of channel block cb: the two 4-row groups of tr_operand() (+ 16 rows per
+  // row step).
+  uint32_t to[CB][2];
   {
     const int i = l & 15;
-    const uint32_t tbase = mb ? lds_address(sm.q[0]) : lds_address(sm.dout[0]);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int half = hh == 0 ? mb : 1 - mb;
-        const int r0 = 32 * half + 4 * g + (i >> 2);
-        const int col = 32 * cb + 16 * ((l >> 4) & 1) + 4 * (i & 3);
-        to[hh][cb][0] = tbase + (uint32_t)rm_byte<D>(r0, col);
-        to[hh][cb][1] = tbase + (uint32_t)rm_byte<D>(r0 + 8, col);
-      }
+    for (int cb = 0; cb < CB; ++cb) {
+      const int r0 = 4 * g + (i >> 2);
+      const int col = 32 * cb + 16 * ((l >> 4) & 1) + 4 * (i & 3);
+      to[cb][0] = (uint32_t)rm_byte<D>(r0, col);
+      to[cb][1] = (uint32_t)rm_byte<D>(r0 + 8, col);
+    }
   }
   // (kept whole: otherwise the compiler splits them into shared parts and
   // adds those again in every tile)
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    asm volatile("" : "+v"(qo[s]));
-    asm volatile("" : "+v"(ko[s]));
+  for (int s = 0; s < KSTEPS; ++s) asm volatile("" : "+v"(fo[s]));
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    asm volatile("" : "+v"(to[cb][0]));
+    asm volatile("" : "+v"(to[cb][1]));
   }
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      asm volatile("" : "+v"(to[hh][cb][0]));
-      asm volatile("" : "+v"(to[hh][cb][1]));
-    }
   constexpr uint32_t QTILE = BQ * D * 2;             // bytes per Q (or dO) tile
-  constexpr uint32_t DOUT = 2 * QTILE;               // sm.dout[0] - sm.q[0]
-  constexpr uint32_t VOFF = BK * D * 2;              // sm.v - sm.k
+  constexpr uint32_t DOUT = NBUF * QTILE;            // sm.dout[0] - sm.q[0]
+  constexpr uint32_t RB = 32 * 2 * D;                // bytes of 32 tile rows
   static_assert(offsetof(Smem<D>, dout) - offsetof(Smem<D>, q) == DOUT, "tile layout");
-  static_assert(offsetof(Smem<D>, v) - offsetof(Smem<D>, k) == VOFF, "tile layout");
-  char* xmine = reinterpret_cast<char*>(sm.xch[w]);
-  const char* xpeer = reinterpret_cast<const char*>(sm.xch[w ^ 4]);
-  int it_global = 0;   // iteration count over heads and passes (selects the LDS buffer)
+  static_assert(DOUT + QTILE <= 65536, "immediate offsets");
+  const uint32_t q0 = lds_address(sm.q[0]);
+  char* xgrp = reinterpret_cast<char*>(sm.xch[kg]);
+
+  // One query tile of this wavefront's role: entry list[e] in LDS buffer
+  // buf, its P in xch[kg][par], its stored-dS slot (dS wavefront, storing).
+  // Both roles run the same products on different operands, so that the
+  // accumulators stay in place; only the vector work between the products
+  // differs by role.
+  auto work = [&](auto masked_c, int e, int buf, int par, int64_t slot) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const uint32_t tile = q0 + (uint32_t)buf * QTILE;
+    const uint32_t fbase = tile + (is_p ? 0u : DOUT);   // rows: Q (P) or dO (dS)
+    const uint32_t tbase = tile + (is_p ? DOUT : 0u);   // transposed: dO^T (P) or Q^T (dS)
+    char* xp = xgrp + par * (BQ * 32 * 2);
+
+    // S (P wavefront) or dP (dS wavefront) for the tile's 64 rows x the
+    // wavefront's 32 keys: row operands from LDS, the key operands in
+    // registers (lane = key, registers = rows). Operands read three MFMAs
+    // ahead.
+    f32x16 sp[2] = {f32x16{}, f32x16{}};
+    {
+      constexpr int NJ = 2 * KSTEPS;   // (step, row block)
+      u32x4 op[NJ];
+      auto rd = [&](int j) { op[j] = lds16(fo[j >> 1] + fbase, (j & 1) * RB); };
+#pragma unroll
+      for (int j = 0; j < 3; ++j) rd(j);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        if (j + 3 < NJ) rd(j + 3);
+        sp[j & 1] = mfma32(op[j], kvf[j >> 1], sp[j & 1]);
+      }
+      sched_lds_mfma<NJ, 1, 3>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // The transposed operands of the first three column products, read
+    // before the vector work so that it covers their latency.
+    constexpr int NS = 4 * CB;   // (row step, channel block)
+    u32x4 ta[NS];
+    auto tread = [&](int j) {
+      const int t = j / CB, cb = j % CB;
+      const u32x2 x = lds_tr16(to[cb][0] + tbase, t * 16 * 2 * D);
+      const u32x2 y = lds_tr16(to[cb][1] + tbase, t * 16 * 2 * D);
+      ta[j] = u32x4{x[0], x[1], y[0], y[1]};
+    };
+#pragma unroll
+    for (int j = 0; j < 3; ++j) tread(j);
+    __builtin_amdgcn_sched_barrier(0);
+
+    u32x4 bop[4];   // B operands of the column products, one per 16-row step
+    if (is_p) {
+      // P = exp2(S * scale * log2(e) - LSE * log2(e)), 0 on masked pairs
+      const int m0 = (int)(sm.list[e] & ~kPartialBit) * BQ;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ml = 32 * rb + 8 * q4 + 4 * g;
+          const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * q4 + r;
+            float p = fast_exp2(fmaf(sp[rb][i], C, -l2[r]));
+            if constexpr (MASKED) {
+              const uint32_t mm = (uint32_t)(m0 + ml + r);
+              const bool mk = (mm - (uint32_t)b_lts < b_lw) | (mm - (uint32_t)b_uts < b_uw);
+              p = mk ? 0.f : p;
+            }
+            sp[rb][i] = p;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bop[2 * rb + t][j] = pack_bf16(sp[rb][8 * t + 2 * j], sp[rb][8 * t + 2 * j + 1]);
+      }
+      // hand P over (lane-linear, 1 KiB per row step)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) *reinterpret_cast<u32x4*>(xp + (t * 64 + l) * 16) = bop[t];
+    } else {
+      // dS = P (dP - D), with the bf16 P the dV product used
+      u32x4 pr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) pr[t] = *reinterpret_cast<const u32x4*>(xp + (t * 64 + l) * 16);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ml = 32 * rb + 8 * q4 + 4 * g;
+          const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * q4 + r;
+            const uint32_t wd = pr[2 * rb + i / 8][(i % 8) / 2];
+            const float p = (i & 1) ? bf16_hi(wd) : bf16_lo(wd);
+            sp[rb][i] = p * (sp[rb][i] - dd[r]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bop[2 * rb + t][j] = pack_bf16(sp[rb][8 * t + 2 * j], sp[rb][8 * t + 2 * j + 1]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // dV^T += dO^T P (P wavefront) or dK^T += Q^T dS (dS wavefront) over the
+    // 64 rows; transposed operands three MFMAs ahead.
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      if (j + 3 < NS) tread(j + 3);
+      acc[j % CB] = mfma32(ta[j], bop[j / CB], acc[j % CB]);
+    }
+#pragma unroll
+    for (int j = 0; j < NS - 3; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    if (!is_p && store_ds) {   // 4 stores per lane, counted by the wait at the top of the next iteration
+      // The stored tile is 16 MFMA operand fragments of 1 KiB, fragment
+      // (rb, s) = query rows 32 rb .. 32 rb + 31 x keys 16 s .. 16 s + 15.
+      // Lane L's 16 bytes at L * 16 hold the row of fragment column
+      // c = L % 32 (row 32 rb + 16 c[3] + 8 j[2] + 4 c[4] + j[1:0] for
+      // element j's half, the order in which the accumulator holds rows) and
+      // keys 16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3 (h = L / 32), the
+      // order in which the dQ kernel's transposing K^T reads take the keys.
+      // The wavefront's 32 keys are fragments (rb, 2 kg) and (rb, 2 kg + 1).
+      // They go through the LDS buffer P came in (P is in registers now) as
+      // two row-major [key][column] tiles; transposing reads of them yield
+      // whole fragment lanes, so each non-temporal store writes one
+      // contiguous KiB. LDS accesses of one wavefront execute in order.
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<u32x4*>(xp + rb * 2048 + rm_byte<32>(lr, 8 * (2 * g + t))) = bop[2 * rb + t];
+      char* dst = reinterpret_cast<char*>(ds_rep + slot * (BK * BQ));
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int sp2 = 0; sp2 < 2; ++sp2) {
+          const int r0 = 16 * sp2 + 4 * g;
+          const u32x4 x = tr_operand<32>(xp + rb * 2048, l, 0, r0, r0 + 8);
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst + (rb * 8 + 2 * kg + sp2) * 1024 + l * 16));
+        }
+    }
+  };
+
+  int it_global = 0;   // iteration count over heads and passes (selects the LDS buffers)
   const int ngroup = GROUPED ? a.group : 1;
   for (int gi = gsel; gi < (split ? gsel + 1 : ngroup); ++gi) {
     h = hk * ngroup + gi;
@@ -346,179 +475,58 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
       const int n_list = compact_classes_split<LIST_CAP, THREADS>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list,
                                                                   sm.rank, sm.scan, tid, ragged_k, &n_full);
       if (n_list == 0) continue;
-      const int pass_base = it_global - head_base;   // this head's non-SKIP tiles in earlier passes
+      const int base = it_global;
+      const int pass_base = base - head_base;   // this head's non-SKIP tiles in earlier passes
+      stage_q((int)(sm.list[0] & ~kPartialBit), base % NBUF);
 
-      stage_q((int)(sm.list[0] & ~kPartialBit), it_global % NBUF);
-
-      // FULL tiles first, then PARTIAL ones, each with its own straight-line
-      // body (one branch-free basic block per query tile).
-      auto iteration = [&](auto masked_c, auto buf_c, int it) {
-        constexpr bool MASKED = decltype(masked_c)::value;
-        constexpr int buf = decltype(buf_c)::value;   // it_global % NBUF
-        const int qt = (int)(sm.list[it] & ~kPartialBit);
-        const int m0 = qt * BQ;
-        // This tile's loads done (and, at a pass's first tile, the K / V tiles).
+      // Iteration it: the P wavefronts take list entry it, the dS wavefronts
+      // entry it - 1. FULL entries come first, then PARTIAL ones (only the P
+      // wavefronts evaluate the mask); the first iteration has work for the P
+      // wavefronts alone and one more at the end for the dS wavefronts alone.
+      auto top = [&](int it) {
+        // This tile's loads done (and, at a pass's first tile, the key rows).
         // Younger vector-memory operations that may stay in flight: the dS
-        // stores of the previous iteration (vmcnt counts stores too).
-        if (store_ds && it > 0) wait_vmem_le<2>();
+        // wavefront's stores of the previous iteration (vmcnt counts stores).
+        if (!is_p && store_ds && it >= 2) wait_vmem_le<4>();
         else wait_vmem();
-        __syncthreads();   // tile `buf` visible to all; the buffer read last iteration is free
-        if (it + 1 < n_list) stage_q((int)(sm.list[it + 1] & ~kPartialBit), buf ^ 1);
-
-        // S = Q K^T and dP = dO V^T for the wavefront's 32 rows x 32 keys
-        // (lane = key, registers = query rows). The four operands of step s
-        // are read two steps ahead of its products (three sets in registers).
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
-        {
-          u32x4 op[3][4];
-          auto read = [&](int s, u32x4 (&o)[4]) {
-            o[0] = lds16(qo[s], buf * QTILE);
-            o[1] = lds16(ko[s]);
-            o[2] = lds16(qo[s], DOUT + buf * QTILE);
-            o[3] = lds16(ko[s], VOFF);
-          };
-          read(0, op[0]);
-          read(1, op[1]);
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) {
-            if (s + 2 < KSTEPS) read(s + 2, op[(s + 2) % 3]);
-            sacc = mfma32(op[s % 3][0], op[s % 3][1], sacc);
-            dpacc = mfma32(op[s % 3][2], op[s % 3][3], dpacc);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-          for (int s = 0; s < KSTEPS - 2; ++s) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // P = exp2(S * scale * log2(e) - LSE * log2(e)), dS = P (dP - D),
-        // both rounded to bf16 MFMA operands
-        u32x4 pp[2], dsp[2];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ml = 32 * mb + 8 * q4 + 4 * g;
-          const f32x4 l2 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][ml]);
-          const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][ml]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * q4 + r;
-            float p = fast_exp2(fmaf(sacc[i], C, -l2[r]));
-            if constexpr (MASKED) {
-              const int mm = m0 + ml + r;
-              const bool mk = ((uint32_t)mm - (uint32_t)b_lts < b_lw) | ((uint32_t)mm - (uint32_t)b_uts < b_uw);
-              p = mk ? 0.f : p;
-            }
-            sacc[i] = p;
-            dpacc[i] = p * (dpacc[i] - dd[r]);
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            pp[t][j] = pack_bf16(sacc[8 * t + 2 * j], sacc[8 * t + 2 * j + 1]);
-            dsp[t][j] = pack_bf16(dpacc[8 * t + 2 * j], dpacc[8 * t + 2 * j + 1]);
-          }
-
-        if (store_ds) {   // 2 stores per lane, counted by the wait above
-          // The stored tile is 16 MFMA operand fragments of 1 KiB, fragment
-          // (rb, s) = query rows 32 rb .. 32 rb + 31 x keys 16 s .. 16 s + 15.
-          // Lane L's 16 bytes at L * 16 hold the row of fragment column
-          // c = L % 32 (row 32 rb + 16 c[3] + 8 j[2] + 4 c[4] + j[1:0] for
-          // element j's half, the order in which the accumulator holds rows) and
-          // keys 16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3 (h = L / 32), the
-          // order in which the dQ kernel's transposing K^T reads take the keys.
-          // The wavefront's 32 keys x 32 rows are fragments (mb, 2 kg) and
-          // (mb, 2 kg + 1). They go through its own LDS block as a row-major
-          // [key][column] tile; transposing reads of it yield whole fragment
-          // lanes, so each store writes 1 KiB of consecutive bytes. LDS accesses
-          // of one wavefront execute in order; no barrier is needed.
-#pragma unroll
-          for (int t = 0; t < 2; ++t) *reinterpret_cast<u32x4*>(xmine + rm_byte<32>(lr, 8 * (2 * g + t))) = dsp[t];
-          const int64_t slot = slot0 + pass_base + sm.rank[it];
-          char* tile = reinterpret_cast<char*>(ds_rep + slot * (BK * BQ));
-#pragma unroll
-          for (int sp = 0; sp < 2; ++sp) {
-            const int r0 = 16 * sp + 4 * g;
-            const u32x4 x = tr_operand<32>(xmine, l, 0, r0, r0 + 8);
-            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(tile + (mb * 8 + 2 * kg + sp) * 1024 + l * 16));
-          }
-        }
-
-        // Hand over the half the other wavefront needs (its P to the dV
-        // wavefront, its dS to the dK wavefront), keep the own one; then
-        // dV^T += dO^T P (first half) or dK^T += Q^T dS (second half), over
-        // all 64 rows: own rows first, then the other half's. The transposed
-        // operand of step j is read three steps ahead.
-        auto products = [&](auto is_k_c) {
-          constexpr bool IS_K = decltype(is_k_c)::value;
-          u32x4 own[2], peer[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            own[t] = IS_K ? dsp[t] : pp[t];
-            *reinterpret_cast<u32x4*>(xmine + (t * 64 + l) * 16) = IS_K ? pp[t] : dsp[t];
-          }
-          __syncthreads();   // the halves handed over are visible
-#pragma unroll
-          for (int t = 0; t < 2; ++t) peer[t] = *reinterpret_cast<const u32x4*>(xpeer + (t * 64 + l) * 16);
-          constexpr int NS = 4 * CB;   // (row step, channel block) products
-          u32x4 ta[NS];
-          auto tread = [&](int j) {
-            const int hh = j / (2 * CB), t = (j / CB) & 1, cb = j % CB;
-            const uint32_t o = buf * QTILE + t * 16 * (2 * D);   // tile buffer, 16-row step
-            const u32x2 x = lds_tr16(to[hh][cb][0], o);
-            const u32x2 y = lds_tr16(to[hh][cb][1], o);
-            ta[j] = u32x4{x[0], x[1], y[0], y[1]};
-          };
-#pragma unroll
-          for (int j = 0; j < 3; ++j) tread(j);
-#pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            if (j + 3 < NS) tread(j + 3);
-            const int hh = j / (2 * CB), t = (j / CB) & 1, cb = j % CB;
-            acc[cb] = mfma32(ta[j], hh == 0 ? own[t] : peer[t], acc[cb]);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x100, 6 + 2, 0);
-#pragma unroll
-          for (int j = 0; j < NS - 3; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        };
-        if (mb) products(std::true_type{});
-        else products(std::false_type{});
+        // the tile visible to all, the P handed over last iteration too; the
+        // buffer of entry it - 2 is free
+        __syncthreads();
+        if (it + 1 < n_list) stage_q((int)(sm.list[it + 1] & ~kPartialBit), (base + it + 1) % NBUF);
       };
-      using B0 = std::integral_constant<int, 0>;
-      using B1 = std::integral_constant<int, 1>;
-      int it = 0;
-      for (; it < n_full; ++it, ++it_global) {
-        if (it_global & 1) iteration(std::false_type{}, B1{}, it);
-        else iteration(std::false_type{}, B0{}, it);
+      auto run = [&](auto masked_c, int it) {
+        const int e = is_p ? it : it - 1;
+        work(masked_c, e, (base + e) % NBUF, (base + e) & 1,
+             !is_p && store_ds ? slot0 + pass_base + sm.rank[e] : 0);
+      };
+      top(0);
+      if (is_p) {
+        if (n_full > 0) run(std::false_type{}, 0);
+        else run(std::true_type{}, 0);
       }
-      for (; it < n_list; ++it, ++it_global) {
-        if (it_global & 1) iteration(std::true_type{}, B1{}, it);
-        else iteration(std::true_type{}, B0{}, it);
+      int it = 1;
+      for (; it < n_full; ++it) {
+        top(it);
+        run(std::false_type{}, it);
       }
+      for (; it < n_list; ++it) {
+        top(it);
+        run(std::true_type{}, it);
+      }
+      top(it);
+      if (!is_p) run(std::false_type{}, it);
+      it_global += n_list;
     }
   }
-  if (mb == 0) __builtin_amdgcn_s_setprio(0);
-  // A key tile that no query tile sees skips the loop above with its K / V
-  // direct loads possibly still in flight: they must land before the
-  // workgroup ends and its LDS goes to another one.
+  if (is_p) __builtin_amdgcn_s_setprio(0);
+  // A key tile that no query tile sees skips the loop above with its key row
+  // loads possibly still in flight: they land before the workgroup ends.
   wait_vmem();
 
-  // ---- epilogue: dV = dV^T (first half), dK = scale * dK^T (second half),
+  // ---- epilogue: dV = dV^T (P wavefront), dK = scale * dK^T (dS wavefront),
   // transposed back on store ----
   if (key_ok && split) {   // float32 partials [2][B][H][Sk][D]: dK, then dV
-    const bool is_k = mb == 1;
+    const bool is_k = !is_p;
     float* out = a.part + (is_k ? 0 : (int64_t)a.batch * a.heads * a.seq_k * D) +
                  (((int64_t)b * a.heads + hk * a.group + gsel) * a.seq_k + n) * D;
     const float sc = is_k ? a.scale : 1.f;
@@ -529,7 +537,7 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
         *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * q4 + 4 * g) =
             f32x4{acc[cb][4 * q4] * sc, acc[cb][4 * q4 + 1] * sc, acc[cb][4 * q4 + 2] * sc, acc[cb][4 * q4 + 3] * sc};
   } else if (key_ok) {
-    const bool is_k = mb == 1;
+    const bool is_k = !is_p;
     const int64_t off = is_k ? (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)hk * a.k_sh
                              : (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)hk * a.v_sh;
     void* out = is_k ? a.dk : a.dv;
