@@ -319,6 +319,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-store-ds", action="store_true",
                     help="minimum backward workspace: dQ recomputes S and dP instead of reading stored dS")
+    ap.add_argument("--no-recompute", action="store_true",
+                    help="skip timing the minimum-workspace (recompute dQ) backward beside the headline")
     ap.add_argument("--fp8-forward", action="store_true",
                     help="time only the FP8 forward (E4M3 codes of the workload's shape) and print its line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -436,7 +438,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, r.vectors)
     del r
     torch.cuda.empty_cache()
-    if w.backward and store_ds:
+    if w.backward and store_ds and not args.no_recompute:
         # the same step with the minimum workspace: dQ recomputes S and dP, and
         # no intermediate matrix is kept in HBM
         log(f"[bench] {w.name} with the minimum backward workspace (recompute dQ)")
