@@ -140,7 +140,7 @@ fm_status fm_workspace_size(const fm_problem* problem, const fm_mask* mask,
 /* Bytes of workspace with which fm_attn_bwd keeps dS instead of recomputing
  * it: the dK/dV kernel writes the bf16 dS tiles it forms anyway, and dQ is the
  * product scale * dS K over the stored tiles. That is fm_workspace_size(.., 1)
- * plus a slot index per tile of the dK/dV tiling and 2 bytes per (query row,
+ * plus two slot indices per tile of the dK/dV tiling and 2 bytes per (query row,
  * key) pair of every non-SKIP tile, for every (b, h) (rows and keys padded to
  * the tile). The count depends on the mask contents, so the call classifies
  * the mask on `stream` using `workspace` (device, at least
@@ -322,7 +322,7 @@ typedef enum {
   FM_STAGE_BWD = 4,         /* dK / dV kernel */
   FM_STAGE_BWD_DQ = 5,      /* dQ kernel */
   FM_STAGE_LOCALIZE = 6,
-  FM_STAGE_BWD_PLAN = 7,    /* stored-dS slot plan (count, scan) */
+  FM_STAGE_BWD_PLAN = 7,    /* stored-dS slot plan (count, scan, slots, query-major copy) */
   FM_STAGE_BWD_DQ_DS = 8,   /* dQ from stored dS */
   FM_STAGE_ORDER = 9,       /* launch orders, longest tiles first (count, sort) */
   FM_STAGE_TRANSFER = 10,   /* mask-pruned K/V transfer set */

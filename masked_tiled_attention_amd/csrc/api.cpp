@@ -181,11 +181,12 @@ fm_status check_ptr(const void* ptr, const char* name) {
 // LSE * log2(e) and D [B][H][Sp] float32 (Sp = Sq rounded up to 128, the
 // padding rows neutral) and the stored-dS plan counters. total is the
 // minimum. Beyond it, the backward may place the stored-dS slot map
-// [Bm*Hm][Tk][Tq] int32 at `slots` and the dS tiles from `ds` on.
+// [Bm*Hm][Tk][Tq] int32 at `slots`, its query-major copy [Bm*Hm][Tq][Tk] at
+// `slots_q` and the dS tiles from `ds` on.
 // 256-byte aligned sections.
 struct Layout {
   size_t summary = 0, map = 0, summary_q = 0, map_q = 0, lse2 = 0, drow = 0;
-  size_t row_cnt = 0, row_off = 0, plan = 0, total = 0, slots = 0, ds = 0;
+  size_t row_cnt = 0, row_off = 0, plan = 0, total = 0, slots = 0, slots_q = 0, ds = 0;
   size_t counts = 0, order = 0;   // forward launch order
   size_t vt = 0;                   // FP8 forward: V^T tiles [B][H_kv][Tk][8 KiB]
   size_t order_k = 0, order_qq = 0;   // backward launch orders (counts, then order)
@@ -279,7 +280,8 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t
       off = align256(off + (size_t)p->batch * p->heads * p->seqlen_k * p->head_dim * 4 * 2);
     }
     L.slots = off;
-    L.ds = align256(off + (size_t)(mrows * tk * tq * 4));
+    L.slots_q = align256(L.slots + (size_t)(mrows * tk * tq * 4));
+    L.ds = align256(L.slots_q + (size_t)(mrows * tq * tk * 4));
   } else {
     add_tiling(fm::kFwdBlockQ, fm::kFwdBlockK, &L.summary, &L.map);
     const size_t rows = (size_t)(bh * ceil_div(p->seqlen_q, fm::kFwdBlockQ)) * 4;
@@ -638,6 +640,7 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   const bool maybe_ds = ws_bytes >= L.ds;
   if (maybe_ds) {
     a.slots = reinterpret_cast<int32_t*>(w + L.slots);
+    a.slots_q = reinterpret_cast<int32_t*>(w + L.slots_q);
     a.ds = reinterpret_cast<uint16_t*>(w + L.ds);
     a.ds_capacity = (int64_t)(ws_bytes - L.ds);
     hipError_t e = run_stage(FM_STAGE_BWD_PLAN, stream, [&] { return fm::launch_bwd_plan(a, true, stream); });

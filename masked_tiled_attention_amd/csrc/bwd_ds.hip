@@ -13,12 +13,14 @@
 //   plan_count  non-SKIP tiles per key-tile row of the dK/dV class map;
 //   plan_scan   one workgroup: exclusive prefix sums (slot offsets), the total
 //               and whether the workspace holds every tile for every (b, h);
+//   plan_slots  each non-SKIP tile's slot (the dK/dV kernel's store address);
+//   plan_transpose  the slot map query-major, -1 for SKIP tiles (the dQ
+//               kernel's key-tile lists);
 //   dq_ds       one workgroup per (b, h, pair of 64-row query tiles), or per
 //               part of the pair's list when few pairs have long key ranges:
-//               for each key tile non-SKIP for either, K and the pair's stored
-//               dS tiles go straight into LDS (one stage; two workgroups per
-//               CU) and
-//               dQ^T += K^T dS^T accumulates in registers;
+//               for each key tile non-SKIP for either, K goes into LDS and
+//               each wavefront's stored dS fragments straight into registers,
+//               and dQ^T += K^T dS^T accumulates in registers;
 //   dq_merge    split lists: dQ = the sum of the parts' float32 partials.
 #include <climits>
 #include <cmath>
@@ -84,6 +86,32 @@ __global__ __launch_bounds__(256) void plan_slots_kernel(BwdArgs a) {
   }
 }
 
+// grid (tk / 64, tq / 64, mask rows): slots_q[mr][qt][kt] = slots[mr][kt][qt]
+// for non-SKIP tiles, -1 for SKIP ones; 64 x 64 blocks through LDS, so that
+// both the reads and the writes are row-contiguous. The dQ kernel reads its
+// query tiles' rows of this copy.
+__global__ __launch_bounds__(256) void plan_transpose_kernel(BwdArgs a) {
+  __shared__ int32_t t[64][65];
+  const int kt0 = blockIdx.x * 64, q0 = blockIdx.y * 64, mr = blockIdx.z;
+  const int r = threadIdx.x >> 6, c = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int kt = kt0 + r + 4 * j, q = q0 + c;
+    int32_t v = -1;
+    if (kt < a.tk && q < a.tq) {
+      const int64_t o = ((int64_t)mr * a.tk + kt) * a.tq + q;
+      if (a.classes_t[o] != FM_TILE_SKIP) v = a.slots[o];
+    }
+    t[r + 4 * j][c] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int q = q0 + r + 4 * j, kt = kt0 + c;
+    if (q < a.tq && kt < a.tk) a.slots_q[((int64_t)mr * a.tq + q) * a.tk + kt] = t[c][r + 4 * j];
+  }
+}
+
 // One workgroup of 1024: row_off = exclusive prefix sums of row_cnt over the
 // nrows = mask rows * tk rows in order, plan[0] = total, plan[1] = 1 when
 // rep * total tiles fit into ds_capacity bytes (and slots fit in int32).
@@ -124,43 +152,40 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(BwdArgs a, int32_t nrow
 }
 
 // ------------------------------------------------------------------ dQ from dS
-// One workgroup per (b, h, pair of adjacent 64-row query tiles). It walks the
-// key tiles that are non-SKIP for either query tile of the pair; each K tile
-// staged in LDS serves the stored dS tiles of both (two thirds of the bytes
-// staged per tile of work, against one K tile per dS tile).
+// One workgroup per (b, h, pair of adjacent 64-row query tiles): four
+// wavefronts, wavefront w owning rows 32 w .. 32 w + 31 of the pair (query tile
+// w / 2) and all channels. It walks the key tiles that are non-SKIP for either
+// query tile of the pair. A stored dS tile is a set of MFMA operand fragments,
+// and each fragment is used by exactly one wavefront, so the wavefronts load
+// their fragments straight into registers, two key tiles ahead; only the K
+// tile, which all four use, is staged in LDS (two buffers).
 constexpr int PAIR = 2;   // query tiles per workgroup
-// One staged key tile per workgroup (K and the pair's dS tiles, 76 KiB with the
-// lists), so that two workgroups share a CU: one's loads overlap the other's
-// products (1.22 ms at 128K, against 1.34 with two stages and one workgroup
-// per CU).
-constexpr int NSTAGE = 1;
+constexpr int DS_FRAGS = BK / 16;   // dS fragments per wavefront and key tile
 
 template <int D>
 struct alignas(16) DsSmem {
-  uint16_t k[NSTAGE][BK * D];          // key tiles, row-major, swizzled
-  uint16_t ds[NSTAGE][PAIR][BK * BQ];  // dS tiles as stored: 16 MFMA operand fragments of 1 KiB
-  uint32_t list[LIST_CAP];             // key tiles of the pair's list
-  int32_t slot[LIST_CAP][PAIR];        // stored-dS slot per query tile of the pair; -1: SKIP
+  uint16_t k[2][BK * D];       // key tiles, row-major, swizzled
+  uint32_t list[LIST_CAP];     // key tiles of the pair's list
+  int32_t slot[LIST_CAP][PAIR];   // stored-dS slot per query tile of the pair; -1: SKIP
   int32_t scan[NW];
 };
 
-// The pair's key-tile list: ascending key tiles that are non-SKIP for query
-// tile qt0 or qt0 + 1 (the latter only when has1), with both slots. Starts and
-// ends with a barrier.
-__device__ __forceinline__ int compact_pair(const uint8_t* ccol, const int32_t* scol, int64_t stride, int first,
-                                            int count, bool has1, uint32_t* sm_list, int32_t (*sm_slot)[PAIR],
-                                            int32_t* sm_scan, int tid) {
+// The pair's key-tile list: ascending key tiles in [first, first + count)
+// that are non-SKIP for either query tile of the pair, with both slots, read
+// from the two query tiles' rows of the query-major slot map (row1 == nullptr
+// when the pair has one query tile). Starts and ends with a barrier.
+__device__ __forceinline__ int compact_pair(const int32_t* row0, const int32_t* row1, int first, int count,
+                                            uint32_t* sm_list, int32_t (*sm_slot)[PAIR], int32_t* sm_scan, int tid) {
   constexpr int PER = LIST_CAP / NT;
   const int lane = tid & 63, wave = tid >> 6;
-  bool on[PER][PAIR];
+  int32_t sl[PER][PAIR];
   int cnt = 0;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int idx = tid * PER + e;
-    const int64_t o = (int64_t)(first + idx) * stride;
-    on[e][0] = idx < count && ccol[o] != FM_TILE_SKIP;
-    on[e][1] = idx < count && has1 && ccol[o + 1] != FM_TILE_SKIP;
-    cnt += on[e][0] || on[e][1];
+    sl[e][0] = idx < count ? row0[first + idx] : -1;
+    sl[e][1] = idx < count && row1 ? row1[first + idx] : -1;
+    cnt += sl[e][0] >= 0 || sl[e][1] >= 0;
   }
   int incl = cnt;
 #pragma unroll
@@ -179,12 +204,10 @@ __device__ __forceinline__ int compact_pair(const uint8_t* ccol, const int32_t* 
   }
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    if (on[e][0] || on[e][1]) {
-      const int kt = first + tid * PER + e;
-      const int64_t o = (int64_t)kt * stride;
-      sm_list[pos] = (uint32_t)kt;
-      sm_slot[pos][0] = on[e][0] ? scol[o] : -1;
-      sm_slot[pos][1] = on[e][1] ? scol[o + 1] : -1;
+    if (sl[e][0] >= 0 || sl[e][1] >= 0) {
+      sm_list[pos] = (uint32_t)(first + tid * PER + e);
+      sm_slot[pos][0] = sl[e][0];
+      sm_slot[pos][1] = sl[e][1];
       ++pos;
     }
   }
@@ -193,20 +216,20 @@ __device__ __forceinline__ int compact_pair(const uint8_t* ccol, const int32_t* 
 }
 
 template <int D, bool F32>
-__global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_ds_kernel(BwdArgs a) {
   if (a.plan == nullptr || a.plan[1] == 0) return;   // dQ comes from the recompute kernel
   constexpr int CB = D / 32;              // 32-channel blocks of dQ^T
-  constexpr int RB = 2 * PAIR;            // 32-row blocks of the pair
-  constexpr int BLK = CB * RB / NW;       // (channel block, row block) pairs per wavefront
   constexpr int KR = (BK * D / 8) / NT;   // 16-byte chunks per thread of a float32 key tile
   constexpr int ES = F32 ? 4 : 2;
   __shared__ DsSmem<D> sm;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63;
-  const int lr = l & 31;
   const int g = l >> 5;
+  const int q = w >> 1;        // this wavefront's query tile within the pair
+  const int half = w & 1;      // its 32-row half of that tile
 
   // Later query tiles first, heads interleaved: neighbouring workgroups work
   // on nearby rows and share K tiles in L2 (this kernel is bound by memory
@@ -226,24 +249,20 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   const int mrow = (a.mask.bm > 1 ? b : 0) * a.mask.hm + (a.mask.hm > 1 ? h : 0);
   const int rep_i = (a.mask.bm > 1 ? 0 : b) * (a.mask.hm > 1 ? 1 : a.heads) + (a.mask.hm > 1 ? 0 : h);
   const int64_t total = __builtin_amdgcn_readfirstlane(a.plan[0]);   // uniform
-  const uint16_t* ds_rep = a.ds + (int64_t)rep_i * total * (BK * BQ);
-  const uint8_t* ccol = a.classes_t + (int64_t)mrow * a.tk * a.tq + qt0;   // stride tq over kt
-  const int32_t* scol = a.slots + (int64_t)mrow * a.tk * a.tq + qt0;
+  // this wavefront's fragments of a stored tile start here (bytes)
+  const char* ds_rep = reinterpret_cast<const char*>(a.ds + (int64_t)rep_i * total * (BK * BQ)) +
+                       half * (DS_FRAGS * 1024) + l * 16;
+  const int32_t* srow0 = a.slots_q + ((int64_t)mrow * a.tq + qt0) * a.tk;
+  const int32_t* srow1 = has1 ? srow0 + a.tk : nullptr;
 
-  // This wavefront's channel block and row blocks (row block rb: query tile
-  // rb / 2 of the pair, rows 32 (rb % 2) ..). For d = 128 a wavefront owns one
-  // channel block and all four row blocks; for d = 64 one channel block and
-  // one row block of each query tile.
-  const int cbw = CB == 4 ? w : (w & 1);
-  auto rb_of = [&](int j) { return CB == 4 ? j : (w >> 1) + 2 * j; };
-  f32x16 acc[BLK];
+  f32x16 acc[CB];
 #pragma unroll
-  for (int j = 0; j < BLK; ++j) acc[j] = f32x16{};
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
 
-  // ---- staging: K (bf16: direct loads; float32: through registers) and the
-  // present dS tiles ----
+  // ---- K staging (bf16: direct loads; float32: through registers) ----
   const int64_t k_ld = a.k_ss * ES;
-  const char* kbh = reinterpret_cast<const char*>(a.k) + ((int64_t)b * a.k_sb + (int64_t)__builtin_amdgcn_readfirstlane(h / a.group) * a.k_sh) * ES;
+  const char* kbh = reinterpret_cast<const char*>(a.k) +
+                    ((int64_t)b * a.k_sb + (int64_t)__builtin_amdgcn_readfirstlane(h / a.group) * a.k_sh) * ES;
   using DmaK = DmaTile<D, BK, NT>;
   constexpr int NOFF = F32 ? KR : 1;
   uint32_t koff[NOFF];
@@ -252,9 +271,7 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
   } else {
     koff[0] = DmaK::offset(k_ld, tid);
   }
-  constexpr int SPER = BK * BQ * 2 / 1024 / NW;   // dS fragments per wavefront and tile
-  const uint32_t sdst = lds_address(sm.ds) + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
-  auto stage = [&](int idx, int buf) {   // list entry idx -> stage buf
+  auto stage_k = [&](int idx, int buf) {
     const int kt = __builtin_amdgcn_readfirstlane((int)sm.list[idx]);   // uniform
     const int n0 = kt * BK;
     if constexpr (F32) {
@@ -264,95 +281,141 @@ __global__ __launch_bounds__(NT) void bwd_dq_ds_kernel(BwdArgs a) {
     } else {
       DmaK::load(reinterpret_cast<char*>(sm.k[buf]), kbh + n0 * k_ld, koff[0], k_ld, tid, a.seq_k - n0);
     }
+  };
+  // ---- this wavefront's dS fragments of list entry idx, into registers ----
+  // Returns whether its query tile has the tile (wavefront-uniform). The loads
+  // are issued either way (an absent tile re-reads the other query tile's,
+  // which the entry always has), so that every entry issues the same number
+  // of loads and the waits below count them exactly.
+  u32x4 dsr[3][DS_FRAGS];
+  auto load_ds = [&](int idx, u32x4 (&r)[DS_FRAGS]) __attribute__((always_inline)) {
+    const int32_t own = __builtin_amdgcn_readfirstlane(sm.slot[idx][q]);
+    const int32_t other = __builtin_amdgcn_readfirstlane(sm.slot[idx][q ^ 1]);
+    const int64_t slot = own >= 0 ? own : other;
+    const char* src = ds_rep + slot * (BK * BQ * 2);
 #pragma unroll
-    for (int q = 0; q < PAIR; ++q) {
-      const int64_t slot = __builtin_amdgcn_readfirstlane(sm.slot[idx][q]);   // uniform
-      if (slot < 0) continue;
-      // the tile is copied as stored, fragment i * NW + w by this wavefront
-      const char* src = reinterpret_cast<const char*>(ds_rep + slot * (BK * BQ)) + w * 1024;
-      const uint32_t dst = sdst + (uint32_t)(buf * PAIR + q) * (BK * BQ * 2);
-#pragma unroll
-      for (int i = 0; i < SPER; ++i)
-        DmaK::dma16_nt(src + i * NW * 1024, 16u * (uint32_t)l, dst + (uint32_t)(i * NW) * 1024u);
-    }
+    for (int s = 0; s < DS_FRAGS; ++s) r[s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + s * 1024));
+    return own >= 0;
   };
 
-  // dQ^T (channels x rows) += K^T (channels x keys) dS^T (keys x rows), 16
-  // keys per step: K^T read transposed, dS^T as the stored fragment lane, both
-  // with the same key order per lane half. Only the present query tiles' row
-  // blocks take part (P0, P1: query tile 0, 1 present).
-  auto products = [&](const char* kb, const char* sb, auto p0_c, auto p1_c) {
-    constexpr bool P0 = decltype(p0_c)::value, P1 = decltype(p1_c)::value;
-    constexpr int NJ = (P0 ? BLK / 2 : 0) + (P1 ? BLK / 2 : 0);
+  // LDS addresses of this lane's two transposing K reads per channel block in
+  // buffer 0, first 16-key step. The swizzle depends on the row modulo 16, so
+  // step s adds s * 16 rows as an immediate offset and buffer 1 adds one
+  // tile. Kept opaque so that the compiler does not rebuild them per read.
+  uint32_t ko[CB][2];
+  {
+    const uint32_t kbase = lds_address(sm.k[0]);
+    const int i = l & 15;
+    const int r = 4 * g + (i >> 2);
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int r0 = 16 * s + 4 * g;
-      const u32x4 ka = tr_operand<D>(kb, l, 32 * cbw, r0, r0 + 8);
-#pragma unroll
-      for (int j = 0; j < BLK; ++j) {
-        const int rb = rb_of(j);
-        const int q = rb >> 1;
-        if ((q == 0 && !P0) || (q == 1 && !P1)) continue;
-        acc[j] = mfma32(ka, *reinterpret_cast<const u32x4*>(sb + q * (BK * BQ * 2) + ((rb & 1) * 8 + s) * 1024 + l * 16),
-                        acc[j]);
-      }
-    }
-    sched_lds_mfma<(BK / 16) * NJ, (1 + 2 * NJ) / NJ, 2>();
-  };
-
-  for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
-    const int n_list = compact_pair(ccol, scol, (int64_t)a.tq, kt0, min(LIST_CAP, a.tk - kt0), has1, sm.list,
-                                    sm.slot, sm.scan, tid);
-    // this workgroup's part of the list (all of it unless lists are split)
-    const int lo = (int)((int64_t)n_list * sp / ks), hi = (int)((int64_t)n_list * (sp + 1) / ks);
-    if (lo == hi) continue;
-    stage(lo, 0);
-
-    for (int it = lo; it < hi; ++it) {
-      const int buf = 0;
-      wait_vmem();       // this stage landed (nothing younger is in flight)
-      __syncthreads();   // the stage is visible to all
-      const char* kb = reinterpret_cast<const char*>(sm.k[buf]);
-      const char* sb = reinterpret_cast<const char*>(sm.ds[buf]);
-      const bool p0 = sm.slot[it][0] >= 0, p1 = sm.slot[it][1] >= 0;
-      if (p0 && p1) products(kb, sb, std::true_type{}, std::true_type{});
-      else if (p0) products(kb, sb, std::true_type{}, std::false_type{});
-      else products(kb, sb, std::false_type{}, std::true_type{});
-      __syncthreads();   // every wavefront is done with the stage
-      if (it + 1 < hi) stage(it + 1, 0);
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = 32 * cb + 16 * ((l >> 4) & 1) + 4 * (i & 3);
+      ko[cb][0] = kbase + (uint32_t)rm_byte<D>(r, col);
+      ko[cb][1] = kbase + (uint32_t)rm_byte<D>(r + 8, col);
+      asm volatile("" : "+v"(ko[cb][0]));
+      asm volatile("" : "+v"(ko[cb][1]));
     }
   }
 
-  // ---- epilogue: dQ = scale * (dQ^T)^T; lane = query row, registers = channels ----
-  // Column c of stored fragment row block rb is row 32 rb + 16 t + 4 g +
-  // (j < 4 ? j : j + 4) with g, t = bits 4, 3 of c, j = c % 8.
+  // dQ^T (channels x rows) += K^T (channels x keys) dS^T (keys x rows), 16
+  // keys per step: K^T read transposed from LDS, dS^T the wavefront's
+  // fragment, both with the same key order per lane half.
+  auto products = [&](int buf, const u32x4 (&r)[DS_FRAGS]) __attribute__((always_inline)) {
+    const uint32_t tb = (uint32_t)buf * (BK * D * 2);
+    uint32_t ka[CB][2];
 #pragma unroll
-  for (int j = 0; j < BLK; ++j) {
-    const int rb = rb_of(j);
-    const int c = lr;
+    for (int cb = 0; cb < CB; ++cb) {
+      ka[cb][0] = ko[cb][0] + tb;
+      ka[cb][1] = ko[cb][1] + tb;
+    }
+#pragma unroll
+    for (int s = 0; s < DS_FRAGS; ++s) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const u32x2 x = lds_tr16(ka[cb][0], (uint32_t)s * (16 * 2 * D));
+        const u32x2 y = lds_tr16(ka[cb][1], (uint32_t)s * (16 * 2 * D));
+        acc[cb] = mfma32(u32x4{x[0], x[1], y[0], y[1]}, r[s], acc[cb]);
+      }
+    }
+    sched_lds_mfma<DS_FRAGS * CB, 2, 2>();
+  };
+
+  for (int kt0 = 0; kt0 < a.tk; kt0 += LIST_CAP) {
+    const int n_list = compact_pair(srow0, srow1, kt0, min(LIST_CAP, a.tk - kt0), sm.list, sm.slot, sm.scan, tid);
+    // this workgroup's part of the list (all of it unless lists are split)
+    const int lo = (int)((int64_t)n_list * sp / ks), hi = (int)((int64_t)n_list * (sp + 1) / ks);
+    if (lo == hi) continue;
+
+    // Pipeline: K of entry i is issued one entry ahead, this wavefront's dS
+    // fragments two ahead. In the main loop every entry issues its eight dS
+    // loads (an entry near the end re-loads the last one), and each of them
+    // is consumed by a later entry, so none is dropped by the compiler. At
+    // the top of entry i the loads in flight are then, oldest first, dS(i),
+    // K(i) and dS(i + 1): waiting until only dS(i + 1)'s remain covers entry
+    // i. The last two entries (the tail) issue no dS loads and wait for all.
+    bool pres[3];
+    stage_k(lo, 0);
+    pres[0] = load_ds(lo, dsr[0]);
+    pres[1] = load_ds(min(lo + 1, hi - 1), dsr[1]) && lo + 1 < hi;
+    pres[2] = false;
+    auto entry = [&](auto ring_c, auto tail_c, int it) __attribute__((always_inline)) {
+      constexpr int R = decltype(ring_c)::value;
+      constexpr int R2 = (R + 2) % 3;
+      constexpr bool TAIL = decltype(tail_c)::value;
+      const int buf = (it - lo) & 1;
+      if constexpr (TAIL) wait_vmem();
+      else wait_vmem_le<DS_FRAGS>();
+      __syncthreads();   // K(it) visible to all; every wavefront is done with K(it - 1)
+      if (it + 1 < hi) stage_k(it + 1, buf ^ 1);
+      if constexpr (!TAIL) pres[R2] = load_ds(min(it + 2, hi - 1), dsr[R2]) && it + 2 < hi;
+      if (pres[R]) products(buf, dsr[R]);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    int it = lo;
+    for (; it + 2 < hi; it += 3) {
+      entry(I0{}, std::false_type{}, it);
+      entry(I1{}, std::false_type{}, it + 1);
+      entry(I2{}, std::false_type{}, it + 2);
+    }
+    if (it < hi) entry(I0{}, std::true_type{}, it);
+    if (it + 1 < hi) entry(I1{}, std::true_type{}, it + 1);
+    __syncthreads();   // K buffers free before the next pass restages them
+  }
+
+  // ---- epilogue: dQ = scale * (dQ^T)^T; lane = query row, registers = channels ----
+  // Column c of a stored fragment of row half t is row 32 t + 16 u + 4 v +
+  // (j < 4 ? j : j + 4) with v, u = bits 4, 3 of c, j = c % 8.
+  {
+    const int c = l & 31;
     const int jj = c & 7;
-    const int m = (qt0 + (rb >> 1)) * BQ + 32 * (rb & 1) + 16 * ((c >> 3) & 1) + 4 * (c >> 4) + (jj < 4 ? jj : jj + 4);
+    const int m = (qt0 + q) * BQ + 32 * half + 16 * ((c >> 3) & 1) + 4 * (c >> 4) + (jj < 4 ? jj : jj + 4);
     if (m < a.seq_q && ks > 1) {   // float32 partial [ks][B][H][Sq][D]
       float* out = a.dqpart + ((((int64_t)sp * a.batch + b) * a.heads + h) * a.seq_q + m) * D;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<f32x4*>(out + 32 * cbw + 8 * q4 + 4 * g) =
-            f32x4{acc[j][4 * q4] * a.scale, acc[j][4 * q4 + 1] * a.scale, acc[j][4 * q4 + 2] * a.scale,
-                  acc[j][4 * q4 + 3] * a.scale};
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(out + 32 * cb + 8 * q4 + 4 * g) =
+              f32x4{acc[cb][4 * q4] * a.scale, acc[cb][4 * q4 + 1] * a.scale, acc[cb][4 * q4 + 2] * a.scale,
+                    acc[cb][4 * q4 + 3] * a.scale};
     } else if (m < a.seq_q) {
       const int64_t qoff = (int64_t)b * a.q_sb + (int64_t)m * a.q_ss + (int64_t)h * a.q_sh;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int c0 = 32 * cbw + 8 * q4 + 4 * g;
-        const float x0 = acc[j][4 * q4] * a.scale, x1 = acc[j][4 * q4 + 1] * a.scale;
-        const float x2 = acc[j][4 * q4 + 2] * a.scale, x3 = acc[j][4 * q4 + 3] * a.scale;
-        if constexpr (F32) {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dq) + qoff + c0) = f32x4{x0, x1, x2, x3};
-        } else {
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.dq) + qoff + c0) =
-              u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int c0 = 32 * cb + 8 * q4 + 4 * g;
+          const float x0 = acc[cb][4 * q4] * a.scale, x1 = acc[cb][4 * q4 + 1] * a.scale;
+          const float x2 = acc[cb][4 * q4 + 2] * a.scale, x3 = acc[cb][4 * q4 + 3] * a.scale;
+          if constexpr (F32) {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.dq) + qoff + c0) = f32x4{x0, x1, x2, x3};
+          } else {
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.dq) + qoff + c0) =
+                u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+          }
         }
-      }
     }
   }
 }
@@ -403,6 +466,9 @@ hipError_t launch_bwd_plan(const BwdArgs& a, bool with_slots, hipStream_t stream
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, a, (int32_t)(mrows * a.tk));
   if ((e = hipGetLastError()) != hipSuccess || !with_slots) return e;
   hipLaunchKernelGGL(plan_slots_kernel, dim3(a.tk, mrows), dim3(256), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_transpose_kernel, dim3((a.tk + 63) / 64, (a.tq + 63) / 64, mrows), dim3(256), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

@@ -129,6 +129,7 @@ struct BwdArgs {
   int32_t* row_off;          // [bm*hm][tk] exclusive prefix sums of row_cnt
   int32_t* plan;             // [0] total non-SKIP tiles, [1] 1 if the dS store is in use
   int32_t* slots;            // [bm*hm][tk][tq] slot of each non-SKIP tile
+  int32_t* slots_q;          // [bm*hm][tq][tk] the same, query-major, -1 for SKIP tiles
   uint16_t* ds;              // [rep][total][kBwdBlockK keys][kBwdBlockQ rows] bf16
   int64_t ds_capacity;       // bytes available at ds
   int32_t rep;               // (b, h) pairs per mask row
