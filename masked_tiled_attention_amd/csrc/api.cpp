@@ -394,7 +394,8 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   // the recompute dQ map
   const int64_t mrows = (int64_t)mk.bm * mk.hm;
   auto order = [&](size_t at, const uint8_t* cls, int64_t nrows, int64_t lines_per_mr, int64_t len, int64_t outer,
-                   int64_t line, int64_t elem, int32_t group, int64_t group_stride) -> const int32_t* {
+                   int64_t line, int64_t elem, int32_t group, int64_t group_stride,
+                   bool mark_empty) -> const int32_t* {
     fm::OrderArgs o{};
     o.classes = cls;
     o.rows = (int32_t)(nrows * lines_per_mr);
@@ -405,6 +406,7 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
     o.elem_stride = elem;
     o.group = group;
     o.group_stride = group_stride;
+    o.mark_empty = mark_empty ? 1 : 0;
     o.counts = reinterpret_cast<int32_t*>(w + at);
     o.order = o.counts + o.rows;
     if (run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_order(o, stream); }) != hipSuccess) return nullptr;
@@ -412,12 +414,12 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   };
   const int32_t kv_group = mk.hm > 1 ? a.group : 1;   // class rows per K/V mask row
   a.order_k = order(L.order_k, classes_t, (int64_t)mk.bm * (mk.hm > 1 ? a.heads_kv : 1), tk, tq,
-                    (int64_t)kv_group * tk * tq, tq, 1, kv_group, (int64_t)tk * tq);
+                    (int64_t)kv_group * tk * tq, tq, 1, kv_group, (int64_t)tk * tq, true);
   if (!a.order_k) return hip_fail(hipGetLastError(), "backward order launch");
   // the recompute dQ kernel's order only when its path is certain (the
   // workspace cannot hold the stored-dS slot map); else it keeps the default
   if (ws_bytes < L.ds) {
-    a.order_qq = order(L.order_qq, classes_q, mrows, tq_q, tk_q, (int64_t)tq_q * tk_q, tk_q, 1, 1, 0);
+    a.order_qq = order(L.order_qq, classes_q, mrows, tq_q, tk_q, (int64_t)tq_q * tk_q, tk_q, 1, 1, 0, false);
     if (!a.order_qq) return hip_fail(hipGetLastError(), "backward order launch");
   }
   *lay = L;

@@ -162,7 +162,11 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   // float32 partial dK, dV that a second kernel sums.
   const int split = GROUPED && a.part != nullptr;
   const int rep = split ? a.rep_kv * a.group : a.rep_kv;
-  const int line = __builtin_amdgcn_readfirstlane(a.order_k[blockIdx.x / rep]);   // K/V mask row * tk + key tile
+  const uint32_t ent = (uint32_t)__builtin_amdgcn_readfirstlane(a.order_k[blockIdx.x / rep]);
+  // A line whose key tile no query tile sees (flagged by the order sort): its
+  // dK and dV are zero, written by the epilogue without loading anything.
+  const bool empty = (ent & kEmptyLine) != 0;
+  const int line = (int)(ent & ~kEmptyLine);   // K/V mask row * tk + key tile
   // (integer divisions by launch constants expand to vector code: the results
   // are taken back to scalar registers so that the addresses stay scalar)
   const int kt = __builtin_amdgcn_readfirstlane(line % a.tk);
@@ -191,6 +195,26 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     const void* src = is_p ? a.k : a.v;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) kvf[s] = load8_as_bf16<F32>(src, off + 16 * s);
+  }
+  if (empty) {   // dK = dV = 0 for this tile's keys: no list, bounds or tiles
+    if (!key_ok) return;
+    const bool is_k = !is_p;
+    if (split) {   // float32 partials [2][B][H][Sk][D]: dK, then dV
+      float* out = a.part + (is_k ? 0 : (int64_t)a.batch * a.heads * a.seq_k * D) +
+                   (((int64_t)b * a.heads + hk * a.group + gsel) * a.seq_k + n) * D;
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) *reinterpret_cast<f32x4*>(out + 8 * c + 4 * g) = f32x4{};
+    } else {
+      const int64_t off = is_k ? (int64_t)b * a.k_sb + (int64_t)n * a.k_ss + (int64_t)hk * a.k_sh
+                               : (int64_t)b * a.v_sb + (int64_t)n * a.v_ss + (int64_t)hk * a.v_sh;
+      char* out = reinterpret_cast<char*>(is_k ? a.dk : a.dv) + off * ES;
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        if constexpr (F32) *reinterpret_cast<f32x4*>(out + (8 * c + 4 * g) * 4) = f32x4{};
+        else *reinterpret_cast<u32x2*>(out + (8 * c + 4 * g) * 2) = u32x2{0u, 0u};
+      }
+    }
+    return;
   }
 
   // Per query head (set at the start of each head): the lane's key bounds

@@ -175,7 +175,8 @@ __global__ __launch_bounds__(1024) void order_sort_kernel(OrderArgs a) {
     pre += v[i];
   }
   __syncthreads();
-  for (int r = tid; r < a.rows; r += 1024) a.order[atomicAdd(&hist[key(r)], 1)] = r;
+  for (int r = tid; r < a.rows; r += 1024)
+    a.order[atomicAdd(&hist[key(r)], 1)] = (int32_t)((uint32_t)r | (a.mark_empty && a.counts[r] <= 0 ? kEmptyLine : 0u));
 }
 
 }  // namespace

@@ -94,7 +94,9 @@ struct OrderArgs {
   int64_t group_stride;
   int32_t* counts;         // [rows] non-SKIP entries per line
   int32_t* order;          // [rows] line indices, longest first
+  int32_t mark_empty;      // set: lines with no non-SKIP entry carry kEmptyLine
 };
+constexpr uint32_t kEmptyLine = 0x80000000u;   // order entry flag: the line has no work
 hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
 
 struct BwdArgs {
@@ -140,7 +142,7 @@ struct BwdArgs {
   int32_t rep_kv;
   // Launch orders, longest first (see FwdArgs::order): key tiles of the dK/dV
   // tiling and the recompute dQ kernel's query tiles (may be nullptr).
-  const int32_t* order_k;
+  const int32_t* order_k;   // key-tile lines longest first; empty lines flagged with kEmptyLine
   const int32_t* order_qq;
   // Grouped-query attention with a mask shared by all heads: one dK/dV
   // workgroup per query head, float32 partials [2][B][H][Sk][D] (dK, then dV)

@@ -90,6 +90,43 @@ def test_gqa_head_dim_64_and_float32(gpu_lib):
     _check(gpu_lib, q, k, v, do, tuple(x[None, None] for x in SM.causal(256)), 0.125, "float32")
 
 
+def _dead_keys(n, lo, hi, base):
+    """`base` bounds with keys [lo, hi) masked for every row."""
+    lts, lte, uts, ute = (np.array(x) for x in base)
+    lts[lo:hi], lte[lo:hi] = 0, n
+    return lts, lte, uts, ute
+
+
+@pytest.mark.parametrize("case", ["shared", "per_head", "float32"])
+def test_gqa_key_tiles_masked_for_every_row(gpu_lib, case):
+    """Keys [128, 384) are masked for every row of every query head: their two
+    key tiles have no non-SKIP tile in any head of the group, so the dK/dV
+    workgroups write zeros without walking a list. Shared mask (float32
+    partials per query head, summed afterwards), per-head masks (the group
+    walked in one workgroup) and float32 inputs and outputs (one K/V head per
+    query head)."""
+    n, d = 520, 128
+    rng = np.random.default_rng(75)
+    if case == "per_head":
+        H, hkv = 4, 2
+        fams = [SM.causal(n), SM.document_causal(SM.uniform_doc_lengths(rng, n, 40, 300)),
+                SM.prefix_lm(n, n // 4), SM.sliding_window_causal(n, 150)]
+        vec = SM.stack([[_dead_keys(n, 128, 384, fams[h]) for h in range(H)]])
+    else:
+        H, hkv = (4, 2) if case == "shared" else (2, 2)
+        vec = tuple(x[None, None] for x in _dead_keys(n, 128, 384, SM.causal(n)))
+    dtype = torch.float32 if case == "float32" else torch.bfloat16
+    q, k, v, do = _inputs(1, n, H, hkv, d, seed=76, dtype=dtype)
+    _check(gpu_lib, q, k, v, do, vec, 1 / math.sqrt(d), f"dead key tiles, {case}")
+    qc, kc, vc, doc = (t.cuda() for t in (q, k, v, do))
+    m = dev_mask(vec)
+    o, lse = gpu_lib.fm_attn_fwd(qc, kc, vc, m, 1 / math.sqrt(d))
+    _, dk, dv = gpu_lib.fm_attn_bwd(qc, kc, vc, o, lse, doc, m, 1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    assert torch.all(dk[:, 128:384] == 0) and torch.all(dv[:, 128:384] == 0)
+    assert torch.any(dk[:, :128] != 0) and torch.any(dv[:, 384:] != 0)
+
+
 def test_gqa_rejects_non_dividing_heads(gpu_lib):
     q, k, v = ST.qkv(1, 64, 64, 4, 128, seed=1)
     k, v = k[:, :, :3].contiguous(), v[:, :, :3].contiguous()
