@@ -297,14 +297,14 @@ BWD_STAGES = ("bwd_pre", "bwd_plan", "bwd", "bwd_dq", "bwd_dq_ds")
 
 
 def split_ms(st, backward):
-    """(forward ms, backward ms) per step from stage times. Classification
-    runs once in the forward and twice in the backward (one per backward
-    tiling); its small cost is split in that ratio, as is the launch-order
-    pass."""
+    """(forward ms, backward ms) per step from stage times. The summary, class
+    map and launch-order passes run as one launch each in the forward and in
+    the backward (which does both of its tilings in each); their small cost is
+    split evenly."""
     per = lambda s: st[s][0]
     shared = per("classify_summary") + per("classify_map") + per("order")
-    fwd_ms = per("fwd") + (shared / 3 if backward else shared)
-    bwd_ms = sum(per(s) for s in BWD_STAGES) + 2 * shared / 3 if backward else 0.0
+    fwd_ms = per("fwd") + (shared / 2 if backward else shared)
+    bwd_ms = sum(per(s) for s in BWD_STAGES) + shared / 2 if backward else 0.0
     return fwd_ms, bwd_ms
 
 

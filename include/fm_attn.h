@@ -140,9 +140,9 @@ fm_status fm_workspace_size(const fm_problem* problem, const fm_mask* mask,
 /* Bytes of workspace with which fm_attn_bwd keeps dS instead of recomputing
  * it: the dK/dV kernel writes the bf16 dS tiles it forms anyway, and dQ is the
  * product scale * dS K over the stored tiles. That is fm_workspace_size(.., 1)
- * plus two slot indices per tile of the dK/dV tiling and 2 bytes per (query row,
- * key) pair of every non-SKIP tile, for every (b, h) (rows and keys padded to
- * the tile). The count depends on the mask contents, so the call classifies
+ * plus one slot index per tile of the dK/dV tiling, one count per 64 of its
+ * tiles, and 2 bytes per (query row, key) pair of every non-SKIP tile, for
+ * every (b, h) (rows and keys padded to the tile). The count depends on the mask contents, so the call classifies
  * the mask on `stream` using `workspace` (device, at least
  * fm_workspace_size(.., 1) bytes, 256-byte aligned; contents overwritten) and
  * waits for the stream. */
@@ -318,13 +318,13 @@ typedef enum {
   FM_STAGE_CLASSIFY_SUMMARY = 0,
   FM_STAGE_CLASSIFY_MAP = 1,
   FM_STAGE_FWD = 2,
-  FM_STAGE_BWD_PRE = 3,
+  FM_STAGE_BWD_PRE = 3,     /* backward: D = rowsum(dO * O), with the stored-dS slot map */
   FM_STAGE_BWD = 4,         /* dK / dV kernel */
   FM_STAGE_BWD_DQ = 5,      /* dQ kernel */
   FM_STAGE_LOCALIZE = 6,
-  FM_STAGE_BWD_PLAN = 7,    /* stored-dS slot plan (count, scan, slots, query-major copy) */
+  FM_STAGE_BWD_PLAN = 7,    /* not recorded: the stored-dS plan runs in the ORDER and BWD_PRE launches */
   FM_STAGE_BWD_DQ_DS = 8,   /* dQ from stored dS */
-  FM_STAGE_ORDER = 9,       /* launch orders, longest tiles first (count, sort) */
+  FM_STAGE_ORDER = 9,       /* launch orders, longest tiles first (backward: with the stored-dS offsets) */
   FM_STAGE_TRANSFER = 10,   /* mask-pruned K/V transfer set */
   FM_STAGE_CHUNK_WORK = 11, /* open pairs per chunk of the query axis */
   FM_STAGE_VT = 12,         /* FP8 forward: V^T tile pre-pass */

@@ -180,16 +180,17 @@ fm_status check_ptr(const void* ptr, const char* name) {
 // tiles, transposed, and the dQ tiles), plus for the backward the per-row
 // LSE * log2(e) and D [B][H][Sp] float32 (Sp = Sq rounded up to 128, the
 // padding rows neutral) and the stored-dS plan counters. total is the
-// minimum. Beyond it, the backward may place the stored-dS slot map
-// [Bm*Hm][Tk][Tq] int32 at `slots`, its query-major copy [Bm*Hm][Tq][Tk] at
-// `slots_q` and the dS tiles from `ds` on.
+// minimum. Beyond it, the backward may place the chunk prefixes of the dK/dV
+// class rows [Bm*Hm][Tk][ceil(Tq / 64)] int32 at `chunk_pre`, the query-major
+// stored-dS slot map [Bm*Hm][Tq][Tk] int32 at `slots_q` and the dS tiles from
+// `ds` on.
 // 256-byte aligned sections.
 struct Layout {
   size_t summary = 0, map = 0, summary_q = 0, map_q = 0, lse2 = 0, drow = 0;
-  size_t row_cnt = 0, row_off = 0, plan = 0, total = 0, slots = 0, slots_q = 0, ds = 0;
+  size_t row_cnt = 0, row_off = 0, plan = 0, total = 0, chunk_pre = 0, slots_q = 0, ds = 0;
   size_t counts = 0, order = 0;   // forward launch order
   size_t vt = 0;                   // FP8 forward: V^T tiles [B][H_kv][Tk][8 KiB]
-  size_t order_k = 0, order_qq = 0;   // backward launch orders (counts, then order)
+  size_t order_k = 0, order_qq = 0;   // backward launch orders (dQ: its counts, then the order)
   size_t part = 0;                     // split-head dK/dV partials (0: not used)
   size_t opart = 0, lpart = 0;         // split-list forward partials (0: not used)
   int32_t ksplit = 1;
@@ -266,8 +267,8 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t
     L.plan = off;
     off = align256(off + 16);
     const int64_t tq_q = ceil_div(p->seqlen_q, fm::kDqBlockQ);
-    L.order_k = off;   // counts then order, for each of the two launch orders
-    off = align256(off + (size_t)(mrows * tk * 8));
+    L.order_k = off;   // the counts are row_cnt
+    off = align256(off + (size_t)(mrows * tk * 4));
     L.order_qq = off;
     off = align256(off + (size_t)(mrows * tq_q * 8));
     L.dq_split = dq_split(p);
@@ -279,8 +280,8 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t
       L.part = off;
       off = align256(off + (size_t)p->batch * p->heads * p->seqlen_k * p->head_dim * 4 * 2);
     }
-    L.slots = off;
-    L.slots_q = align256(L.slots + (size_t)(mrows * tk * tq * 4));
+    L.chunk_pre = off;
+    L.slots_q = align256(L.chunk_pre + (size_t)(mrows * tk * ceil_div(tq, 64) * 4));
     L.ds = align256(L.slots_q + (size_t)(mrows * tq * tk * 4));
   } else {
     add_tiling(fm::kFwdBlockQ, fm::kFwdBlockK, &L.summary, &L.map);
@@ -307,8 +308,8 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t
   return L;
 }
 
-fm_status classify_into(const fm::MaskArgs& mk, int32_t sq, int32_t sk, int32_t bq, int32_t bk,
-                        int32_t transposed, int32_t* summary, uint8_t* classes, hipStream_t s) {
+fm::ClassifyArgs classify_args(const fm::MaskArgs& mk, int32_t sq, int32_t sk, int32_t bq, int32_t bk,
+                               int32_t transposed, int32_t* summary, uint8_t* classes, int32_t* counts = nullptr) {
   fm::ClassifyArgs c{};
   c.mask = mk;
   c.seq_q = sq;
@@ -320,6 +321,15 @@ fm_status classify_into(const fm::MaskArgs& mk, int32_t sq, int32_t sk, int32_t 
   c.summary = summary;
   c.classes = classes;
   c.transposed = transposed;
+  c.counts = counts;
+  return c;
+}
+
+// Summary and class map (with the line counts when `counts` is set).
+fm_status classify_into(const fm::MaskArgs& mk, int32_t sq, int32_t sk, int32_t bq, int32_t bk,
+                        int32_t transposed, int32_t* summary, uint8_t* classes, hipStream_t s,
+                        int32_t* counts = nullptr) {
+  const fm::ClassifyArgs c = classify_args(mk, sq, sk, bq, bk, transposed, summary, classes, counts);
   hipError_t e = run_stage(FM_STAGE_CLASSIFY_SUMMARY, s, [&] { return fm::launch_classify_summary(c, s); });
   if (e != hipSuccess) return hip_fail(e, "classify summary launch");
   e = run_stage(FM_STAGE_CLASSIFY_MAP, s, [&] { return fm::launch_classify_map(c, s); });
@@ -327,10 +337,14 @@ fm_status classify_into(const fm::MaskArgs& mk, int32_t sq, int32_t sk, int32_t 
   return FM_OK;
 }
 
-// Validation, classification (both tilings) and the arguments shared by
-// fm_attn_bwd and fm_bwd_workspace_size_ds; tensor pointers are left unset.
+// Validation, the pre-passes and the arguments shared by fm_attn_bwd and
+// fm_bwd_workspace_size_ds; the caller sets the tensor pointers beforehand.
+// `rows`: run the row pass too (needs o, dout, lse). `size_query`: only the
+// tile count is wanted (the plan scan runs whatever the workspace holds).
+// Four launches: summaries, class maps with line counts, launch orders (+
+// slot offsets), and the slot map (stored dS) with the row pass.
 fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t ws_bytes, hipStream_t stream,
-                    fm::BwdArgs* out, Layout* lay) {
+                    bool rows, bool size_query, fm::BwdArgs* out, Layout* lay) {
   fm_status st = check_problem(p);
   if (st != FM_OK) return st;
   if (p->dtype == FM_FP8_E4M3) return fail(FM_ERR_UNSUPPORTED, "the backward takes bf16 or float32 inputs");
@@ -350,12 +364,7 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   char* w = static_cast<char*>(ws);
   uint8_t* classes_t = reinterpret_cast<uint8_t*>(w + L.map);
   uint8_t* classes_q = reinterpret_cast<uint8_t*>(w + L.map_q);
-  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kBwdBlockQ, fm::kBwdBlockK, 1,
-                     reinterpret_cast<int32_t*>(w + L.summary), classes_t, stream);
-  if (st != FM_OK) return st;
-  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kDqBlockQ, fm::kDqBlockK, 0,
-                     reinterpret_cast<int32_t*>(w + L.summary_q), classes_q, stream);
-  if (st != FM_OK) return st;
+  const int64_t mrows = (int64_t)mk.bm * mk.hm;
 
   fm::BwdArgs& a = *out;
   a.lse2 = reinterpret_cast<float*>(w + L.lse2);
@@ -382,45 +391,66 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   a.tk_q = tk_q;
   a.row_cnt = reinterpret_cast<int32_t*>(w + L.row_cnt);
   a.row_off = reinterpret_cast<int32_t*>(w + L.row_off);
-  a.plan = reinterpret_cast<int32_t*>(w + L.plan);
   a.rep = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : p->heads);
   a.rep_kv = (mk.bm > 1 ? 1 : p->batch) * (mk.hm > 1 ? 1 : a.heads_kv);
   a.part = L.part ? reinterpret_cast<float*>(w + L.part) : nullptr;
   a.dq_split = L.dq_split;
   a.dqpart = L.dqpart ? reinterpret_cast<float*>(w + L.dqpart) : nullptr;
-  // launch orders: key-tile rows of the transposed dK/dV map (one line per
-  // K/V mask row and key tile, counting the class rows of the K/V head's
-  // query heads when the mask has a row per head) and the query-tile rows of
-  // the recompute dQ map
-  const int64_t mrows = (int64_t)mk.bm * mk.hm;
-  auto order = [&](size_t at, const uint8_t* cls, int64_t nrows, int64_t lines_per_mr, int64_t len, int64_t outer,
-                   int64_t line, int64_t elem, int32_t group, int64_t group_stride,
-                   bool mark_empty) -> const int32_t* {
-    fm::OrderArgs o{};
-    o.classes = cls;
-    o.rows = (int32_t)(nrows * lines_per_mr);
-    o.len = (int32_t)len;
-    o.inner = (int32_t)lines_per_mr;
-    o.outer_stride = outer;
-    o.line_stride = line;
-    o.elem_stride = elem;
-    o.group = group;
-    o.group_stride = group_stride;
-    o.mark_empty = mark_empty ? 1 : 0;
-    o.counts = reinterpret_cast<int32_t*>(w + at);
-    o.order = o.counts + o.rows;
-    if (run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_order(o, stream); }) != hipSuccess) return nullptr;
-    return o.order;
-  };
+  // Stored dS when the workspace can hold at least the slot map; whether it
+  // holds every dS tile is decided on the device by the plan.
+  const bool maybe_ds = !size_query && ws_bytes >= L.ds;
+  a.plan = (maybe_ds || size_query) ? reinterpret_cast<int32_t*>(w + L.plan) : nullptr;
+  if (maybe_ds) {
+    a.chunk_pre = reinterpret_cast<int32_t*>(w + L.chunk_pre);
+    a.slots_q = reinterpret_cast<int32_t*>(w + L.slots_q);
+    a.ds = reinterpret_cast<uint16_t*>(w + L.ds);
+    a.ds_capacity = (int64_t)(ws_bytes - L.ds);
+  }
+  const bool f32 = p->dtype == FM_FP32;
+  int32_t* counts_q = reinterpret_cast<int32_t*>(w + L.order_qq);
+  fm::ClassifyArgs ct = classify_args(mk, p->seqlen_q, p->seqlen_k, fm::kBwdBlockQ, fm::kBwdBlockK, 1,
+                                      reinterpret_cast<int32_t*>(w + L.summary), classes_t, a.row_cnt);
+  ct.chunk_pre = a.chunk_pre;
+  const fm::ClassifyArgs cq = classify_args(mk, p->seqlen_q, p->seqlen_k, fm::kDqBlockQ, fm::kDqBlockK, 0,
+                                            reinterpret_cast<int32_t*>(w + L.summary_q), classes_q, counts_q);
+  hipError_t e = run_stage(FM_STAGE_CLASSIFY_SUMMARY, stream, [&] { return fm::launch_bwd_summaries(ct, cq, stream); });
+  if (e != hipSuccess) return hip_fail(e, "backward summary launch");
+  e = run_stage(FM_STAGE_CLASSIFY_MAP, stream, [&] { return fm::launch_bwd_maps(ct, cq, stream); });
+  if (e != hipSuccess) return hip_fail(e, "backward class map launch");
+
+  // Launch orders: key-tile lines of the dK/dV map (one per K/V mask row and
+  // key tile, counting the class rows of the K/V head's query heads when the
+  // mask has a row per head) and, when its path is certain (the workspace
+  // cannot hold the stored-dS slot map), the recompute dQ kernel's query-tile
+  // lines; else that kernel keeps the default order.
   const int32_t kv_group = mk.hm > 1 ? a.group : 1;   // class rows per K/V mask row
-  a.order_k = order(L.order_k, classes_t, (int64_t)mk.bm * (mk.hm > 1 ? a.heads_kv : 1), tk, tq,
-                    (int64_t)kv_group * tk * tq, tq, 1, kv_group, (int64_t)tk * tq, true);
-  if (!a.order_k) return hip_fail(hipGetLastError(), "backward order launch");
-  // the recompute dQ kernel's order only when its path is certain (the
-  // workspace cannot hold the stored-dS slot map); else it keeps the default
-  if (ws_bytes < L.ds) {
-    a.order_qq = order(L.order_qq, classes_q, mrows, tq_q, tk_q, (int64_t)tq_q * tk_q, tk_q, 1, 1, 0, false);
-    if (!a.order_qq) return hip_fail(hipGetLastError(), "backward order launch");
+  fm::OrderArgs ok{};
+  ok.counts = a.row_cnt;
+  ok.rows = (int32_t)((int64_t)mk.bm * (mk.hm > 1 ? a.heads_kv : 1) * tk);
+  ok.len = tq;
+  ok.inner = tk;
+  ok.outer_stride = (int64_t)kv_group * tk;
+  ok.group = kv_group;
+  ok.group_stride = tk;
+  ok.order = reinterpret_cast<int32_t*>(w + L.order_k);
+  ok.mark_empty = 1;
+  fm::OrderArgs oq{};
+  if (!size_query && ws_bytes < L.ds) {
+    oq.counts = counts_q;
+    oq.rows = (int32_t)(mrows * tq_q);
+    oq.len = tk_q;
+    oq.inner = oq.rows;
+    oq.group = 1;
+    oq.order = counts_q + oq.rows;
+  }
+  e = run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_bwd_orders(ok, oq, a, stream); });
+  if (e != hipSuccess) return hip_fail(e, "backward order launch");
+  a.order_k = ok.order;
+  a.order_qq = oq.order;
+  if (maybe_ds || rows) {
+    e = run_stage(FM_STAGE_BWD_PRE, stream,
+                  [&] { return fm::launch_bwd_rows(a, maybe_ds, rows, p->head_dim, f32, stream); });
+    if (e != hipSuccess) return hip_fail(e, "backward row pass launch");
   }
   *lay = L;
   return FM_OK;
@@ -511,7 +541,9 @@ fm_status fwd_common(const fm_problem* p, const void* q, const void* k, const vo
   char* w = static_cast<char*>(ws);
   int32_t* summary = reinterpret_cast<int32_t*>(w + L.summary);
   uint8_t* classes = reinterpret_cast<uint8_t*>(w + L.map);
-  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kFwdBlockQ, fm::kFwdBlockK, 0, summary, classes, stream);
+  int32_t* counts = reinterpret_cast<int32_t*>(w + L.counts);
+  st = classify_into(mk, p->seqlen_q, p->seqlen_k, fm::kFwdBlockQ, fm::kFwdBlockK, 0, summary, classes, stream,
+                     counts);
   if (st != FM_OK) return st;
 
   fm::FwdArgs a{};
@@ -535,15 +567,11 @@ fm_status fwd_common(const fm_problem* p, const void* q, const void* k, const vo
   a.tq = tq;
   a.tk = tk;
   fm::OrderArgs oa{};
-  oa.classes = classes;
+  oa.counts = counts;
   oa.rows = (int32_t)((int64_t)mk.bm * mk.hm * tq);
   oa.len = tk;
-  oa.inner = tq;
-  oa.outer_stride = (int64_t)tq * tk;
-  oa.line_stride = tk;
-  oa.elem_stride = 1;
+  oa.inner = oa.rows;
   oa.group = 1;
-  oa.counts = reinterpret_cast<int32_t*>(w + L.counts);
   oa.order = reinterpret_cast<int32_t*>(w + L.order);
   hipError_t e = run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_order(oa, stream); });
   if (e != hipSuccess) return hip_fail(e, "forward order launch");
@@ -625,8 +653,6 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
       (st = check_ptr(dq, "dq")) || (st = check_ptr(dk, "dk")) || (st = check_ptr(dv, "dv")))
     return st;
   fm::BwdArgs a{};
-  Layout L;
-  if ((st = bwd_setup(p, mask, ws, ws_bytes, stream, &a, &L)) != FM_OK) return st;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -636,24 +662,11 @@ fm_status fm_attn_bwd(const fm_problem* p, const void* q, const void* k, const v
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  // Stored dS when the workspace can hold at least the slot map; whether it
-  // holds every dS tile is decided on the device by the plan.
-  char* w = static_cast<char*>(ws);
-  const bool maybe_ds = ws_bytes >= L.ds;
-  if (maybe_ds) {
-    a.slots = reinterpret_cast<int32_t*>(w + L.slots);
-    a.slots_q = reinterpret_cast<int32_t*>(w + L.slots_q);
-    a.ds = reinterpret_cast<uint16_t*>(w + L.ds);
-    a.ds_capacity = (int64_t)(ws_bytes - L.ds);
-    hipError_t e = run_stage(FM_STAGE_BWD_PLAN, stream, [&] { return fm::launch_bwd_plan(a, true, stream); });
-    if (e != hipSuccess) return hip_fail(e, "stored-dS plan launch");
-  } else {
-    a.plan = nullptr;
-  }
+  Layout L;
+  if ((st = bwd_setup(p, mask, ws, ws_bytes, stream, true, false, &a, &L)) != FM_OK) return st;
+  const bool maybe_ds = a.plan != nullptr;
   const bool f32 = p->dtype == FM_FP32;
-  hipError_t e = run_stage(FM_STAGE_BWD_PRE, stream, [&] { return fm::launch_bwd_pre(a, p->head_dim, f32, stream); });
-  if (e != hipSuccess) return hip_fail(e, "backward pre-pass launch");
-  e = run_stage(FM_STAGE_BWD, stream, [&] { return fm::launch_bwd_dkdv(a, p->head_dim, f32, stream); });
+  hipError_t e = run_stage(FM_STAGE_BWD, stream, [&] { return fm::launch_bwd_dkdv(a, p->head_dim, f32, stream); });
   if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
   // both dQ kernels are launched when the dS store may be in use; each exits
   // at once unless the plan selected its path
@@ -696,11 +709,9 @@ fm_status fm_bwd_workspace_size_ds(const fm_problem* p, const fm_mask* mask, voi
   if (!bytes) return fail(FM_ERR_INVALID_ARGUMENT, "bytes is NULL");
   fm::BwdArgs a{};
   Layout L;
-  fm_status st = bwd_setup(p, mask, ws, ws_bytes, stream, &a, &L);
+  fm_status st = bwd_setup(p, mask, ws, ws_bytes, stream, false, true, &a, &L);
   if (st != FM_OK) return st;
-  a.ds_capacity = 0;
-  hipError_t e = run_stage(FM_STAGE_BWD_PLAN, stream, [&] { return fm::launch_bwd_plan(a, false, stream); });
-  if (e != hipSuccess) return hip_fail(e, "stored-dS plan launch");
+  hipError_t e;
   int32_t total = 0;
   if ((e = hipMemcpyAsync(&total, a.plan, sizeof(total), hipMemcpyDeviceToHost, stream)) != hipSuccess ||
       (e = hipStreamSynchronize(stream)) != hipSuccess)

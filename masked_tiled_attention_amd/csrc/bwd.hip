@@ -11,8 +11,7 @@
 // Section "Three ways to raise GPU utilization": work is split over batch,
 // heads and sequence tiles, and each wavefront owns its own output rows.
 //
-// Kernels:
-//   bwd_pre   D per query row;
+// Kernels (the row pass D = rowsum(dO * O) runs with the pre-passes):
 //   bwd_dkdv  one workgroup per (batch, head, 128-key tile) with K and V in
 //             LDS; each pair of wavefronts owns 32 keys, forms S and dP for
 //             half the rows of every non-SKIP 64-row query tile each, and one
@@ -38,63 +37,6 @@ namespace {
 constexpr int NW = 4;            // wavefronts per workgroup
 constexpr int NT = NW * 64;      // threads per workgroup
 constexpr int LIST_CAP = 1024;   // class bytes compacted per pass (4 per thread)
-
-// ------------------------------------------------------------------ pre-pass
-// Per query row (padded to Sp): D = rowsum(dO * O) and LSE * log2(e), the
-// latter +inf where the row sees no key (LSE = -inf) so that P = 0 there; rows
-// past Sq get +inf and 0, so tiles may read whole padded row blocks.
-template <int D, bool F32>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
-  constexpr int TPR = D / 8;            // threads per row
-  constexpr int RPB = 256 / TPR;        // rows per block
-  const int sub = threadIdx.x % TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;   // (b, m, h) linear, m < Sp
-  const int64_t nrows = (int64_t)a.batch * a.seq_pad * a.heads;
-  float part = 0.f;
-  int b = 0, m = 0, h = 0;
-  if (row < nrows) {
-    h = (int)(row % a.heads);
-    m = (int)((row / a.heads) % a.seq_pad);
-    b = (int)(row / ((int64_t)a.heads * a.seq_pad));
-  }
-  if (row < nrows && m < a.seq_q) {
-    const int64_t off = (int64_t)b * a.o_sb + (int64_t)m * a.o_ss + (int64_t)h * a.o_sh + 8 * sub;
-    float x[8], y[8];
-    if constexpr (F32) {
-      const float* po = reinterpret_cast<const float*>(a.o) + off;
-      const float* pd = reinterpret_cast<const float*>(a.dout) + off;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[i] = po[i];
-        y[i] = pd[i];
-      }
-    } else {
-      const u32x4 vo = ld16(reinterpret_cast<const uint16_t*>(a.o) + off);
-      const u32x4 vd = ld16(reinterpret_cast<const uint16_t*>(a.dout) + off);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_lo(vo[i]);
-        x[2 * i + 1] = bf16_hi(vo[i]);
-        y[2 * i] = bf16_lo(vd[i]);
-        y[2 * i + 1] = bf16_hi(vd[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) part = fmaf(x[i], y[i], part);
-  }
-#pragma unroll
-  for (int o = TPR / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-  if (row < nrows && sub == 0) {
-    const int64_t r = ((int64_t)b * a.heads + h) * a.seq_pad + m;
-    float l2 = INFINITY;
-    if (m < a.seq_q) {
-      const float lse = a.lse[((int64_t)b * a.heads + h) * a.seq_q + m];
-      l2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-    }
-    a.lse2[r] = l2;
-    a.drow[r] = part;
-  }
-}
 
 // ------------------------------------------------------------------ dK / dV
 // One workgroup per (batch, K/V head, 128-key tile), eight wavefronts, two per
@@ -822,14 +764,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-template <int D, bool F32>
-hipError_t launch_pre_t(const BwdArgs& a, hipStream_t s) {
-  const int64_t nrows = (int64_t)a.batch * a.seq_pad * a.heads;
-  const int rpb = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_pre_kernel<D, F32>), dim3((unsigned)((nrows + rpb - 1) / rpb)), dim3(256), 0, s, a);
-  return hipGetLastError();
-}
-
 // Split heads: dK, dV of K/V head hk = the sum of the float32 partials of its
 // `group` query heads; one thread per 4 channels of one key.
 template <int D, bool F32>
@@ -882,11 +816,6 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool f32, hipStream_t s) {
-  if (head_dim == 128) return f32 ? launch_pre_t<128, true>(a, s) : launch_pre_t<128, false>(a, s);
-  return f32 ? launch_pre_t<64, true>(a, s) : launch_pre_t<64, false>(a, s);
-}
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, bool f32, hipStream_t s) {
   if (head_dim == 128) return f32 ? launch_dkdv_t<128, true>(a, s) : launch_dkdv_t<128, false>(a, s);

@@ -1,4 +1,4 @@
-// Backward with stored dS: slot plan and dQ = scale * dS K.
+// Backward with stored dS: dQ = scale * dS K.
 //
 // "FlashAttention-2 ... GPU work partitioning" (iplexlaw.co.kr), section
 // "Block processing keeps the global normalization": dQ = scale * dS K with
@@ -9,13 +9,9 @@
 // instead of a second kernel that recomputes S and dP (6 d flops per open
 // pair then, 2 d flops and 2 bytes of dS traffic per pair here).
 //
+// The slot plan (each non-SKIP tile's slot, the total, and whether the
+// workspace holds every tile for every (b, h)) comes from the pre-passes.
 // Kernels:
-//   plan_count  non-SKIP tiles per key-tile row of the dK/dV class map;
-//   plan_scan   one workgroup: exclusive prefix sums (slot offsets), the total
-//               and whether the workspace holds every tile for every (b, h);
-//   plan_slots  each non-SKIP tile's slot (the dK/dV kernel's store address);
-//   plan_transpose  the slot map query-major, -1 for SKIP tiles (the dQ
-//               kernel's key-tile lists);
 //   dq_ds       one workgroup per (b, h, pair of 64-row query tiles), or per
 //               part of the pair's list when few pairs have long key ranges:
 //               for each key tile non-SKIP for either, K goes into LDS and
@@ -37,119 +33,6 @@ constexpr int BK = kBwdBlockK;   // keys per dS tile
 constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr int LIST_CAP = 1024;
-constexpr int64_t kTileBytes = (int64_t)BQ * BK * 2;
-
-// ------------------------------------------------------------------ plan
-// grid (tk, mask rows): row_cnt[mr][kt] = non-SKIP entries of class row (mr, kt).
-__global__ __launch_bounds__(256) void plan_count_kernel(BwdArgs a) {
-  const int kt = blockIdx.x, mr = blockIdx.y;
-  const uint8_t* row = a.classes_t + ((int64_t)mr * a.tk + kt) * a.tq;
-  int c = 0;
-  for (int q = threadIdx.x; q < a.tq; q += 256) c += row[q] != FM_TILE_SKIP;
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-  __shared__ int red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) a.row_cnt[(int64_t)mr * a.tk + kt] = red[0] + red[1] + red[2] + red[3];
-}
-
-// grid (tk, mask rows): slots[mr][kt][qt] = row_off[mr][kt] + rank of qt
-// among the row's non-SKIP entries (entries of SKIP tiles are not written).
-__global__ __launch_bounds__(256) void plan_slots_kernel(BwdArgs a) {
-  const int kt = blockIdx.x, mr = blockIdx.y;
-  const int64_t r = (int64_t)mr * a.tk + kt;
-  const uint8_t* row = a.classes_t + r * a.tq;
-  int32_t* out = a.slots + r * a.tq;
-  __shared__ int wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int carry = a.row_off[r];
-  for (int base = 0; base < a.tq; base += 256) {
-    const int q = base + tid;
-    const int v = q < a.tq && row[q] != FM_TILE_SKIP;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    int pre = carry, chunk = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < wv) pre += wsum[k];
-      chunk += wsum[k];
-    }
-    if (v) out[q] = pre + incl - 1;
-    carry += chunk;
-    __syncthreads();
-  }
-}
-
-// grid (tk / 64, tq / 64, mask rows): slots_q[mr][qt][kt] = slots[mr][kt][qt]
-// for non-SKIP tiles, -1 for SKIP ones; 64 x 64 blocks through LDS, so that
-// both the reads and the writes are row-contiguous. The dQ kernel reads its
-// query tiles' rows of this copy.
-__global__ __launch_bounds__(256) void plan_transpose_kernel(BwdArgs a) {
-  __shared__ int32_t t[64][65];
-  const int kt0 = blockIdx.x * 64, q0 = blockIdx.y * 64, mr = blockIdx.z;
-  const int r = threadIdx.x >> 6, c = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int kt = kt0 + r + 4 * j, q = q0 + c;
-    int32_t v = -1;
-    if (kt < a.tk && q < a.tq) {
-      const int64_t o = ((int64_t)mr * a.tk + kt) * a.tq + q;
-      if (a.classes_t[o] != FM_TILE_SKIP) v = a.slots[o];
-    }
-    t[r + 4 * j][c] = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int q = q0 + r + 4 * j, kt = kt0 + c;
-    if (q < a.tq && kt < a.tk) a.slots_q[((int64_t)mr * a.tq + q) * a.tk + kt] = t[c][r + 4 * j];
-  }
-}
-
-// One workgroup of 1024: row_off = exclusive prefix sums of row_cnt over the
-// nrows = mask rows * tk rows in order, plan[0] = total, plan[1] = 1 when
-// rep * total tiles fit into ds_capacity bytes (and slots fit in int32).
-__global__ __launch_bounds__(1024) void plan_scan_kernel(BwdArgs a, int32_t nrows) {
-  __shared__ int wsum[16];
-  __shared__ int64_t carry;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < nrows; base += 1024) {
-    const int i = base + tid;
-    const int v = i < nrows ? a.row_cnt[i] : 0;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    int64_t pre = carry;
-    int chunk = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (k < wv) pre += wsum[k];
-      chunk += wsum[k];
-    }
-    if (i < nrows) a.row_off[i] = (int32_t)min(pre + incl - v, (int64_t)INT_MAX);
-    __syncthreads();
-    if (tid == 0) carry += chunk;
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const int64_t total = carry;
-    a.plan[0] = (int32_t)min(total, (int64_t)INT_MAX);
-    a.plan[1] = (total < INT_MAX && total * a.rep * kTileBytes <= a.ds_capacity) ? 1 : 0;
-  }
-}
 
 // ------------------------------------------------------------------ dQ from dS
 // One workgroup per (b, h, pair of adjacent 64-row query tiles): four
@@ -457,20 +340,6 @@ hipError_t launch_dq_ds_t(const BwdArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-hipError_t launch_bwd_plan(const BwdArgs& a, bool with_slots, hipStream_t stream) {
-  const int mrows = a.mask.bm * a.mask.hm;
-  hipLaunchKernelGGL(plan_count_kernel, dim3(a.tk, mrows), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, a, (int32_t)(mrows * a.tk));
-  if ((e = hipGetLastError()) != hipSuccess || !with_slots) return e;
-  hipLaunchKernelGGL(plan_slots_kernel, dim3(a.tk, mrows), dim3(256), 0, stream, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_transpose_kernel, dim3((a.tk + 63) / 64, (a.tq + 63) / 64, mrows), dim3(256), 0, stream,
-                     a);
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, bool f32, hipStream_t s) {
   if (head_dim == 128) return f32 ? launch_dq_ds_t<128, true>(a, s) : launch_dq_ds_t<128, false>(a, s);

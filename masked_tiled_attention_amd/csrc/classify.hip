@@ -1,208 +1,172 @@
-// Tile classification pre-pass.
+// Pre-pass kernels: tile classification, launch orders and, for the
+// backward, the row pass and the stored-dS slot plan.
 //
 // The pages do not describe a tile pre-pass; its rule is the reading stated in
-// fm_attn.h (fm_tile_classify). Two kernels:
-//   summary: one workgroup per (bm, hm, key tile) reduces min / max of the four
-//            bound vectors over the tile's columns -> 8 int32;
-//   map:     one thread per (query tile, key tile) applies the rule to the
-//            summary and writes one class byte, row-major in either order.
-// Both are integer-only and bound by launch latency and HBM at these sizes.
+// fm_attn.h (fm_tile_classify). The bodies live in prep.hpp. Forward (and
+// fm_tile_classify):
+//   summary   one workgroup per (mask row, key tile): min / max of the four
+//             bound vectors over the tile's columns -> 8 int32;
+//   map       one workgroup per (mask row, map line): the line's classes from
+//             the summaries, and its non-SKIP count;
+//   order     one workgroup: lines sorted by count, longest first.
+// The backward runs the same steps fused into four launches whose workgroups
+// pick their task by index, since each launch in a chain of dependent ones
+// costs a few microseconds whatever its size.
+// Everything here is integer work bound by launch latency and HBM.
 #include <climits>
 
 #include "fm_device.hpp"
 #include "fm_internal.hpp"
+#include "prep.hpp"
 
 namespace fm {
 namespace {
 
-constexpr int kSumThreads = 256;
-
-__device__ __forceinline__ int wave_min(int x) {
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o, 64));
-  return x;
-}
-__device__ __forceinline__ int wave_max(int x) {
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o, 64));
-  return x;
+__global__ __launch_bounds__(256) void classify_summary_kernel(ClassifyArgs a) {
+  prep::summary_tile(a, blockIdx.x, blockIdx.y);
 }
 
-__global__ __launch_bounds__(kSumThreads) void classify_summary_kernel(ClassifyArgs a) {
-  const int kt = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int bm = bh / a.mask.hm, hm = bh % a.mask.hm;
-  const int64_t base = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
-  const int c0 = kt * a.block_k;
-  const int c1 = min(c0 + a.block_k, a.seq_k);
-
-  // lanes accumulate (min, max) of lts, lte, uts, ute
-  int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-  int mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
-  for (int c = c0 + (int)threadIdx.x; c < c1; c += kSumThreads) {
-    int v[4];
-    if (a.mask.has_lower) {
-      v[0] = a.mask.lts[base + c];
-      v[1] = a.mask.lte[base + c];
-    } else {
-      v[0] = a.seq_q;
-      v[1] = a.seq_q;
-    }
-    if (a.mask.has_upper) {
-      v[2] = a.mask.uts[base + c];
-      v[3] = a.mask.ute[base + c];
-    } else {
-      v[2] = 0;
-      v[3] = 0;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      mn[i] = min(mn[i], v[i]);
-      mx[i] = max(mx[i], v[i]);
-    }
-  }
-  __shared__ int red[kSumThreads / 64][8];
-  const int w = threadIdx.x / 64;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int a0 = wave_min(mn[i]);
-    int a1 = wave_max(mx[i]);
-    if (lane_id() == 0) {
-      red[w][2 * i] = a0;
-      red[w][2 * i + 1] = a1;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < 8) {
-    const int i = threadIdx.x;
-    int r = red[0][i];
-    for (int ww = 1; ww < kSumThreads / 64; ++ww) r = (i & 1) ? max(r, red[ww][i]) : min(r, red[ww][i]);
-    a.summary[((int64_t)bh * a.tk + kt) * 8 + i] = r;
-  }
-}
-
-__device__ __forceinline__ uint8_t classify_one(const int* s, int r0, int r1) {
-  // s: min lts, max lts, min lte, max lte, min uts, max uts, min ute, max ute
-  const bool covers_l = s[1] <= r0 && s[2] >= r1;
-  const bool covers_u = s[5] <= r0 && s[6] >= r1;
-  if (covers_l || covers_u) return (uint8_t)FM_TILE_SKIP;
-  const bool misses_l = s[3] <= r0 || s[0] >= r1;
-  const bool misses_u = s[7] <= r0 || s[4] >= r1;
-  return (uint8_t)((misses_l && misses_u) ? FM_TILE_FULL : FM_TILE_PARTIAL);
-}
-
-// Not transposed: grid (ceil(tk/256), tq, bm*hm); thread -> key tile.
-// Transposed:     grid (ceil(tq/256), tk, bm*hm); thread -> query tile.
+// grid (lines, bm * hm): lines = tq, or tk when transposed
 __global__ __launch_bounds__(256) void classify_map_kernel(ClassifyArgs a) {
-  const int bh = blockIdx.z;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  int qt, kt;
-  if (a.transposed) {
-    kt = blockIdx.y;
-    qt = t;
-    if (qt >= a.tq) return;
-  } else {
-    qt = blockIdx.y;
-    kt = t;
-    if (kt >= a.tk) return;
-  }
-  const int* sp = a.summary + ((int64_t)bh * a.tk + kt) * 8;
-  int s[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s[i] = sp[i];
-  const int r0 = qt * a.block_q;
-  const int r1 = min(r0 + a.block_q, a.seq_q);
-  const uint8_t c = classify_one(s, r0, r1);
-  if (a.transposed)
-    a.classes[((int64_t)bh * a.tk + kt) * a.tq + qt] = c;
-  else
-    a.classes[((int64_t)bh * a.tq + qt) * a.tk + kt] = c;
+  prep::map_line(a, blockIdx.x, blockIdx.y);
 }
 
-// grid (rows): counts[r] = number of non-SKIP entries of class-map line r.
-__global__ __launch_bounds__(256) void order_count_kernel(OrderArgs a) {
-  const int r = blockIdx.x;
-  const uint8_t* line = a.classes + (int64_t)(r / a.inner) * a.outer_stride + (int64_t)(r % a.inner) * a.line_stride;
-  int c = 0;
-  for (int gi = 0; gi < a.group; ++gi)
-    for (int i = threadIdx.x; i < a.len; i += 256) c += line[gi * a.group_stride + i * a.elem_stride] != FM_TILE_SKIP;
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-  __shared__ int red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) a.counts[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+__global__ __launch_bounds__(1024) void order_sort_kernel(OrderArgs a) { prep::sort_lines(a); }
+
+// Backward launch 1: summaries of the dK/dV tiling (ct), then of the dQ
+// tiling (cq).
+__global__ __launch_bounds__(256) void bwd_summaries_kernel(ClassifyArgs ct, ClassifyArgs cq) {
+  const int mrows = ct.mask.bm * ct.mask.hm;
+  const int blk = blockIdx.x;
+  if (blk < ct.tk * mrows) return prep::summary_tile(ct, blk % ct.tk, blk / ct.tk);
+  const int b2 = blk - ct.tk * mrows;
+  prep::summary_tile(cq, b2 % cq.tk, b2 / cq.tk);
 }
 
-// One workgroup of 1024: counting sort of the rows by count, descending, with
-// the counts grouped into at most 4096 buckets (order within a bucket is
-// arbitrary; only the launch order depends on it).
-constexpr int kOrderBuckets = 4096;
-__global__ __launch_bounds__(1024) void order_sort_kernel(OrderArgs a) {
-  __shared__ int hist[kOrderBuckets];
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // a line counts up to len entries in each of its `group` class-map lines
-  const int64_t cmax = (int64_t)a.len * a.group;
-  const int nb = (int)min(cmax + 1, (int64_t)kOrderBuckets);
-  auto key = [&](int r) {   // descending count -> ascending key in [0, nb)
-    const int64_t c = min(max((int64_t)a.counts[r], (int64_t)0), cmax);
-    return nb - 1 - (int)(c * nb / (cmax + 1));
-  };
-  for (int i = tid; i < nb; i += 1024) hist[i] = 0;
-  __syncthreads();
-  for (int r = tid; r < a.rows; r += 1024) atomicAdd(&hist[key(r)], 1);
-  __syncthreads();
-  // exclusive scan: thread t owns buckets 4t .. 4t+3
-  int v[4], s = 0;
+// Backward launch 2: the lines of both class maps (ct transposed: key-tile
+// lines; cq: query-tile lines).
+__global__ __launch_bounds__(256) void bwd_maps_kernel(ClassifyArgs ct, ClassifyArgs cq) {
+  const int mrows = ct.mask.bm * ct.mask.hm;
+  const int blk = blockIdx.x;
+  if (blk < ct.tk * mrows) return prep::map_line(ct, blk % ct.tk, blk / ct.tk);
+  const int b2 = blk - ct.tk * mrows;
+  prep::map_line(cq, b2 % cq.tq, b2 / cq.tq);
+}
+
+// Backward launch 3: workgroup 0 sorts the dK/dV order, 1 the recompute dQ
+// kernel's (when set), and the last one scans the slot offsets (when the
+// plan is set).
+__global__ __launch_bounds__(1024) void bwd_orders_kernel(OrderArgs ok, OrderArgs oq, BwdArgs a) {
+  const int blk = blockIdx.x;
+  if (blk == 0) return prep::sort_lines(ok);
+  if (blk == 1 && oq.order) return prep::sort_lines(oq);
+  prep::scan_slots(a, a.mask.bm * a.mask.hm * a.tk);
+}
+
+// Stored dS: slots_q[mr][qt][kt] = the slot of tile (kt, qt) for non-SKIP
+// tiles (row_off of the key-tile row + non-SKIP tiles before its 64-tile chunk
+// + its rank within the chunk), -1 for SKIP ones. Block (kb, ch, mr) of
+// ceil(tk / 16) x ceil(tq / 64) x mask rows: each wavefront ranks four
+// key-tile rows of a 64-tile chunk (one ballot each); the 16 x 64 block goes
+// out through LDS so that the query-major writes are 64-byte runs.
+__device__ __forceinline__ void slots_block(const BwdArgs& a, int kb, int ch, int mr) {
+  __shared__ int32_t t[16][65];
+  const int kt0 = kb * 16, q0 = ch * 64;
+  const int w = threadIdx.x >> 6, c = threadIdx.x & 63;
+  const int nch = (a.tq + 63) / 64;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int b = 4 * tid + i;
-    v[i] = b < nb ? hist[b] : 0;
-    s += v[i];
-  }
-  int incl = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
-  int pre = incl - s;
-  for (int k = 0; k < wv; ++k) pre += wsum[k];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int b = 4 * tid + i;
-    if (b < nb) hist[b] = pre;
-    pre += v[i];
+  for (int j = 0; j < 4; ++j) {
+    const int r = w + 4 * j, kt = kt0 + r, q = q0 + c;   // kt is uniform per wavefront
+    bool open = false;
+    if (kt < a.tk && q < a.tq) open = a.classes_t[((int64_t)mr * a.tk + kt) * a.tq + q] != FM_TILE_SKIP;
+    const uint64_t bal = __ballot(open);
+    int32_t v = -1;
+    if (open) {
+      const int64_t row = (int64_t)mr * a.tk + kt;
+      const int64_t s = (int64_t)a.row_off[row] + a.chunk_pre[row * nch + ch] + __popcll(bal & ((1ull << c) - 1));
+      v = (int32_t)min(s, (int64_t)INT_MAX);   // beyond INT_MAX the plan disables the store
+    }
+    t[r][c] = v;
   }
   __syncthreads();
-  for (int r = tid; r < a.rows; r += 1024)
-    a.order[atomicAdd(&hist[key(r)], 1)] = (int32_t)((uint32_t)r | (a.mark_empty && a.counts[r] <= 0 ? kEmptyLine : 0u));
+  const int kk = threadIdx.x & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int qq = (threadIdx.x >> 4) + 16 * j, q = q0 + qq, kt = kt0 + kk;
+    if (q < a.tq && kt < a.tk) a.slots_q[((int64_t)mr * a.tq + q) * a.tk + kt] = t[kk][qq];
+  }
+}
+
+// Backward launch 4: n_slots blocks of the slot map (stored dS), then the row
+// pass (D and LSE * log2(e)), which the dK/dV kernel reads next, together with
+// dO.
+template <int D, bool F32>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(BwdArgs a, int n_slots) {
+  const int blk = blockIdx.x;
+  if (blk < n_slots) {
+    const int gx = (a.tk + 15) / 16, gy = (a.tq + 63) / 64;
+    return slots_block(a, blk % gx, (blk / gx) % gy, blk / (gx * gy));
+  }
+  prep::row_stats<D, F32>(a, blk - n_slots);
+}
+
+template <int D, bool F32>
+hipError_t launch_rows_t(const BwdArgs& a, bool slots, bool rows, hipStream_t s) {
+  const int64_t n_slots = slots ? (int64_t)((a.tk + 15) / 16) * ((a.tq + 63) / 64) * a.mask.bm * a.mask.hm : 0;
+  int64_t nblk = n_slots;
+  if (rows) {
+    const int64_t nrows = (int64_t)a.batch * a.seq_pad * a.heads;
+    const int rpb = 256 / (D / 8);
+    nblk += (nrows + rpb - 1) / rpb;
+  }
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_rows_kernel<D, F32>), dim3((unsigned)nblk), dim3(256), 0, s, a, (int)n_slots);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_order(const OrderArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(order_count_kernel, dim3(a.rows), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(order_sort_kernel, dim3(1), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream) {
-  dim3 grid(a.tk, a.mask.bm * a.mask.hm);
-  hipLaunchKernelGGL(classify_summary_kernel, grid, dim3(kSumThreads), 0, stream, a);
+  hipLaunchKernelGGL(classify_summary_kernel, dim3(a.tk, a.mask.bm * a.mask.hm), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_classify_map(const ClassifyArgs& a, hipStream_t stream) {
-  dim3 grid;
-  if (a.transposed)
-    grid = dim3((a.tq + 255) / 256, a.tk, a.mask.bm * a.mask.hm);
-  else
-    grid = dim3((a.tk + 255) / 256, a.tq, a.mask.bm * a.mask.hm);
+  const dim3 grid(a.transposed ? a.tk : a.tq, a.mask.bm * a.mask.hm);
   hipLaunchKernelGGL(classify_map_kernel, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+// Each of these launches does the work of two or more small kernels: each
+// such kernel is far too small to fill the chip, and in a chain of dependent
+// launches each costs a few microseconds whatever its size.
+hipError_t launch_bwd_summaries(const ClassifyArgs& ct, const ClassifyArgs& cq, hipStream_t stream) {
+  const int64_t mrows = (int64_t)ct.mask.bm * ct.mask.hm;
+  hipLaunchKernelGGL(bwd_summaries_kernel, dim3((unsigned)((ct.tk + cq.tk) * mrows)), dim3(256), 0, stream, ct, cq);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_maps(const ClassifyArgs& ct, const ClassifyArgs& cq, hipStream_t stream) {
+  const int64_t mrows = (int64_t)ct.mask.bm * ct.mask.hm;
+  hipLaunchKernelGGL(bwd_maps_kernel, dim3((unsigned)((ct.tk + cq.tq) * mrows)), dim3(256), 0, stream, ct, cq);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_orders(const OrderArgs& ok, const OrderArgs& oq, const BwdArgs& a, hipStream_t stream) {
+  const int nblk = 1 + (oq.order ? 1 : 0) + (a.plan ? 1 : 0);
+  hipLaunchKernelGGL(bwd_orders_kernel, dim3(nblk), dim3(1024), 0, stream, ok, oq, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_rows(const BwdArgs& a, bool slots, bool rows, int head_dim, bool f32, hipStream_t stream) {
+  if (head_dim == 128)
+    return f32 ? launch_rows_t<128, true>(a, slots, rows, stream) : launch_rows_t<128, false>(a, slots, rows, stream);
+  return f32 ? launch_rows_t<64, true>(a, slots, rows, stream) : launch_rows_t<64, false>(a, slots, rows, stream);
 }
 
 }  // namespace fm

@@ -35,6 +35,8 @@ struct ClassifyArgs {
   int32_t* summary;        // [bm][hm][tk][8]
   uint8_t* classes;        // [bm][hm][tq][tk] or [bm][hm][tk][tq]
   int32_t transposed;
+  int32_t* counts;         // nullptr, or [bm][hm][lines] non-SKIP entries per map line
+  int32_t* chunk_pre;      // nullptr, or [bm][hm][lines][ceil(len / 64)] non-SKIP entries before each 64-entry chunk
 };
 
 struct FwdArgs {
@@ -82,22 +84,20 @@ struct VtArgs {
   uint8_t* vt;
 };
 
-// Lines of a class map ordered by their non-SKIP count, descending. Line r
-// (r = mask row * inner + i) holds `len` entries starting at
-// (r / inner) * outer_stride + (r % inner) * line_stride, elem_stride apart:
-// rows of a [mr][inner][len] map or columns of a [mr][len][inner] map.
+// Lines ordered by their non-SKIP count, descending. Line r counts `group`
+// class-map lines of up to `len` entries each, whose counts (from the class
+// map pass) are counts[(r / inner) * outer_stride + (r % inner) +
+// gi * group_stride] for gi < group.
 struct OrderArgs {
-  const uint8_t* classes;
+  const int32_t* counts;
   int32_t rows, len, inner;
-  int64_t outer_stride, line_stride, elem_stride;
-  int32_t group;           // a line counts `group` class-map lines, group_stride apart
+  int64_t outer_stride;
+  int32_t group;
   int64_t group_stride;
-  int32_t* counts;         // [rows] non-SKIP entries per line
   int32_t* order;          // [rows] line indices, longest first
   int32_t mark_empty;      // set: lines with no non-SKIP entry carry kEmptyLine
 };
 constexpr uint32_t kEmptyLine = 0x80000000u;   // order entry flag: the line has no work
-hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
 
 struct BwdArgs {
   const void* q;
@@ -129,9 +129,9 @@ struct BwdArgs {
   // workspace cannot hold the slot map at all.
   int32_t* row_cnt;          // [bm*hm][tk] non-SKIP tiles per key-tile row
   int32_t* row_off;          // [bm*hm][tk] exclusive prefix sums of row_cnt
+  int32_t* chunk_pre;        // [bm*hm][tk][ceil(tq / 64)] non-SKIP tiles of the row before each 64-tile chunk
   int32_t* plan;             // [0] total non-SKIP tiles, [1] 1 if the dS store is in use
-  int32_t* slots;            // [bm*hm][tk][tq] slot of each non-SKIP tile
-  int32_t* slots_q;          // [bm*hm][tq][tk] the same, query-major, -1 for SKIP tiles
+  int32_t* slots_q;          // [bm*hm][tq][tk] slot of each non-SKIP tile, query-major, -1 for SKIP tiles
   uint16_t* ds;              // [rep][total][kBwdBlockK keys][kBwdBlockQ rows] bf16
   int64_t ds_capacity;       // bytes available at ds
   int32_t rep;               // (b, h) pairs per mask row
@@ -162,7 +162,6 @@ __device__ __forceinline__ void ordered_bh(int mr, int j, const MaskArgs& m, int
   *h = m.hm > 1 ? mr % m.hm : j % heads;
 }
 
-hipError_t launch_bwd_plan(const BwdArgs& a, bool with_slots, hipStream_t stream);
 hipError_t launch_bwd_dq_ds(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 
 constexpr int kMaxChunks = 64;
@@ -194,10 +193,23 @@ struct ChunkWorkArgs {
 // Launchers: enqueue on `stream`, return hipGetLastError() of the launch.
 hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream);
 hipError_t launch_classify_map(const ClassifyArgs& a, hipStream_t stream);
+hipError_t launch_order(const OrderArgs& a, hipStream_t stream);
+// Backward pre-passes, fused into four launches:
+//   summaries   the summaries of both tilings;
+//   maps        both class maps with the line counts (row_cnt for the dK/dV
+//               tiling, the dQ tiling's into cq.counts) and, with
+//               ct.chunk_pre set, the chunk prefixes of the dK/dV rows;
+//   orders      the launch orders ok and (oq.order set) oq, and, with
+//               a.plan set, the slot offsets and the plan;
+//   rows        the query-major slot map (`slots`, stored dS) and the row
+//               pass D, LSE * log2(e) (`rows`; needs o, dout, lse).
+hipError_t launch_bwd_summaries(const ClassifyArgs& ct, const ClassifyArgs& cq, hipStream_t stream);
+hipError_t launch_bwd_maps(const ClassifyArgs& ct, const ClassifyArgs& cq, hipStream_t stream);
+hipError_t launch_bwd_orders(const OrderArgs& ok, const OrderArgs& oq, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_rows(const BwdArgs& a, bool slots, bool rows, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_vt(const VtArgs& a, int head_dim, hipStream_t stream);
-hipError_t launch_bwd_pre(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, bool f32, hipStream_t stream);
 hipError_t launch_localize(const LocalizeArgs& a, hipStream_t stream);

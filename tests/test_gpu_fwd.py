@@ -99,6 +99,24 @@ def test_fwd_split_lists(gpu_lib):
                 assert torch.all(o[:, 100:160] == 0) and torch.all(lse[:, :, 100:160] == -math.inf)
 
 
+def test_fwd_split_lists_ragged_rows_repeated(gpu_lib):
+    """Split lists with a ragged last query tile (200 rows: tiles of 128 and
+    72 rows), called twice on one workspace: nothing from the first call's
+    partials leaks into the second, and both calls give the same bits."""
+    rng = np.random.default_rng(6)
+    sq, sk = 200, 65536
+    vec = tuple(rng.integers(-20, sq + 20, (1, 1, sk)).astype(np.int32) for _ in range(4))
+    q, k, v = ST.qkv(1, sq, sk, 3, 128, seed=86)
+    o, lse = _compare_fwd(gpu_lib, q, k, v, vec, 0.088, "split ragged rows")
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    m = dev_mask(vec)
+    ws = torch.empty(gpu_lib.fm_workspace_size(qd, kd, vd, m, False), dtype=torch.uint8, device="cuda")
+    outs = [gpu_lib.fm_attn_fwd(qd, kd, vd, m, 0.088, workspace=ws) for _ in range(2)]
+    torch.cuda.synchronize()
+    for o2, l2 in outs:
+        assert torch.equal(o2.cpu(), o) and torch.equal(l2.cpu(), lse)
+
+
 def test_fwd_fully_masked_rows_and_tiles(gpu_lib):
     """Rows 100..299 see no key at all: whole query tiles are SKIP everywhere."""
     n = 600
