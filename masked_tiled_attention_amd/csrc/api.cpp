@@ -267,8 +267,8 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t
     L.plan = off;
     off = align256(off + 16);
     const int64_t tq_q = ceil_div(p->seqlen_q, fm::kDqBlockQ);
-    L.order_k = off;   // the counts are row_cnt
-    off = align256(off + (size_t)(mrows * tk * 4));
+    L.order_k = off;   // the counts are row_cnt; then the number of lines with work
+    off = align256(off + (size_t)(mrows * tk * 4) + 4);
     L.order_qq = off;
     off = align256(off + (size_t)(mrows * tq_q * 8));
     L.dq_split = dq_split(p);
@@ -434,6 +434,7 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   ok.group_stride = tk;
   ok.order = reinterpret_cast<int32_t*>(w + L.order_k);
   ok.mark_empty = 1;
+  ok.live = ok.order + ok.rows;
   fm::OrderArgs oq{};
   if (!size_query && ws_bytes < L.ds) {
     oq.counts = counts_q;
@@ -446,6 +447,7 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   e = run_stage(FM_STAGE_ORDER, stream, [&] { return fm::launch_bwd_orders(ok, oq, a, stream); });
   if (e != hipSuccess) return hip_fail(e, "backward order launch");
   a.order_k = ok.order;
+  a.order_live = ok.live;
   a.order_qq = oq.order;
   if (maybe_ds || rows) {
     e = run_stage(FM_STAGE_BWD_PRE, stream,

@@ -61,6 +61,7 @@ constexpr int BK = kBwdBlockK;   // 128 keys per workgroup
 constexpr int WAVES = 8;         // 4 key groups x (P, dS)
 constexpr int THREADS = WAVES * 64;
 constexpr int NBUF = 3;          // query tiles in LDS
+constexpr int kZeroShare = 4;    // empty lines written per workgroup with work, at most
 
 template <int D>
 struct alignas(16) Smem {
@@ -105,9 +106,15 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   const int split = GROUPED && a.part != nullptr;
   const int rep = split ? a.rep_kv * a.group : a.rep_kv;
   const uint32_t ent = (uint32_t)__builtin_amdgcn_readfirstlane(a.order_k[blockIdx.x / rep]);
-  // A line whose key tile no query tile sees (flagged by the order sort): its
-  // dK and dV are zero, written by the epilogue without loading anything.
+  // A line whose key tile no query tile sees (flagged by the order sort, which
+  // puts those lines last): its dK and dV are zero. The first kZeroShare
+  // workgroups' worth of them are written by the workgroups with work (each
+  // takes up to kZeroShare, strided), so that the stores drain while those
+  // run; the workgroups of such lines end at once. Any others write their own.
+  const int64_t busy = (int64_t)__builtin_amdgcn_readfirstlane(*a.order_live) * rep;
+  const int64_t zeros = min((int64_t)gridDim.x - busy, kZeroShare * busy);   // lines zeroed by others
   const bool empty = (ent & kEmptyLine) != 0;
+  if (empty && (int64_t)blockIdx.x - busy < zeros) return;
   const int line = (int)(ent & ~kEmptyLine);   // K/V mask row * tk + key tile
   // (integer divisions by launch constants expand to vector code: the results
   // are taken back to scalar registers so that the addresses stay scalar)
@@ -119,12 +126,43 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   const int b = __builtin_amdgcn_readfirstlane(a.mask.bm > 1 ? kr / hkm : jr / (a.mask.hm > 1 ? 1 : a.heads_kv));
   const int hk = __builtin_amdgcn_readfirstlane(a.mask.hm > 1 ? kr % hkm : jr % a.heads_kv);
   const int bm = __builtin_amdgcn_readfirstlane(kr / hkm);
+  constexpr int ES = F32 ? 4 : 2;
+
+  // workgroup i with work writes the zeros of the empty workgroups busy + j,
+  // j = i, i + busy, ... below zeros: dK then dV rows of the line's 128 keys,
+  // 16 bytes per lane
+  for (int64_t j = blockIdx.x; j < zeros; j += busy) {
+    const int64_t wg = busy + j;
+    const int zl = (int)((uint32_t)__builtin_amdgcn_readfirstlane(a.order_k[wg / rep]) & ~kEmptyLine);
+    const int zkt = __builtin_amdgcn_readfirstlane(zl % a.tk);
+    const int zkr = __builtin_amdgcn_readfirstlane(zl / a.tk);
+    const int zjr = __builtin_amdgcn_readfirstlane((int)((wg % rep) / (split ? a.group : 1)));
+    const int zg = __builtin_amdgcn_readfirstlane(split ? (int)(wg % a.group) : 0);
+    const int zb = __builtin_amdgcn_readfirstlane(a.mask.bm > 1 ? zkr / hkm : zjr / (a.mask.hm > 1 ? 1 : a.heads_kv));
+    const int zh = __builtin_amdgcn_readfirstlane(a.mask.hm > 1 ? zkr % hkm : zjr % a.heads_kv);
+    const int lc = split ? __builtin_ctz(D * 4 / 16) : __builtin_ctz(D * ES / 16);   // log2 of chunks per row
+    for (int c = tid; c < (2 * BK) << lc; c += THREADS) {
+      const int row = c >> lc, ch = c & ((1 << lc) - 1);
+      const bool is_k = row < BK;
+      const int nz = zkt * BK + (row & (BK - 1));
+      if (nz >= a.seq_k) continue;
+      char* out;
+      if (split) {   // float32 partials [2][B][H][Sk][D]: dK, then dV
+        out = reinterpret_cast<char*>(a.part + (is_k ? 0 : (int64_t)a.batch * a.heads * a.seq_k * D) +
+                                      (((int64_t)zb * a.heads + zh * a.group + zg) * a.seq_k + nz) * D);
+      } else {
+        const int64_t off = is_k ? (int64_t)zb * a.k_sb + (int64_t)nz * a.k_ss + (int64_t)zh * a.k_sh
+                                 : (int64_t)zb * a.v_sb + (int64_t)nz * a.v_ss + (int64_t)zh * a.v_sh;
+        out = reinterpret_cast<char*>(is_k ? a.dk : a.dv) + off * ES;
+      }
+      *reinterpret_cast<u32x4*>(out + 16 * ch) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 
   const int n = kt * BK + 32 * kg + lr;   // this lane's key
   const bool key_ok = n < a.seq_k;
   const bool ragged_k = (a.seq_k % BK) != 0 && kt == a.tk - 1;
   const bool store_ds = a.plan != nullptr && a.plan[1] != 0;
-  constexpr int ES = F32 ? 4 : 2;
 
   // ---- the lane's key row as MFMA B operands, once: K for the P wavefront,
   // V for the dS wavefront, channels 16 s + 8 g .. + 7 in step s (keys past

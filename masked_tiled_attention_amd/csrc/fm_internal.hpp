@@ -95,7 +95,8 @@ struct OrderArgs {
   int32_t group;
   int64_t group_stride;
   int32_t* order;          // [rows] line indices, longest first
-  int32_t mark_empty;      // set: lines with no non-SKIP entry carry kEmptyLine
+  int32_t mark_empty;      // set: lines with no non-SKIP entry carry kEmptyLine and go last
+  int32_t* live;           // with mark_empty, optional: the number of lines before the empty ones
 };
 constexpr uint32_t kEmptyLine = 0x80000000u;   // order entry flag: the line has no work
 
@@ -142,7 +143,8 @@ struct BwdArgs {
   int32_t rep_kv;
   // Launch orders, longest first (see FwdArgs::order): key tiles of the dK/dV
   // tiling and the recompute dQ kernel's query tiles (may be nullptr).
-  const int32_t* order_k;   // key-tile lines longest first; empty lines flagged with kEmptyLine
+  const int32_t* order_k;   // key-tile lines longest first; empty lines flagged with kEmptyLine, last
+  const int32_t* order_live;   // the number of order_k lines before the empty ones
   const int32_t* order_qq;
   // Grouped-query attention with a mask shared by all heads: one dK/dV
   // workgroup per query head, float32 partials [2][B][H][Sk][D] (dK, then dV)

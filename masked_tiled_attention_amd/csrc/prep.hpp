@@ -161,15 +161,19 @@ __device__ __forceinline__ void sort_lines(const OrderArgs& a) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t cmax = (int64_t)a.len * a.group;
-  const int nb = (int)min(cmax + 1, (int64_t)kOrderBuckets);
+  // with mark_empty, lines with no work take a bucket of their own, the last
+  const int nb = (int)min(cmax + 1, (int64_t)kOrderBuckets - (a.mark_empty ? 1 : 0));
+  const int nbt = nb + (a.mark_empty ? 1 : 0);
   auto count = [&](int r) {
     const int64_t at = (int64_t)(r / a.inner) * a.outer_stride + r % a.inner;
     int64_t c = 0;
     for (int gi = 0; gi < a.group; ++gi) c += a.counts[at + gi * a.group_stride];
     return min(max(c, (int64_t)0), cmax);
   };
-  auto key = [&](int64_t c) { return nb - 1 - (int)(c * nb / (cmax + 1)); };   // descending count
-  for (int i = tid; i < nb; i += 1024) hist[i] = 0;
+  auto key = [&](int64_t c) {   // descending count
+    return a.mark_empty && c == 0 ? nb : nb - 1 - (int)(c * nb / (cmax + 1));
+  };
+  for (int i = tid; i < nbt; i += 1024) hist[i] = 0;
   __syncthreads();
   for (int r = tid; r < a.rows; r += 1024) atomicAdd(&hist[key(count(r))], 1);
   __syncthreads();
@@ -178,7 +182,7 @@ __device__ __forceinline__ void sort_lines(const OrderArgs& a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = 4 * tid + i;
-    v[i] = b < nb ? hist[b] : 0;
+    v[i] = b < nbt ? hist[b] : 0;
     sum += v[i];
   }
   int incl = sum;
@@ -194,7 +198,8 @@ __device__ __forceinline__ void sort_lines(const OrderArgs& a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int b = 4 * tid + i;
-    if (b < nb) hist[b] = pre;
+    if (b < nbt) hist[b] = pre;
+    if (a.live != nullptr && b == nbt - 1) *a.live = pre;   // lines before the empty ones
     pre += v[i];
   }
   __syncthreads();
