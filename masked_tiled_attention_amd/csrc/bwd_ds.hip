@@ -306,7 +306,7 @@ void bwd_dq_ds_kernel(BwdArgs a) {
 // Split lists: dQ = the sum of the parts' float32 partials (fixed order), one
 // thread per 4 channels of one row. Exits when the plan chose the recompute
 // path.
-template <int D, bool F32>
+template <int D, bool F32, int KS>
 __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a) {
   if (a.plan == nullptr || a.plan[1] == 0) return;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // ((b * H + h) * Sq + m) * D / 4 + c4
@@ -314,8 +314,14 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a) {
   if (i >= rows * (D / 4)) return;
   const int64_t r = i / (D / 4);
   const int c0 = (int)(i % (D / 4)) * 4;
-  f32x4 x = f32x4{};
-  for (int s = 0; s < a.dq_split; ++s) x += *reinterpret_cast<const f32x4*>(a.dqpart + (s * rows + r) * D + c0);
+  // KS (the part count) is a compile-time constant so that every part's load
+  // goes out before the sum
+  f32x4 y[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) y[s] = *reinterpret_cast<const f32x4*>(a.dqpart + (s * rows + r) * D + c0);
+  f32x4 x = y[0];
+#pragma unroll
+  for (int s = 1; s < KS; ++s) x += y[s];
   const int m = (int)(r % a.seq_q);
   const int h = (int)((r / a.seq_q) % a.heads);
   const int b = (int)(r / ((int64_t)a.seq_q * a.heads));
@@ -330,12 +336,16 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(BwdArgs a) {
 template <int D, bool F32>
 hipError_t launch_dq_ds_t(const BwdArgs& a, hipStream_t s) {
   const int ks = a.dq_split > 1 ? a.dq_split : 1;
+  if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return hipErrorInvalidValue;
   const int npair = (a.tq + PAIR - 1) / PAIR;
   hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F32>), dim3(npair * a.batch * a.heads * ks), dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   const int64_t n = (int64_t)a.batch * a.heads * a.seq_q * (D / 4);
-  hipLaunchKernelGGL((dq_merge_kernel<D, F32>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (ks == 2) hipLaunchKernelGGL((dq_merge_kernel<D, F32, 2>), grid, dim3(256), 0, s, a);
+  else if (ks == 4) hipLaunchKernelGGL((dq_merge_kernel<D, F32, 4>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((dq_merge_kernel<D, F32, 8>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

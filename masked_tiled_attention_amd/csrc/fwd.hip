@@ -375,27 +375,37 @@ void fwd_kernel(FwdArgs a) {
 // Split lists: O and LSE of each row from the parts' normalised partial O_s
 // and LSE_s: LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the
 // parts' softmax weights). A row no part sees keeps O = 0, LSE = -inf. One
-// thread per 4 channels of one row.
-template <int D, bool F32>
+// thread per 4 channels of one row; KS (the part count) is a compile-time
+// constant so that every part's loads go out before any is used.
+template <int D, bool F32, int KS>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // ((b * H + h) * Sq + m) * D / 4 + c4
   const int64_t rows = (int64_t)a.batch * a.heads * a.seq_q;
   if (i >= rows * (D / 4)) return;
   const int64_t r = i / (D / 4);
   const int c0 = (int)(i % (D / 4)) * 4;
-  float mx = -INFINITY;
-  for (int s = 0; s < a.ksplit; ++s) mx = fmaxf(mx, a.lpart[s * rows + r]);
-  f32x4 o = f32x4{};
-  float lse = -INFINITY;
-  if (mx > -INFINITY) {
-    float sum = 0.f;
-    for (int s = 0; s < a.ksplit; ++s) sum += __expf(a.lpart[s * rows + r] - mx);
-    lse = mx + __logf(sum);
-    for (int s = 0; s < a.ksplit; ++s) {
-      const float ws = __expf(a.lpart[s * rows + r] - lse);
-      o += ws * *reinterpret_cast<const f32x4*>(a.opart + (s * rows + r) * D + c0);
-    }
+  float lp[KS];
+  f32x4 op[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    lp[s] = a.lpart[s * rows + r];
+    op[s] = *reinterpret_cast<const f32x4*>(a.opart + (s * rows + r) * D + c0);
   }
+  // no branch (it would hold the O loads back behind the LSE loads): with no
+  // part seeing the row every weight is exp(-inf) = 0 against a zero reference
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) mx = fmaxf(mx, lp[s]);
+  const bool seen = mx > -INFINITY;
+  const float mref = seen ? mx : 0.f;
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) sum += __expf(lp[s] - mref);
+  const float lse = seen ? mref + __logf(sum) : -INFINITY;
+  const float lref = seen ? lse : 0.f;
+  f32x4 o = f32x4{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) o += __expf(lp[s] - lref) * op[s];
   const int m = (int)(r % a.seq_q);
   const int h = (int)((r / a.seq_q) % a.heads);
   const int b = (int)(r / ((int64_t)a.seq_q * a.heads));
@@ -411,12 +421,16 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a) {
 template <int D, bool F32>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int ks = a.ksplit > 1 ? a.ksplit : 1;
+  if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return hipErrorInvalidValue;
   const int nblk = a.tq * a.batch * a.heads * ks;
   hipLaunchKernelGGL((fwd_kernel<D, F32>), dim3(nblk), dim3(NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   const int64_t n = (int64_t)a.batch * a.heads * a.seq_q * (D / 4);
-  hipLaunchKernelGGL((fwd_merge_kernel<D, F32>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (ks == 2) hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 2>), grid, dim3(256), 0, stream, a);
+  else if (ks == 4) hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 4>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 8>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
