@@ -227,15 +227,16 @@ int32_t dq_split(const fm_problem* p) {
 }
 
 // The same for the query tiles of the bf16 / float32 forward (two workgroups
-// per CU): the count doubles (up to 8) while the split launch stays within
-// 2048 workgroups and each part keeps at least 64 key tiles of 64 keys.
+// per CU, 512 at once): as many parts (up to 8) as keep the split launch
+// within about three rounds of the 512, 1536 workgroups, and each part at
+// least 64 key tiles of 64 keys. Each round costs every workgroup its fixed
+// start and end, and each part a float32 partial row to write and merge, so
+// three rounds measured better than four on the context-parallel rank share.
 int32_t fwd_split(const fm_problem* p) {
   if (p->dtype == FM_FP8_E4M3) return 1;
   const int64_t nwg = ceil_div(p->seqlen_q, fm::kFwdBlockQ) * p->batch * p->heads;
   const int64_t tk = ceil_div(p->seqlen_k, fm::kFwdBlockK);
-  int32_t ks = 1;
-  while (ks < 8 && nwg * 2 * ks <= 2048 && tk >= 128 * ks) ks *= 2;
-  return ks;
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>({8, 1536 / nwg, tk / 64}));
 }
 
 // max_split caps the forward's list parts (1: no split partials).

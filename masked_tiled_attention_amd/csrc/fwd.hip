@@ -421,16 +421,22 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a) {
 template <int D, bool F32>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int ks = a.ksplit > 1 ? a.ksplit : 1;
-  if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return hipErrorInvalidValue;
+  if (ks > 8) return hipErrorInvalidValue;
   const int nblk = a.tq * a.batch * a.heads * ks;
   hipLaunchKernelGGL((fwd_kernel<D, F32>), dim3(nblk), dim3(NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   const int64_t n = (int64_t)a.batch * a.heads * a.seq_q * (D / 4);
   const dim3 grid((unsigned)((n + 255) / 256));
-  if (ks == 2) hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 2>), grid, dim3(256), 0, stream, a);
-  else if (ks == 4) hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 4>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 8>), grid, dim3(256), 0, stream, a);
+  switch (ks) {
+    case 2: hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 2>), grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 3>), grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 4>), grid, dim3(256), 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 5>), grid, dim3(256), 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 6>), grid, dim3(256), 0, stream, a); break;
+    case 7: hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 7>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((fwd_merge_kernel<D, F32, 8>), grid, dim3(256), 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -99,6 +99,29 @@ def test_fwd_split_lists(gpu_lib):
                 assert torch.all(o[:, 100:160] == 0) and torch.all(lse[:, :, 100:160] == -math.inf)
 
 
+@pytest.mark.parametrize("parts,sq,heads,sk", [(3, 1280, 40, 12288), (5, 1280, 30, 20480),
+                                                (6, 1024, 32, 24576), (7, 1280, 20, 28672)])
+def test_fwd_split_part_counts(gpu_lib, parts, sq, heads, sk):
+    """Part counts that are not powers of two. The library cuts each list
+    into min(8, 1536 // workgroups) parts (at most one per 64 key tiles), so
+    these shapes take 3, 5, 6 and 7 parts (each count is a merge kernel of its
+    own). Random bounds give PARTIAL tiles and uneven parts. Eight rows of
+    every query tile of every head against the oracle, O and LSE."""
+    nwg = -(-sq // 128) * heads
+    assert min(8, 1536 // nwg, -(-sk // 64) // 64) == parts
+    rng = np.random.default_rng(100 + parts)
+    vec = tuple(rng.integers(-20, sq + 20, (1, 1, sk)).astype(np.int32) for _ in range(4))
+    q, k, v = ST.qkv(1, sq, sk, heads, 64, seed=110 + parts)
+    log(f"fwd {parts} parts: q={tuple(q.shape)} k={tuple(k.shape)}")
+    o, lse = _run_fwd(gpu_lib, q, k, v, vec, 0.125)
+    rows = np.concatenate([t + np.array([0, 1, 31, 64, 95, 100, 126, 127]) for t in range(0, sq, 128)])
+    qn, kn, vn = np64(q), np64(k), np64(v)
+    for h in range(heads):
+        ro, rl = OA.forward_rows(qn, kn, vn, vec, 0.125, 0, h, rows)
+        assert_close(np64(o)[0, rows, h], ro, f"{parts} parts head {h} O")
+        assert_close(lse[0, h, rows].double().numpy(), rl, f"{parts} parts head {h} LSE")
+
+
 def test_fwd_split_lists_ragged_rows_repeated(gpu_lib):
     """Split lists with a ragged last query tile (200 rows: tiles of 128 and
     72 rows), called twice on one workspace: nothing from the first call's
