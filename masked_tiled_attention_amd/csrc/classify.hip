@@ -4,8 +4,9 @@
 // The pages do not describe a tile pre-pass; its rule is the reading stated in
 // fm_attn.h (fm_tile_classify). The bodies live in prep.hpp. Forward (and
 // fm_tile_classify):
-//   summary   one workgroup per (mask row, key tile): min / max of the four
-//             bound vectors over the tile's columns -> 8 int32;
+//   summary   one wavefront per (mask row, key tile), four per workgroup:
+//             min / max of the four bound vectors over the tile's columns
+//             -> 8 int32;
 //   map       one workgroup per (mask row, map line): the line's classes from
 //             the summaries, and its non-SKIP count;
 //   order     one workgroup: lines sorted by count, longest first.
@@ -22,8 +23,10 @@
 namespace fm {
 namespace {
 
+// grid (ceil(tk / 4), bm * hm): wavefront w takes key tile 4 * blockIdx.x + w
 __global__ __launch_bounds__(256) void classify_summary_kernel(ClassifyArgs a) {
-  prep::summary_tile(a, blockIdx.x, blockIdx.y);
+  const int kt = 4 * blockIdx.x + (int)(threadIdx.x >> 6);
+  if (kt < a.tk) prep::summary_tile(a, kt, blockIdx.y);
 }
 
 // grid (lines, bm * hm): lines = tq, or tk when transposed
@@ -35,12 +38,13 @@ __global__ __launch_bounds__(1024) void order_sort_kernel(OrderArgs a) { prep::s
 
 // Backward launch 1: summaries of the dK/dV tiling (ct), then of the dQ
 // tiling (cq).
+// (one wavefront per tile, four per workgroup)
 __global__ __launch_bounds__(256) void bwd_summaries_kernel(ClassifyArgs ct, ClassifyArgs cq) {
   const int mrows = ct.mask.bm * ct.mask.hm;
-  const int blk = blockIdx.x;
-  if (blk < ct.tk * mrows) return prep::summary_tile(ct, blk % ct.tk, blk / ct.tk);
-  const int b2 = blk - ct.tk * mrows;
-  prep::summary_tile(cq, b2 % cq.tk, b2 / cq.tk);
+  const int t = 4 * blockIdx.x + (int)(threadIdx.x >> 6);
+  if (t < ct.tk * mrows) return prep::summary_tile(ct, t % ct.tk, t / ct.tk);
+  const int t2 = t - ct.tk * mrows;
+  if (t2 < cq.tk * mrows) prep::summary_tile(cq, t2 % cq.tk, t2 / cq.tk);
 }
 
 // Backward launch 2: the lines of both class maps (ct transposed: key-tile
@@ -132,7 +136,7 @@ hipError_t launch_order(const OrderArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_classify_summary(const ClassifyArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(classify_summary_kernel, dim3(a.tk, a.mask.bm * a.mask.hm), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(classify_summary_kernel, dim3((a.tk + 3) / 4, a.mask.bm * a.mask.hm), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -147,7 +151,8 @@ hipError_t launch_classify_map(const ClassifyArgs& a, hipStream_t stream) {
 // launches each costs a few microseconds whatever its size.
 hipError_t launch_bwd_summaries(const ClassifyArgs& ct, const ClassifyArgs& cq, hipStream_t stream) {
   const int64_t mrows = (int64_t)ct.mask.bm * ct.mask.hm;
-  hipLaunchKernelGGL(bwd_summaries_kernel, dim3((unsigned)((ct.tk + cq.tk) * mrows)), dim3(256), 0, stream, ct, cq);
+  hipLaunchKernelGGL(bwd_summaries_kernel, dim3((unsigned)(((ct.tk + cq.tk) * mrows + 3) / 4)), dim3(256), 0, stream,
+                     ct, cq);
   return hipGetLastError();
 }
 

@@ -29,19 +29,20 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
-// 256 threads: min and max of the four bound vectors over the columns of key
+// One wavefront: min and max of the four bound vectors over the columns of key
 // tile kt of mask row bh -> summary[bh][kt][8] (min lts, max lts, min lte, max
 // lte, min uts, max uts, min ute, max ute). A missing pair reads as the empty
 // interval [Sq, Sq) (lower) or [0, 0) (upper).
 __device__ __forceinline__ void summary_tile(const ClassifyArgs& a, int kt, int bh) {
-  __shared__ int red[4][8];
+  // one wavefront per tile (a workgroup's wavefronts take consecutive tiles)
+  const int lane = (int)(threadIdx.x & 63);
   const int bm = bh / a.mask.hm, hm = bh % a.mask.hm;
   const int64_t base = (int64_t)bm * a.mask.stride_b + (int64_t)hm * a.mask.stride_h;
   const int c0 = kt * a.block_k;
   const int c1 = min(c0 + a.block_k, a.seq_k);
   int mn[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
   int mx[4] = {INT_MIN, INT_MIN, INT_MIN, INT_MIN};
-  for (int c = c0 + (int)threadIdx.x; c < c1; c += 256) {
+  for (int c = c0 + lane; c < c1; c += 64) {
     int v[4];
     if (a.mask.has_lower) {
       v[0] = a.mask.lts[base + c];
@@ -63,23 +64,14 @@ __device__ __forceinline__ void summary_tile(const ClassifyArgs& a, int kt, int 
       mx[i] = max(mx[i], v[i]);
     }
   }
-  const int w = threadIdx.x / 64;
+  int r = 0;   // lane i < 8 keeps summary value i
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int a0 = wave_min(mn[i]);
     const int a1 = wave_max(mx[i]);
-    if (lane_id() == 0) {
-      red[w][2 * i] = a0;
-      red[w][2 * i + 1] = a1;
-    }
+    r = lane == 2 * i ? a0 : (lane == 2 * i + 1 ? a1 : r);
   }
-  __syncthreads();
-  if (threadIdx.x < 8) {
-    const int i = threadIdx.x;
-    int r = red[0][i];
-    for (int ww = 1; ww < 4; ++ww) r = (i & 1) ? max(r, red[ww][i]) : min(r, red[ww][i]);
-    a.summary[((int64_t)bh * a.tk + kt) * 8 + i] = r;
-  }
+  if (lane < 8) a.summary[((int64_t)bh * a.tk + kt) * 8 + lane] = r;
 }
 
 // The class of query rows [r0, r1) against a key tile with summary s: SKIP
