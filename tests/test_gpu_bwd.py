@@ -177,6 +177,26 @@ def test_bwd_key_tiles_masked_for_every_row(gpu_lib):
     _compare_ds(gpu_lib, q, k, v, do, vec, 1 / math.sqrt(d), "dead key tiles, stored dS")
 
 
+@pytest.mark.parametrize("hkv", [2, 1])
+def test_bwd_mostly_dead_key_tiles(gpu_lib, hkv):
+    """Only keys [0, 200) are open (causal among them), so 30 of the 32
+    key tiles of 128 keys have no non-SKIP tile. The workgroups with work
+    write the zeros of up to four empty key tiles each and the remaining
+    empty ones write their own, so both kinds run. 2 query heads on hkv K/V
+    heads (one K/V head: float32 partials per query head, summed afterwards);
+    both workspaces."""
+    sq, sk, H, d = 256, 4096, 2, 128
+    j = np.arange(sk)
+    vec = tuple(np.ascontiguousarray(x.astype(np.int32)[None, None]) for x in (
+        np.where(j < 200, sq, 0), np.full(sk, sq), np.zeros(sk), np.where(j < 200, j, 0)))
+    q, k, v, do = ST.qkv(1, sq, sk, H, d, seed=43, with_do=True)
+    k, v = k[:, :, :hkv].contiguous(), v[:, :, :hkv].contiguous()
+    _, dk, dv = _compare(gpu_lib, q, k, v, do, vec, 1 / math.sqrt(d), f"dead key tiles, {hkv} K/V heads")
+    assert torch.all(dk[:, 200:] == 0) and torch.all(dv[:, 200:] == 0)
+    # (dK, dV of the stored-dS backward equal those of the recompute one, bit for bit)
+    _compare_ds(gpu_lib, q, k, v, do, vec, 1 / math.sqrt(d), f"dead key tiles, {hkv} K/V heads, stored dS")
+
+
 def test_bwd_stored_ds_more_key_tiles_than_one_list(gpu_lib):
     """140,000 keys: 1094 key tiles, more than one compacted list of the dQ
     kernel, which then walks its key tiles in two passes. With so few query
