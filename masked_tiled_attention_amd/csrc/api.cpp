@@ -191,6 +191,7 @@ struct Layout {
   size_t counts = 0, order = 0;   // forward launch order
   size_t vt = 0;                   // FP8 forward: V^T tiles [B][H_kv][Tk][8 KiB]
   size_t order_k = 0, order_qq = 0;   // backward launch orders (dQ: its counts, then the order)
+  size_t first_k = 0;                 // dK/dV kernel: the first list entry per key-tile line
   size_t part = 0;                     // split-head dK/dV partials (0: not used)
   size_t opart = 0, lpart = 0;         // split-list forward partials (0: not used)
   int32_t ksplit = 1;
@@ -270,6 +271,8 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t
     const int64_t tq_q = ceil_div(p->seqlen_q, fm::kDqBlockQ);
     L.order_k = off;   // the counts are row_cnt; then the number of lines with work
     off = align256(off + (size_t)(mrows * tk * 4) + 4);
+    L.first_k = off;   // the first list entry of each key-tile line
+    off = align256(off + (size_t)(mrows * tk * 4));
     L.order_qq = off;
     off = align256(off + (size_t)(mrows * tq_q * 8));
     L.dq_split = dq_split(p);
@@ -412,6 +415,8 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   fm::ClassifyArgs ct = classify_args(mk, p->seqlen_q, p->seqlen_k, fm::kBwdBlockQ, fm::kBwdBlockK, 1,
                                       reinterpret_cast<int32_t*>(w + L.summary), classes_t, a.row_cnt);
   ct.chunk_pre = a.chunk_pre;
+  ct.first = reinterpret_cast<int32_t*>(w + L.first_k);
+  a.first_k = ct.first;
   const fm::ClassifyArgs cq = classify_args(mk, p->seqlen_q, p->seqlen_k, fm::kDqBlockQ, fm::kDqBlockK, 0,
                                             reinterpret_cast<int32_t*>(w + L.summary_q), classes_q, counts_q);
   hipError_t e = run_stage(FM_STAGE_CLASSIFY_SUMMARY, stream, [&] { return fm::launch_bwd_summaries(ct, cq, stream); });

@@ -61,6 +61,7 @@ constexpr int BK = kBwdBlockK;   // 128 keys per workgroup
 constexpr int WAVES = 8;         // 4 key groups x (P, dS)
 constexpr int THREADS = WAVES * 64;
 constexpr int NBUF = 3;          // query tiles in LDS
+constexpr int QCAP = kBwdListCap;   // query tiles compacted per list pass (2 per thread)
 constexpr int kZeroShare = 4;    // empty lines written per workgroup with work, at most
 
 template <int D>
@@ -69,8 +70,8 @@ struct alignas(16) Smem {
   uint16_t dout[NBUF][BQ * D];   // dO tiles
   float lse2[NBUF][BQ];          // LSE * log2(e); +inf for rows that see nothing / past the end
   float dd[NBUF][BQ];            // D = rowsum(dO * O)
-  uint32_t list[LIST_CAP];
-  uint16_t rank[LIST_CAP];       // ascending rank of each list entry (stored-dS slot)
+  uint32_t list[QCAP];
+  uint16_t rank[QCAP];           // ascending rank of each list entry (stored-dS slot)
   // per key group, two buffers of 4 KiB: the bf16 P of one query tile (64 rows
   // x 32 keys in MFMA operand order), then the dS wavefront's store staging
   uint16_t xch[4][2][BQ * 32];
@@ -116,6 +117,8 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   const bool empty = (ent & kEmptyLine) != 0;
   if (empty && (int64_t)blockIdx.x - busy < zeros) return;
   const int line = (int)(ent & ~kEmptyLine);   // K/V mask row * tk + key tile
+  // (without a head loop the line is also the class column's mask row and key tile)
+  const int first_q = !GROUPED && a.first_k != nullptr ? __builtin_amdgcn_readfirstlane(a.first_k[line]) : -1;
   // (integer divisions by launch constants expand to vector code: the results
   // are taken back to scalar registers so that the addresses stay scalar)
   const int kt = __builtin_amdgcn_readfirstlane(line % a.tk);
@@ -489,14 +492,24 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
       dbh = reinterpret_cast<const char*>(a.dout) + ((int64_t)b * a.o_sb + (int64_t)h * a.o_sh) * ES;
     }
     const int head_base = it_global;   // non-SKIP tiles of earlier heads
-    for (int qt0 = 0; qt0 < a.tq; qt0 += LIST_CAP) {
+    // Without a head loop, the first list entry is known from the class map
+    // pass: its tile loads go out before the list is compacted.
+    bool prestaged = false;
+    if constexpr (!GROUPED) {
+      if (first_q >= 0) {
+        stage_q(first_q, it_global % NBUF);
+        prestaged = true;
+      }
+    }
+    for (int qt0 = 0; qt0 < a.tq; qt0 += QCAP) {
       int n_full;
-      const int n_list = compact_classes_split<LIST_CAP, THREADS>(ccol, qt0, min(LIST_CAP, a.tq - qt0), sm.list,
-                                                                  sm.rank, sm.scan, tid, ragged_k, &n_full);
+      const int n_list = compact_classes_split<QCAP, THREADS>(ccol, qt0, min(QCAP, a.tq - qt0), sm.list,
+                                                              sm.rank, sm.scan, tid, ragged_k, &n_full);
       if (n_list == 0) continue;
       const int base = it_global;
       const int pass_base = base - head_base;   // this head's non-SKIP tiles in earlier passes
-      stage_q((int)(sm.list[0] & ~kPartialBit), base % NBUF);
+      if (!prestaged) stage_q((int)(sm.list[0] & ~kPartialBit), base % NBUF);
+      prestaged = false;
 
       // Iteration it: the P wavefronts take list entry it, the dS wavefronts
       // entry it - 1. FULL entries come first, then PARTIAL ones (only the P

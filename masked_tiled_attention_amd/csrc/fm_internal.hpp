@@ -14,6 +14,7 @@ constexpr int kFwdBlockQ = 128;
 constexpr int kFwdBlockK = 64;
 constexpr int kBwdBlockQ = 64;    // dK/dV kernel: query rows per inner tile
 constexpr int kBwdBlockK = 128;   // dK/dV kernel: keys per workgroup
+constexpr int kBwdListCap = 1024;  // dK/dV kernel: query tiles compacted per list pass
 constexpr int kDqBlockQ = 128;    // dQ kernel: query rows per workgroup
 constexpr int kDqBlockK = 32;     // dQ kernel: keys per inner tile
 
@@ -37,6 +38,8 @@ struct ClassifyArgs {
   int32_t transposed;
   int32_t* counts;         // nullptr, or [bm][hm][lines] non-SKIP entries per map line
   int32_t* chunk_pre;      // nullptr, or [bm][hm][lines][ceil(len / 64)] non-SKIP entries before each 64-entry chunk
+  int32_t* first;          // nullptr, or (transposed maps) [bm][hm][lines]: the first entry of the dK/dV
+                           // kernel's list for the line, -1 when the line has none (see map_line)
 };
 
 struct FwdArgs {
@@ -145,6 +148,7 @@ struct BwdArgs {
   // tiling and the recompute dQ kernel's query tiles (may be nullptr).
   const int32_t* order_k;   // key-tile lines longest first; empty lines flagged with kEmptyLine, last
   const int32_t* order_live;   // the number of order_k lines before the empty ones
+  const int32_t* first_k;   // nullptr, or per key-tile line the query tile its list starts with
   const int32_t* order_qq;
   // Grouped-query attention with a mask shared by all heads: one dK/dV
   // workgroup per query head, float32 partials [2][B][H][Sk][D] (dK, then dV)

@@ -17,6 +17,7 @@
 namespace fm {
 namespace prep {
 
+static_assert(kBwdListCap % 256 == 0, "list passes end on a map-pass iteration");
 constexpr int kOrderBuckets = 4096;
 constexpr int64_t kTileBytes = (int64_t)kBwdBlockQ * kBwdBlockK * 2;   // one bf16 dS tile
 
@@ -92,8 +93,14 @@ __device__ __forceinline__ uint8_t classify_one(const int* s, int r0, int r1) {
 // non-SKIP entries goes to counts[bh * lines + line]; with a.chunk_pre set,
 // the number of non-SKIP entries before each 64-entry chunk of the line goes
 // to chunk_pre[bh * lines + line][chunk].
+// With a.first set (transposed maps), the line's first entry in the dK/dV
+// kernel's list order goes to first[bh * lines + line]: of the first
+// kBwdListCap-entry pass that has a non-SKIP entry, its first FULL entry, else
+// its first PARTIAL one (all entries count as PARTIAL for the ragged last key
+// tile); -1 for a line with none.
 __device__ __forceinline__ void map_line(const ClassifyArgs& a, int line, int bh) {
   __shared__ int wcnt[4];
+  __shared__ int wmin[2][4];   // per wavefront: first FULL, first non-SKIP entry
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool tr = a.transposed != 0;
   const int len = tr ? a.tq : a.tk;
@@ -110,10 +117,13 @@ __device__ __forceinline__ void map_line(const ClassifyArgs& a, int line, int bh
     r1 = min(r0 + a.block_q, a.seq_q);
   }
   const int nch = (len + 63) / 64;
+  const bool want_first = tr && a.first != nullptr;
+  const bool all_partial = (a.seq_k % a.block_k) != 0 && line == a.tk - 1;   // the ragged last key tile
   int carry = 0;
+  int pass_full = INT_MAX, pass_open = INT_MAX, first = -1;   // (uniform over the workgroup)
   for (int base = 0; base < len; base += 256) {
     const int i = base + tid;
-    bool open = false;
+    bool open = false, full = false;
     if (i < len) {
       if (tr) {
         r0 = i * a.block_q;
@@ -125,22 +135,36 @@ __device__ __forceinline__ void map_line(const ClassifyArgs& a, int line, int bh
       const uint8_t c = classify_one(s, r0, r1);
       out[i] = c;
       open = c != FM_TILE_SKIP;
+      full = c == FM_TILE_FULL && !all_partial;
     }
-    const int wc = __popcll(__ballot(open));
+    const uint64_t bo = __ballot(open), bf = __ballot(full);
+    const int wc = __popcll(bo);
     __syncthreads();   // every thread is done with the previous iteration's counts
-    if (lane == 0) wcnt[wv] = wc;
+    if (lane == 0) {
+      wcnt[wv] = wc;
+      wmin[0][wv] = bf ? base + 64 * wv + __builtin_ctzll(bf) : INT_MAX;
+      wmin[1][wv] = bo ? base + 64 * wv + __builtin_ctzll(bo) : INT_MAX;
+    }
     __syncthreads();
     int pre = carry, tot = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (k < wv) pre += wcnt[k];
       tot += wcnt[k];
+      pass_full = min(pass_full, wmin[0][k]);
+      pass_open = min(pass_open, wmin[1][k]);
     }
     const int ch = base / 64 + wv;
     if (a.chunk_pre && lane == 0 && ch < nch) a.chunk_pre[lid * nch + ch] = pre;
     carry += tot;
+    // end of a list pass (kBwdListCap is a multiple of 256): its first entry
+    if ((base + 256) % kBwdListCap == 0 || base + 256 >= len) {
+      if (first < 0 && pass_open != INT_MAX) first = pass_full != INT_MAX ? pass_full : pass_open;
+      pass_full = pass_open = INT_MAX;
+    }
   }
   if (a.counts && tid == 0) a.counts[lid] = carry;
+  if (want_first && tid == 0) a.first[lid] = first;
 }
 
 // 1024 threads: a.order = the lines sorted by their count, descending (a
