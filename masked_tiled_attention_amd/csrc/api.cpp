@@ -192,6 +192,7 @@ struct Layout {
   size_t vt = 0;                   // FP8 forward: V^T tiles [B][H_kv][Tk][8 KiB]
   size_t order_k = 0, order_qq = 0;   // backward launch orders (dQ: its counts, then the order)
   size_t first_k = 0;                 // dK/dV kernel: the first list entry per key-tile line
+  size_t dq_blocks = 0;               // stored-dS dQ kernel: launch order of its pair blocks
   size_t part = 0;                     // split-head dK/dV partials (0: not used)
   size_t opart = 0, lpart = 0;         // split-list forward partials (0: not used)
   int32_t ksplit = 1;
@@ -273,6 +274,8 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t
     off = align256(off + (size_t)(mrows * tk * 4) + 4);
     L.first_k = off;   // the first list entry of each key-tile line
     off = align256(off + (size_t)(mrows * tk * 4));
+    L.dq_blocks = off;
+    off = align256(off + (size_t)(ceil_div(tq_q, fm::kDqBlockPairs) * 4));
     L.order_qq = off;
     off = align256(off + (size_t)(mrows * tq_q * 8));
     L.dq_split = dq_split(p);
@@ -417,6 +420,10 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   ct.chunk_pre = a.chunk_pre;
   ct.first = reinterpret_cast<int32_t*>(w + L.first_k);
   a.first_k = ct.first;
+  if (maybe_ds && mrows == 1) {   // the stored-dS dQ kernel's block order (one mask row)
+    a.counts_q = counts_q;
+    a.dq_blocks = reinterpret_cast<int32_t*>(w + L.dq_blocks);
+  }
   const fm::ClassifyArgs cq = classify_args(mk, p->seqlen_q, p->seqlen_k, fm::kDqBlockQ, fm::kDqBlockK, 0,
                                             reinterpret_cast<int32_t*>(w + L.summary_q), classes_q, counts_q);
   hipError_t e = run_stage(FM_STAGE_CLASSIFY_SUMMARY, stream, [&] { return fm::launch_bwd_summaries(ct, cq, stream); });

@@ -116,15 +116,27 @@ void bwd_dq_ds_kernel(BwdArgs a) {
 
   // Later query tiles first, heads interleaved: neighbouring workgroups work
   // on nearby rows and share K tiles in L2 (this kernel is bound by memory
-  // traffic, so that beats ordering by length).
+  // traffic, so that beats ordering by length). With one mask row, blocks of
+  // 16 pairs (later pairs first within each) launch longest block first, which
+  // keeps that sharing within a block and cuts the tail.
   // With split lists (a.dq_split > 1), consecutive workgroups take the
   // parts of one pair's key-tile list and write float32 partial dQ.
+  // With a block order (one mask row), launch position p takes block
+  // dq_blocks[p / 16] of 16 pairs counted from the last pair, later pairs
+  // first within it; the launch is padded to whole blocks.
   const int ks = a.dq_split > 1 ? a.dq_split : 1;
   const int sp = (int)(blockIdx.x % ks);   // this workgroup's part
   const int wg = (int)(blockIdx.x / ks);
   const int nbh = a.batch * a.heads;
   const int npair = (a.tq + PAIR - 1) / PAIR;
-  const int qt0 = PAIR * (npair - 1 - wg / nbh);
+  const int pos = wg / nbh;
+  int pair = npair - 1 - pos;
+  if (a.dq_blocks != nullptr) {
+    const int blk = __builtin_amdgcn_readfirstlane(a.dq_blocks[pos / kDqBlockPairs]);
+    pair = npair - 1 - kDqBlockPairs * blk - pos % kDqBlockPairs;
+    if (pair < 0) return;   // padding of the earliest block
+  }
+  const int qt0 = PAIR * pair;
   const bool has1 = qt0 + 1 < a.tq;
   const int bh = wg % nbh;
   const int b = bh / a.heads;
@@ -338,7 +350,8 @@ hipError_t launch_dq_ds_t(const BwdArgs& a, hipStream_t s) {
   const int ks = a.dq_split > 1 ? a.dq_split : 1;
   if (ks != 1 && ks != 2 && ks != 4 && ks != 8) return hipErrorInvalidValue;
   const int npair = (a.tq + PAIR - 1) / PAIR;
-  hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F32>), dim3(npair * a.batch * a.heads * ks), dim3(NT), 0, s, a);
+  const int npos = a.dq_blocks ? (npair + kDqBlockPairs - 1) / kDqBlockPairs * kDqBlockPairs : npair;
+  hipLaunchKernelGGL((bwd_dq_ds_kernel<D, F32>), dim3(npos * a.batch * a.heads * ks), dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ks == 1) return e;
   const int64_t n = (int64_t)a.batch * a.heads * a.seq_q * (D / 4);

@@ -57,13 +57,14 @@ __global__ __launch_bounds__(256) void bwd_maps_kernel(ClassifyArgs ct, Classify
   prep::map_line(cq, b2 % cq.tq, b2 / cq.tq);
 }
 
-// Backward launch 3: workgroup 0 sorts the dK/dV order, 1 the recompute dQ
-// kernel's (when set), and the last one scans the slot offsets (when the
-// plan is set).
+// Backward launch 3: workgroup 0 sorts the dK/dV order, the next ones the
+// recompute dQ kernel's and the stored-dS dQ kernel's block order (each when
+// set), and the last one scans the slot offsets (when the plan is set).
 __global__ __launch_bounds__(1024) void bwd_orders_kernel(OrderArgs ok, OrderArgs oq, BwdArgs a) {
-  const int blk = blockIdx.x;
+  int blk = blockIdx.x;
   if (blk == 0) return prep::sort_lines(ok);
-  if (blk == 1 && oq.order) return prep::sort_lines(oq);
+  if (oq.order && --blk == 0) return prep::sort_lines(oq);
+  if (a.dq_blocks && --blk == 0) return prep::sort_dq_blocks(a);
   prep::scan_slots(a, a.mask.bm * a.mask.hm * a.tk);
 }
 
@@ -163,7 +164,7 @@ hipError_t launch_bwd_maps(const ClassifyArgs& ct, const ClassifyArgs& cq, hipSt
 }
 
 hipError_t launch_bwd_orders(const OrderArgs& ok, const OrderArgs& oq, const BwdArgs& a, hipStream_t stream) {
-  const int nblk = 1 + (oq.order ? 1 : 0) + (a.plan ? 1 : 0);
+  const int nblk = 1 + (oq.order ? 1 : 0) + (a.dq_blocks ? 1 : 0) + (a.plan ? 1 : 0);
   hipLaunchKernelGGL(bwd_orders_kernel, dim3(nblk), dim3(1024), 0, stream, ok, oq, a);
   return hipGetLastError();
 }

@@ -15,6 +15,7 @@ constexpr int kFwdBlockK = 64;
 constexpr int kBwdBlockQ = 64;    // dK/dV kernel: query rows per inner tile
 constexpr int kBwdBlockK = 128;   // dK/dV kernel: keys per workgroup
 constexpr int kBwdListCap = 1024;  // dK/dV kernel: query tiles compacted per list pass
+constexpr int kDqBlockPairs = 16;  // stored-dS dQ launch order: query-tile pairs per block
 constexpr int kDqBlockQ = 128;    // dQ kernel: query rows per workgroup
 constexpr int kDqBlockK = 32;     // dQ kernel: keys per inner tile
 
@@ -150,6 +151,11 @@ struct BwdArgs {
   const int32_t* order_live;   // the number of order_k lines before the empty ones
   const int32_t* first_k;   // nullptr, or per key-tile line the query tile its list starts with
   const int32_t* order_qq;
+  // Stored-dS dQ launch order (mask shared by all rows; else nullptr): blocks
+  // of kDqBlockPairs query-tile pairs, counted from the last pair, longest
+  // list first; counts_q = the dQ map's line counts, written by the map pass.
+  const int32_t* counts_q;
+  int32_t* dq_blocks;
   // Grouped-query attention with a mask shared by all heads: one dK/dV
   // workgroup per query head, float32 partials [2][B][H][Sk][D] (dK, then dV)
   // summed per K/V head afterwards; nullptr: a workgroup runs all the query

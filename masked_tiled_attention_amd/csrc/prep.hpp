@@ -225,6 +225,42 @@ __device__ __forceinline__ void sort_lines(const OrderArgs& a) {
   }
 }
 
+// 1024 threads: the stored-dS dQ kernel's launch order over blocks of
+// kDqBlockPairs query-tile pairs (block b holds pairs npair - 1 - 16 b - i,
+// i < 16: later pairs first within a block, so neighbouring workgroups still
+// share K tiles), the block with the longest list first; ties keep the later
+// block first. A pair's list length is its dQ-map line count (the 128-row
+// line is the pair); one mask row.
+constexpr int kMaxDqBlocks = 4096;   // beyond this, the blocks keep their natural order
+__device__ __forceinline__ void sort_dq_blocks(const BwdArgs& a) {
+  __shared__ int bkey[kMaxDqBlocks];
+  const int npair = a.tq_q;
+  const int nblk = (npair + kDqBlockPairs - 1) / kDqBlockPairs;
+  const int tid = threadIdx.x;
+  if (nblk > kMaxDqBlocks) {
+    for (int b = tid; b < nblk; b += 1024) a.dq_blocks[b] = b;
+    return;
+  }
+  for (int b = tid; b < nblk; b += 1024) {
+    int m = 0;
+    for (int i = 0; i < kDqBlockPairs; ++i) {
+      const int p = npair - 1 - kDqBlockPairs * b - i;
+      if (p >= 0) m = max(m, a.counts_q[p]);
+    }
+    bkey[b] = m;
+  }
+  __syncthreads();
+  for (int b = tid; b < nblk; b += 1024) {
+    const int kb = bkey[b];
+    int rank = 0;
+    for (int o = 0; o < nblk; ++o) {
+      const int ko = bkey[o];
+      rank += (ko > kb) || (ko == kb && o < b);
+    }
+    a.dq_blocks[rank] = b;
+  }
+}
+
 // 1024 threads: row_off = exclusive prefix sums of row_cnt over the nrows =
 // mask rows * tk key-tile rows, plan[0] = the total, plan[1] = 1 when rep *
 // total dS tiles fit into ds_capacity bytes (and slots fit in int32).
