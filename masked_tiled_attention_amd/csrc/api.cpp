@@ -272,8 +272,8 @@ Layout workspace_layout(const fm_problem* p, const fm_mask* m, bool bwd, int32_t
     const int64_t tq_q = ceil_div(p->seqlen_q, fm::kDqBlockQ);
     L.order_k = off;   // the counts are row_cnt; then the number of lines with work
     off = align256(off + (size_t)(mrows * tk * 4) + 4);
-    L.first_k = off;   // the first list entry of each key-tile line
-    off = align256(off + (size_t)(mrows * tk * 4));
+    L.first_k = off;   // the first list entry of each key-tile line, then by order position
+    off = align256(off + (size_t)(mrows * tk * 4) * 2);
     L.dq_blocks = off;
     off = align256(off + (size_t)(ceil_div(tq_q, fm::kDqBlockPairs) * 4));
     L.order_qq = off;
@@ -419,7 +419,7 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
                                       reinterpret_cast<int32_t*>(w + L.summary), classes_t, a.row_cnt);
   ct.chunk_pre = a.chunk_pre;
   ct.first = reinterpret_cast<int32_t*>(w + L.first_k);
-  a.first_k = ct.first;
+  a.first_k = ct.first + mrows * tk;   // filled by the order sort
   if (maybe_ds && mrows == 1) {   // the stored-dS dQ kernel's block order (one mask row)
     a.counts_q = counts_q;
     a.dq_blocks = reinterpret_cast<int32_t*>(w + L.dq_blocks);
@@ -448,6 +448,8 @@ fm_status bwd_setup(const fm_problem* p, const fm_mask* mask, void* ws, size_t w
   ok.order = reinterpret_cast<int32_t*>(w + L.order_k);
   ok.mark_empty = 1;
   ok.live = ok.order + ok.rows;
+  ok.first_in = ct.first;
+  ok.first_out = const_cast<int32_t*>(a.first_k);
   fm::OrderArgs oq{};
   if (!size_query && ws_bytes < L.ds) {
     oq.counts = counts_q;

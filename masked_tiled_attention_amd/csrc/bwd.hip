@@ -117,8 +117,10 @@ __global__ __launch_bounds__(kv::THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   const bool empty = (ent & kEmptyLine) != 0;
   if (empty && (int64_t)blockIdx.x - busy < zeros) return;
   const int line = (int)(ent & ~kEmptyLine);   // K/V mask row * tk + key tile
-  // (without a head loop the line is also the class column's mask row and key tile)
-  const int first_q = !GROUPED && a.first_k != nullptr ? __builtin_amdgcn_readfirstlane(a.first_k[line]) : -1;
+  // (by launch position, so that it loads beside the order entry; without a
+  // head loop the line is also the class column's mask row and key tile)
+  const int first_q =
+      !GROUPED && a.first_k != nullptr ? __builtin_amdgcn_readfirstlane(a.first_k[blockIdx.x / rep]) : -1;
   // (integer divisions by launch constants expand to vector code: the results
   // are taken back to scalar registers so that the addresses stay scalar)
   const int kt = __builtin_amdgcn_readfirstlane(line % a.tk);

@@ -101,6 +101,8 @@ struct OrderArgs {
   int32_t* order;          // [rows] line indices, longest first
   int32_t mark_empty;      // set: lines with no non-SKIP entry carry kEmptyLine and go last
   int32_t* live;           // with mark_empty, optional: the number of lines before the empty ones
+  const int32_t* first_in;   // optional, per line: a value carried into first_out at the line's position
+  int32_t* first_out;
 };
 constexpr uint32_t kEmptyLine = 0x80000000u;   // order entry flag: the line has no work
 
@@ -149,7 +151,7 @@ struct BwdArgs {
   // tiling and the recompute dQ kernel's query tiles (may be nullptr).
   const int32_t* order_k;   // key-tile lines longest first; empty lines flagged with kEmptyLine, last
   const int32_t* order_live;   // the number of order_k lines before the empty ones
-  const int32_t* first_k;   // nullptr, or per key-tile line the query tile its list starts with
+  const int32_t* first_k;   // nullptr, or per order_k position: the query tile its line's list starts with
   const int32_t* order_qq;
   // Stored-dS dQ launch order (mask shared by all rows; else nullptr): blocks
   // of kDqBlockPairs query-tile pairs, counted from the last pair, longest

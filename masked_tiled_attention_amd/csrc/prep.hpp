@@ -221,7 +221,9 @@ __device__ __forceinline__ void sort_lines(const OrderArgs& a) {
   __syncthreads();
   for (int r = tid; r < a.rows; r += 1024) {
     const int64_t c = count(r);
-    a.order[atomicAdd(&hist[key(c)], 1)] = (int32_t)((uint32_t)r | (a.mark_empty && c == 0 ? kEmptyLine : 0u));
+    const int pos = atomicAdd(&hist[key(c)], 1);
+    a.order[pos] = (int32_t)((uint32_t)r | (a.mark_empty && c == 0 ? kEmptyLine : 0u));
+    if (a.first_out) a.first_out[pos] = a.first_in[r];
   }
 }
 
